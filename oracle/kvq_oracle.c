@@ -428,8 +428,8 @@ void kvqo_kvarn_tile(const uint16_t* x16, int64_t stride, int side, float* y_rot
  *    per-token-head only: K scales fp32 [P] at 2*P*D, V scales fp32 [P] after
  *  NVFP4 (in a byte the low nibble holds the first element):
  *    K codes  [P][D/2]      at 0:            byte t*D/2 + d/2, nibble d%2
- *    V codes  [P/4][D][2]   at P*D/2:        byte 2*D*(t/4) + 2*d + (t%4)/2,
- *                                            nibble t%2
+ *    V codes  [P/4][D/2][4] at P*D/2:        byte 2*D*(t/4) + 4*(d/2) + t%4,
+ *                                            nibble d%2
  *    K block scales [P][D/16]  at P*D:       byte t*D/16 + d/16
  *    V block scales [D/16][P]  after:        byte (d/16)*P + t
  *  KVarN k4v2 (P = D = 128):
@@ -522,7 +522,7 @@ static void store_row(const kvqo_layout* L, uint8_t* ch, int t, const float* xk,
     uint8_t* vs = ks + (int64_t)P * D / 16;
     for (int d = 0; d < D; d++) {
       put_nibble(kc + (int64_t)t * D / 2 + d / 2, d % 2, ck[d]);
-      put_nibble(vc + 2LL * D * (t / 4) + 2 * d + (t % 4) / 2, t % 2, cv[d]);
+      put_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 4, d % 2, cv[d]);
     }
     for (int b = 0; b < D / 16; b++) {
       ks[(int64_t)t * (D / 16) + b] = bk[b];
@@ -588,7 +588,7 @@ static void load_row(const kvqo_layout* L, const uint8_t* ch, int t, double* k, 
       const uint8_t* vs = ks + (int64_t)P * D / 16;
       for (int d = 0; d < D; d++) {
         uint8_t a = get_nibble(kc + (int64_t)t * D / 2 + d / 2, d % 2);
-        uint8_t b = get_nibble(vc + 2LL * D * (t / 4) + 2 * d + (t % 4) / 2, t % 2);
+        uint8_t b = get_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 4, d % 2);
         double sbk = kvqo_e4m3_decode(ks[(int64_t)t * (D / 16) + d / 16]);
         double sbv = kvqo_e4m3_decode(vs[(int64_t)(d / 16) * P + t]);
         /* x_hat = s_t * s_b * q, [P5] §双层缩放怎样恢复动态范围 */

@@ -23,8 +23,8 @@ MUTANTS = [
      "(void)0;", 0, [pins.pin_kvarn_tile]),
     ("kvarn_dev_scale", "float sd = sqrtf(sum_tree(sq, 128) * 0.0078125f);",
      "float sd = sqrtf(sum_tree(sq, 128) * 0.015625f);", 0, [pins.pin_kvarn_tile]),
-    ("nvfp4_v_nibble_index", "put_nibble(vc + 2LL * D * (t / 4) + 2 * d + (t % 4) / 2, t % 2, cv[d]);",
-     "put_nibble(vc + 2LL * D * (t / 4) + 2 * d + (t % 4) % 2, t % 2, cv[d]);", 0, [pins.pin_layout_bijective]),
+    ("nvfp4_v_nibble_index", "put_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 4, d % 2, cv[d]);",
+     "put_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 2, d % 2, cv[d]);", 0, [pins.pin_layout_bijective]),
     ("gqa_modulo", "int kvh = h / G;", "int kvh = h % H;", 0, [pins.pin_attention]),
     ("softmax_scale_dropped", "lg[t] = acc * scale;", "lg[t] = acc;", 0, [pins.pin_attention]),
     ("e4m3_bias", "v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);", 0,
