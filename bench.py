@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cache quantisation hot path on one MI355X.
+
+A step is one decode step of the workload: quantise-write the new token of
+every sequence (kvq_quantize_write, B tokens) and run dequant-fused paged
+decode attention over the whole context (kvq_decode_attention).  The headline
+workload is INT8 per-token-head at 32K context (B=8, 64 q / 8 kv heads,
+D=128, page 16): `value` is quantised-KV bytes read per second over the timed
+steps.  Inputs are resident in HBM before timing starts; the cache is rotated
+across copies so the 256 MB last-level cache does not hold the next step's
+pages.
+
+Also reported on the same line:
+  write_mtok_s   whole-context quantise-on-write throughput (tokens/s / 1e6)
+  roofline       decode kernel: algorithmic KV bytes per launch / mean launch
+                 duration (HIP events around each decode launch in the timed
+                 region, on the launch stream) against 8 TB/s
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+  formats        the other formats' workloads (decode GB/s, write Mtok/s)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn quantised-KV GB/s (% of HBM peak) + quantize-write Mtok/s, 1 GPU"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Problem:
+    """One workload on the device: inputs, rotated cache copies, workspace."""
+
+    def __init__(self, K, name, fmt, flags=0, copies=0, min_rotation_bytes=1.0e9):
+        import numpy as np
+        import torch
+
+        import workloads
+        t0 = time.time()
+        w = workloads.make(name)
+        sp = w.spec
+        self.w, self.sp, self.fmt, self.flags = w, sp, fmt, flags
+        ks, vs = w.per_tensor_scales(fmt)
+        self.lay = K.layout(fmt, sp.Hkv, sp.D, sp.P, w.num_pages, ks, vs, flags)
+        self.page_bytes = K.kvq_page_bytes(self.lay)
+        self.cache_bytes = self.page_bytes * w.num_pages
+        self.kv_bytes = w.B * (w.T // sp.P) * self.page_bytes  # read by one decode
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.k, self.v = d(w.k16), d(w.v16)
+        self.slots = d(w.slots)
+        self.q, self.bt, self.ctx = d(w.q16), d(w.block_tables), d(w.ctx_lens)
+        # the step's new token: the last position of every sequence
+        last = np.arange(w.B) * w.T + (w.T - 1)
+        self.k_new, self.v_new = d(w.k16[last]), d(w.v16[last])
+        self.slots_new = d(w.slots[last])
+        n = copies or max(2, math.ceil(min_rotation_bytes / self.cache_bytes))
+        self.caches = [torch.zeros(self.cache_bytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        self.ws = K.DecodeWorkspace(self.lay, w.B, sp.Hq, w.block_tables.shape[1])
+        self.out = torch.empty((w.B, sp.Hq, sp.D), dtype=torch.float16, device="cuda")
+        self.sm = 1.0 / math.sqrt(sp.D)
+        self.K = K
+        torch.cuda.synchronize()
+        log(f"[bench] {name} fmt={fmt} flags={flags}: inputs ready in {time.time() - t0:.1f}s, "
+            f"cache {self.cache_bytes / 1e6:.1f} MB x {n} copies, {self.ws.num_splits} splits")
+
+    def write_all(self, i):
+        self.K.kvq_quantize_write(self.lay, self.k, self.v, self.slots, self.caches[i % len(self.caches)])
+
+    def append(self, i):
+        self.K.kvq_quantize_write(self.lay, self.k_new, self.v_new, self.slots_new, self.caches[i % len(self.caches)])
+
+    def decode(self, i):
+        self.K.kvq_decode_attention(self.lay, self.caches[i % len(self.caches)], self.q, self.bt, self.ctx, self.sm,
+                                    self.out, self.ws.buffer)
+
+    def time_write(self, reps=6):
+        import torch
+        for i in range(len(self.caches)):
+            self.write_all(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            self.write_all(i)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        n_tok = self.w.B * self.w.T
+        return n_tok / (ms * 1e-3) / 1e6, ms
+
+    def time_steps(self, steps, warmup):
+        """Timed decode steps; returns (ms per step, mean decode launch ms)."""
+        import torch
+        for i in range(warmup):
+            self.append(i)
+            self.decode(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            self.append(i)
+            ev[i][0].record()
+            self.decode(i)
+            ev[i][1].record()
+        end.record()
+        torch.cuda.synchronize()
+        total = start.elapsed_time(end)
+        dec = [a.elapsed_time(b) for a, b in ev]
+        return total / steps, sum(dec) / len(dec)
+
+
+def cpu_baseline(name, fmt, flags, n_seq, threads):
+    """The oracle on a bounded sample of the workload: quantise-write every
+    token of n_seq sequences, then decode every q head of those sequences.
+    Parallel over (sequence, kv head) units with one thread each (ctypes
+    releases the GIL)."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    O = oracle.default()
+    w = workloads.make(name, B=n_seq)
+    sp = w.spec
+    ks, vs = w.per_tensor_scales(fmt)
+    lay = oracle.layout(fmt, sp.Hkv, sp.D, sp.P, w.num_pages, ks, vs, flags)
+    cache = np.zeros(w.num_pages * O.page_bytes(lay), np.uint8)
+    per_seq = w.T
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda b: O.quantize_write(lay, w.k16[b * per_seq:(b + 1) * per_seq],
+                                               w.v16[b * per_seq:(b + 1) * per_seq],
+                                               w.slots[b * per_seq:(b + 1) * per_seq], cache), range(n_seq)))
+    t_write = time.time() - t0
+    G = sp.Hq // sp.Hkv
+    units = [(b, h) for b in range(n_seq) for h in range(sp.Hkv)]
+
+    def dec(u):
+        b, h = u
+        pairs = np.array([(b, h * G + g) for g in range(G)], np.int32)
+        return O.decode_attention(lay, cache, w.q16, w.block_tables, w.ctx_lens, 1.0 / math.sqrt(sp.D), pairs=pairs)
+
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(dec, units))
+    t_dec = time.time() - t0
+    kv_bytes = n_seq * (w.T // sp.P) * O.page_bytes(lay)
+    return {
+        "value": round(kv_bytes / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{name}: {n_seq} of {sp.B} sequences, all {sp.Hq} q heads (decode, binary64), "
+                   f"after quantise-writing their {n_seq * w.T} tokens (binary32)"),
+        "seconds": round(t_dec, 2),
+        "write_mtok_s": round(n_seq * w.T / t_write / 1e6, 4),
+        "write_seconds": round(t_write, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="int8_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-formats", action="store_true", help="skip the other formats' workloads")
+    ap.add_argument("--cpu-seqs", type=int, default=2)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU: the hot path shards by (sequence, kv head) with no exchange, and this "
+            "build runs and reports a single MI355X only.  Use --gpus 1.")
+        sys.exit(2)
+
+    import torch
+
+    import quantized_decode_attention_amd as K
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    st = K.kvq_check_device(0)
+    if st != 0:
+        log(f"device check failed: {K.kvq_status_string(st)}")
+        sys.exit(1)
+
+    main_fmt = {"int8_32k": (K.KVQ_INT8_PTH, 0), "fp8_sink_4k": (K.KVQ_FP8_PTH, 0),
+                "nvfp4_16k": (K.KVQ_NVFP4, 0)}[args.workload]
+    pb = Problem(K, args.workload, *main_fmt)
+    write_mtok, write_ms = pb.time_write()
+    log(f"[bench] whole-context write: {write_mtok:.1f} Mtok/s ({write_ms:.3f} ms)")
+    ms_step, ms_dec = pb.time_steps(args.steps, args.warmup)
+    value = pb.kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = pb.kv_bytes / (ms_dec * 1e-3) / 1e9
+    log(f"[bench] step {ms_step * 1e3:.1f} us ({value:.0f} GB/s), decode launch {ms_dec * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s, {achieved / HBM_PEAK_GBS:.1%} of peak)")
+    sp, w = pb.sp, pb.w
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32-acc",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "format": K.FORMAT_NAMES[pb.fmt], "batch": w.B, "context": w.T,
+            "q_heads": sp.Hq, "kv_heads": sp.Hkv, "head_dim": sp.D, "page_size": sp.P,
+            "splits": pb.ws.num_splits, "cache_copies": len(pb.caches),
+            "step": "quantize-write 1 new token per sequence + paged decode attention over the context",
+        },
+        "kv_bytes_per_step": pb.kv_bytes,
+        "write_mtok_s": round(write_mtok, 2),
+        "write_gbs": round((2 * w.B * w.T * sp.Hkv * sp.D * 2 + pb.cache_bytes) / (write_ms * 1e-3) / 1e9, 2),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": f"decode_kernel<{pb.fmt}, {sp.D}>", "mean_launch_us": round(ms_dec * 1e3, 2),
+        },
+    }
+    del pb
+    torch.cuda.empty_cache()
+
+    if not args.no_formats:
+        fmts = {}
+        others = [("fp8_sink_4k", K.KVQ_FP8_PER_TENSOR, 0), ("fp8_sink_4k", K.KVQ_FP8_PTH, 0),
+                  ("nvfp4_16k", K.KVQ_NVFP4, 0), ("nvfp4_16k", K.KVQ_NVFP4, K.KVQ_FLAG_NVFP4_4OVER6)]
+        for name, fmt, flags in others:
+            if name == args.workload and fmt == main_fmt[0] and flags == main_fmt[1]:
+                continue
+            p = Problem(K, name, fmt, flags)
+            wm, _ = p.time_write()
+            ms_s, ms_d = p.time_steps(max(20, args.steps // 2), args.warmup)
+            key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "")
+            fmts[key] = {"workload": name, "decode_gbs": round(p.kv_bytes / (ms_d * 1e-3) / 1e9, 1),
+                         "decode_frac_of_peak": round(p.kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "decode_us": round(ms_d * 1e3, 2), "step_us": round(ms_s * 1e3, 2),
+                         "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits}
+            log(f"[bench] {key}: {fmts[key]}")
+            del p
+            torch.cuda.empty_cache()
+        result["formats"] = fmts
+
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"[bench] CPU oracle baseline on {threads} threads ...")
+        result["cpu_baseline"] = cpu_baseline(args.workload, *main_fmt, args.cpu_seqs, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

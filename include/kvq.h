@@ -1,0 +1,215 @@
+/*
+ * kvq.h -- C ABI of libkvq: KV-cache quantise-on-write and dequant-fused paged
+ * GQA decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [P1] "KV Cache 量化深度解析：Per-Tensor、Per-Token-Head 与 NVFP4"
+ *   [P2] "KVarN：华为推出的原生 vLLM KV-cache 量化后端"
+ *   [P3] "KV Cache 量化 · LLM Glossary"
+ *   [P4] "KV 量化" (vLLM / SGLang source walk-through)
+ *   [P5] "NVFP4 KV Cache：Blackwell 上的 4-bit 缓存量化"
+ *
+ * Conventions for every entry point:
+ *   - All pointers except `layout` are device pointers (HIP global memory) on the
+ *     current HIP device, unless stated.  The caller owns every buffer; the
+ *     library allocates no device memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; the returned status covers argument validation and
+ *     kernel-launch errors only.
+ *   - Unsupported combinations are rejected with KVQ_ERR_UNSUPPORTED or
+ *     KVQ_ERR_INVALID_ARG before anything is launched; the library never falls
+ *     back to another format ([P5] §一条完整的上线验证路径 asks that a missing
+ *     capability be explicit).
+ *   - Tensors are dense and contiguous in the stated shapes; binary16 is IEEE
+ *     half precision; inputs are finite.
+ *
+ * Cache layout (the storage contract; page_bytes = num_kv_heads * chunk_bytes):
+ *   the chunk of (page p, kv head h) starts at byte (p * H + h) * chunk_bytes.
+ *   Inside a chunk, with P = page_size, D = head_dim, t = token offset in the
+ *   page and d = channel:
+ *   8-bit formats (FP8 per-tensor, INT8 and FP8 per-token-head): K codes at
+ *   0 and V codes at P*D, each 16*D bytes per group of 16 tokens (u = t/16,
+ *   s = t%16, group at 16*D*u), B = min(16, D/4):
+ *     K  d = (D/4)*g + B*h + e         ->  64*B*h + 16*B*g + B*s + e
+ *     V  d = (D/16)*n + (B/4)*h + j    ->  64*B*h + 16*B*(s/4) + B*n + 4*j + s%4
+ *     (so that each 16-byte decode load of a wavefront reads one contiguous
+ *     run); per-token-head only: K scales fp32 [P] at 2*P*D, then V scales
+ *   NVFP4 (low nibble = even channel):
+ *     K codes  [P][D/2]     at 0         byte t*D/2 + d/2
+ *     V codes  [P/4][D/2][4] at P*D/2    byte 2*D*(t/4) + 4*(d/2) + t%4
+ *     K block scales E4M3 [P][D/16]  at P*D     byte t*D/16 + d/16
+ *     V block scales E4M3 [D/16][P]  after them byte (d/16)*P + t
+ *   KVarN k4v2 g128 (P = D = 128):
+ *     K codes 4-bit [P][D/2] at 0        byte t*D/2 + d/2, low nibble = even d
+ *     V codes 2-bit [P/4][D] at P*D/2    byte D*(t/4) + d, bits 2(t%4)+1..2(t%4)
+ *     fp32 K alpha[D], K beta[D], K rho[P], V alpha[P], V beta[P], V gamma[D]
+ *     (rotated tile rebuilt as K = rho_t (alpha_d code + beta_d),
+ *      V = gamma_d (alpha_t code + beta_t); see kvq_quantize_write)
+ *   Codes: INT8 = two's-complement byte; FP8 = OCP E4M3 ("fn", max 448);
+ *   NVFP4 = E2M1 nibble (sign bit 3) with E4M3 block scales.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage formats.  Values 1..4 follow the mode numbering of vLLM's
+ * KVQuantMode listed in [P1] §二 (NONE = 0 is not a cache format here);
+ * 5 is KVarN's k4v2 g128 preset ([P2] §配置与部署). */
+typedef enum {
+  KVQ_FP8_PER_TENSOR = 1,  /* [P1] §2.1, [P4] §FP8 per-tensor */
+  KVQ_INT8_PTH = 2,        /* per-token-head INT8, [P3] §它改变缓存表示 */
+  KVQ_FP8_PTH = 3,         /* per-token-head FP8, [P1] §2.2 */
+  KVQ_NVFP4 = 4,           /* [P5] §双层缩放怎样恢复动态范围 */
+  KVQ_KVARN_K4V2_G128 = 5  /* [P2] §技术原理 */
+} kvq_format;
+
+/* NVFP4 only: per block, keep the max/4 block scale instead of max/6 when its
+ * squared reconstruction error is strictly smaller ([P5] §用一组数直观看缩放的作用). */
+#define KVQ_FLAG_NVFP4_4OVER6 1u
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1,         /* NULL pointer, negative size, bad scale */
+  KVQ_ERR_UNSUPPORTED = 2,         /* valid request this build does not serve */
+  KVQ_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace smaller than required */
+  KVQ_ERR_DEVICE = 4,              /* current device is not gfx950 */
+  KVQ_ERR_HIP = 5                  /* a HIP call failed (launch error) */
+} kvq_status;
+
+/* One attention layer's cache description.
+ *   format       kvq_format
+ *   flags        KVQ_FLAG_* (only KVQ_FLAG_NVFP4_4OVER6, NVFP4 only)
+ *   num_kv_heads H, >= 1
+ *   head_dim     D: 32, 64 or 128 (KVarN: 128)
+ *   page_size    P tokens per page: 16, 32, 64, 128 or 256 (KVarN: 128, one tile)
+ *   num_pages    pages in the pool, >= 1
+ *   k_scale, v_scale  FP8 per-tensor: the layer's K and V scales (divide on
+ *                write, multiply on read; [P4] §写和读).  NVFP4: the per-layer
+ *                FP32 global scales s_t of K and V.  Finite, in
+ *                [2^-64, 2^64].  Ignored by the other formats. */
+typedef struct {
+  int32_t format;
+  int32_t flags;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_pages;
+  float k_scale;
+  float v_scale;
+} kvq_layout;
+
+/* Bytes of one page (all kv heads, K and V, codes and in-page scales): the real
+ * page size the pool must be sized with ([P5] §“4 bit”为什么不是严格的 4
+ * bits/value; [P4] §scale 和数据放在一起).  Host-only.  Returns -1 for an
+ * invalid or unsupported layout. */
+int64_t kvq_page_bytes(const kvq_layout* layout);
+
+/* KVQ_OK if HIP device `hip_device` is a gfx950 (MI355X), else KVQ_ERR_DEVICE
+ * (also when no device is present).  Host-only, no kernel launched. */
+kvq_status kvq_check_device(int hip_device);
+
+/* Quantise-on-write ([P5] §KV 的写入与读取路径, write path; [P4] §写和读).
+ *   k, v          binary16 [n_tok][H][D], freshly computed keys and values.
+ *   slot_mapping  int64 [n_tok]: token i goes to slot page * P + offset.
+ *                 Negative slots and slots >= num_pages * P are skipped.
+ *   cache         uint8 [num_pages * page_bytes], written in place.
+ * Per format (binary32 arithmetic, correctly rounded division, ties-to-even):
+ *   FP8 per-tensor:   code = E4M3(x / k_scale) (v_scale for V), saturating at
+ *                     448; no scale stored.
+ *   INT8 per-token-head: s = max(max|x|, 1e-8) / 127, code = clip(rne(x / s),
+ *                     -127, 127); s stored in-page ([P3] formula and script).
+ *   FP8 per-token-head: s = max(max|x|, 1e-8) / 448, code = E4M3(x / s)
+ *                     ([P1] §2.2 with FP8_MAX = 448).
+ *   NVFP4:            per 16 channels, s_b = E4M3((max|x| / 6) / s_t),
+ *                     code = E2M1(x / (s_t * s_b)) (ties to even, saturating
+ *                     at 6); a block whose s_b decodes to 0 stores zero codes.
+ *                     With KVQ_FLAG_NVFP4_4OVER6 the max/4 candidate is kept
+ *                     when its binary32 squared error is strictly smaller.
+ *   KVarN k4v2 g128:  per 128-token tile and kv head ([P2] §技术原理):
+ *                     normalised Sylvester Walsh-Hadamard rotation of every
+ *                     token row, 4 sweeps of alternating token / channel
+ *                     deviation normalisation, asymmetric RTN (K: 4-bit per
+ *                     channel over the tile's tokens; V: 2-bit per token over
+ *                     channels), scales folded into the metadata above.
+ *                     Requires n_tok % 128 == 0; tokens 128i..128i+127 must
+ *                     map to slots page*128 + 0..127 of one page (only the
+ *                     first slot of each tile is read).
+ * Errors: KVQ_ERR_INVALID_ARG for NULL pointers, n_tok < 0, bad scales or a
+ * KVarN n_tok not a multiple of 128; KVQ_ERR_UNSUPPORTED for layouts outside
+ * the list above; KVQ_ERR_DEVICE off gfx950. */
+kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const void* v,
+                              const int64_t* slot_mapping, int64_t n_tok, void* cache,
+                              void* stream);
+
+/* Bytes of workspace kvq_decode_attention needs for this problem (host-only;
+ * -1 if invalid): one partial record of binary32 (max, sum, output row) per
+ * (sequence, kv head, context split), 0 when a single split is used.
+ * num_splits: 0 = let the library choose, else the number of context splits
+ * per (sequence, kv head) to use (clamped to [1, min(256, max_pages_per_seq)]). */
+int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                   int32_t max_pages_per_seq, int32_t num_splits);
+
+/* Number of context splits kvq_decode_attention will use (host-only; -1 if
+ * invalid).  Same arguments as kvq_decode_workspace_bytes. */
+int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t max_pages_per_seq,
+                              int32_t num_splits);
+
+/* Dequant-fused paged GQA decode attention ([P5] §K 与 V 的量化误差进入 attention
+ * 的位置不同: O = softmax(Q K^T / sqrt(d) + M) V with M = 0 for decode; the
+ * cache is read through block tables and dequantised in registers, never
+ * expanded to a full-precision copy in memory, [P5] §KV 的写入与读取路径).
+ *   cache          as written by kvq_quantize_write.
+ *   q              binary16 [batch][num_q_heads][D]; q head h reads kv head
+ *                  h / (num_q_heads / H); num_q_heads / H must be 1, 2, 4 or 8.
+ *   block_tables   int32 [batch][max_pages_per_seq]: page of each P-token
+ *                  block of a sequence; entries outside [0, num_pages) are
+ *                  treated as empty pages (their tokens get zero weight).
+ *   context_lens   int32 [batch]: tokens per sequence, clamped to
+ *                  [0, max_pages_per_seq * P]; 0 gives a zero output row.
+ *   sm_scale       logit scale, normally 1/sqrt(D).
+ *   kvarn_tail     KVarN only: binary16 [batch][2][H][128][D] (keys, then
+ *                  values); row j holds token ctx - ctx%128 + j for
+ *                  j < ctx % 128, i.e. the tokens of the incomplete last tile,
+ *                  attended in full precision.  May be NULL when every
+ *                  context is a multiple of 128.  Must be NULL for other
+ *                  formats.
+ *   out            binary16 [batch][num_q_heads][D].
+ *   workspace      device buffer of at least kvq_decode_workspace_bytes(...)
+ *                  bytes (may be NULL when that is 0); its contents need no
+ *                  preparation.  Two calls that overlap in time must not share
+ *                  a workspace.
+ *   num_splits     as for kvq_decode_workspace_bytes.
+ * Launches one kernel, plus a small merge kernel when the context is split.
+ * Accumulation is binary32 (scores and softmax) on MFMA with binary16
+ * operands split into high and low halves, so results track a binary64
+ * reference to about 1e-5 relative. */
+kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, const void* q,
+                                int32_t num_q_heads, const int32_t* block_tables,
+                                int32_t max_pages_per_seq, const int32_t* context_lens,
+                                int32_t batch, float sm_scale, const void* kvarn_tail, void* out,
+                                void* workspace, int64_t workspace_bytes, int32_t num_splits,
+                                void* stream);
+
+/* Expand cached tokens back to binary32 [n_tok][H][D] for inspection and tests
+ * (x_hat = s q, [P3] §它改变缓存表示).  8-bit formats: code value times scale,
+ * one rounding.  NVFP4: E2M1 value times the E4M3 block scale (exact), times
+ * s_t (one rounding).  KVarN: rebuilt in the rotated basis, then rotated back
+ * (binary32, a few ulps).  Skipped slots (as in kvq_quantize_write) leave their
+ * rows untouched. */
+kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int64_t* slot_mapping,
+                          int64_t n_tok, float* k_out, float* v_out, void* stream);
+
+/* Static English description of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -422,9 +422,12 @@ void kvqo_kvarn_tile(const uint16_t* x16, int64_t stride, int side, float* y_rot
  * (page p, head h) starts at byte (p*H + h) * chunk_bytes.  Inside a chunk
  * (P = page_size, D = head_dim, t = token offset in the page, d = channel):
  *
- *  8-bit formats (FP8 per-tensor, INT8 / FP8 per-token-head):
- *    K codes  [P][D]        at 0:            byte t*D + d
- *    V codes  [P/4][D][4]   at P*D:          byte 4*D*(t/4) + 4*d + t%4
+ *  8-bit formats (FP8 per-tensor, INT8 / FP8 per-token-head): K and V each
+ *  take 16*D bytes per group of 16 tokens (u = t/16, s = t%16), at 16*D*u
+ *  inside their region; with B = min(16, D/4):
+ *    K codes  at 0:     d = (D/4)*g + B*h + e  ->  64*B*h + 16*B*g + B*s + e
+ *    V codes  at P*D:   d = (D/16)*n + c, c = (B/4)*h + j  ->
+ *                       64*B*h + 16*B*(s/4) + B*n + 4*j + s%4
  *    per-token-head only: K scales fp32 [P] at 2*P*D, V scales fp32 [P] after
  *  NVFP4 (in a byte the low nibble holds the first element):
  *    K codes  [P][D/2]      at 0:            byte t*D/2 + d/2, nibble d%2
@@ -481,6 +484,20 @@ static uint8_t* chunk_at(const kvqo_layout* L, const uint8_t* cache, int64_t pag
   return (uint8_t*)cache + (page * L->num_kv_heads + h) * kvqo_chunk_bytes(L);
 }
 
+/* Byte offsets of element (t, d) in the 8-bit K and V regions. */
+static int64_t k8_off(int D, int t, int d) {
+  int B = D / 4 < 16 ? D / 4 : 16;
+  int g = d / (D / 4), r = d % (D / 4), h = r / B, e = r % B;
+  int u = t / 16, s = t % 16;
+  return 16LL * D * u + 64 * B * h + 16 * B * g + B * s + e;
+}
+static int64_t v8_off(int D, int t, int d) {
+  int B = D / 4 < 16 ? D / 4 : 16;
+  int n = d / (D / 16), c = d % (D / 16), h = c / (B / 4), j = c % (B / 4);
+  int u = t / 16, s = t % 16;
+  return 16LL * D * u + 64 * B * h + 16 * B * (s / 4) + B * n + 4 * j + s % 4;
+}
+
 static void put_nibble(uint8_t* p, int hi, uint8_t v) {
   if (hi)
     *p = (uint8_t)((*p & 0x0F) | ((v & 15) << 4));
@@ -532,8 +549,8 @@ static void store_row(const kvqo_layout* L, uint8_t* ch, int t, const float* xk,
     uint8_t* kc = ch;
     uint8_t* vc = ch + (int64_t)P * D;
     for (int d = 0; d < D; d++) {
-      kc[(int64_t)t * D + d] = ck[d];
-      vc[4LL * D * (t / 4) + 4 * d + t % 4] = cv[d];
+      kc[k8_off(D, t, d)] = ck[d];
+      vc[v8_off(D, t, d)] = cv[d];
     }
     if (L->format != O_FP8_PER_TENSOR) {
       float* ksc = (float*)(ch + 2LL * P * D);
@@ -566,8 +583,8 @@ static void load_row(const kvqo_layout* L, const uint8_t* ch, int t, double* k, 
         sv = tmp[1];
       }
       for (int d = 0; d < D; d++) {
-        uint8_t a = kc[(int64_t)t * D + d];
-        uint8_t b = vc[4LL * D * (t / 4) + 4 * d + t % 4];
+        uint8_t a = kc[k8_off(D, t, d)];
+        uint8_t b = vc[v8_off(D, t, d)];
         double qa, qb;
         if (L->format == O_INT8_PTH) {
           qa = (double)(int8_t)a;

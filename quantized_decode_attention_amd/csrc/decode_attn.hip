@@ -1,0 +1,547 @@
+// decode_attn.hip -- dequant-fused paged GQA decode attention for FP8
+// per-tensor, INT8 / FP8 per-token-head and NVFP4 caches (gfx950).
+//
+// Computes O = softmax(q K^T * sm_scale) V for every (sequence, q head) with
+// the cache read through block tables ([P5] "NVFP4 KV Cache：Blackwell 上的
+// 4-bit 缓存量化", §K 与 V 的量化误差进入 attention 的位置不同 and §KV 的写入与
+// 读取路径: unpack, apply scales, feed the attention math inside the tile
+// load, never materialise a full-precision copy).
+//
+// Decomposition.  A workgroup of 4 wavefronts owns one (sequence, kv head,
+// context split); wave w walks pages w, w+4, ... of the split.  Per 16-token
+// sub-page a wave computes
+//   S^T[16 tok][16 cols] = K[16 tok][D] * Q^T[D][16 cols]   (D/32 MFMA 16x16x32 f16)
+//   O[16 rows][D]       += P[16 rows][16 tok] * V[16 tok][D] (D/16 MFMA 16x16x16 f16)
+// With K as the A operand the score tile lands in the registers in exactly
+// the layout the second MFMA wants for P (lane l: head l%16, tokens
+// 4*(l/16)..+3), so softmax needs no data movement between the two products.
+// The G query heads of the group occupy MFMA rows 0..G-1; rows G..2G-1 carry
+// the binary16 rounding remainder of P (P = hi + lo), which makes the PV
+// product accurate to ~2^-22 at no extra MFMA cost.  Codes are converted to
+// binary16 exactly (every format's values are binary16 numbers); per-token
+// scales fold into the scores (K) and into P (V), per-tensor / global scales
+// into the score scale and the final output.
+//
+// Cache layout in HBM is chosen for these operands: each lane's K bytes are
+// one contiguous run of D/4 codes of one token, and each lane's V bytes are
+// one contiguous run holding four consecutive tokens per channel, so loads
+// are 16-byte vectors that together cover whole 128-byte lines and need no
+// LDS staging.
+//
+// Splits: each workgroup writes its partial (m, l, O) to the workspace and a
+// second, small kernel merges the partials of every (sequence, kv head).
+#include <math.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kDepth = 4;  // 16-token units per wave: 1 in compute, kDepth-1 in flight
+constexpr int kPageChunk = 256;  // block-table entries staged in LDS at a time
+constexpr float kNegInf = -INFINITY;
+
+__device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d) {
+  half8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ half4_t cat4(half2_t a, half2_t b) {
+  half4_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  return r;
+}
+
+// Raw bytes of one 16-token unit for one lane, as loaded from the chunk.
+template <int FMT, int D>
+struct Raw {
+  static constexpr int KW = (FMT == 4) ? D / 32 : D / 16;  // dwords of K codes
+  static constexpr int VW = (FMT == 4) ? D / 32 : D / 16;  // dwords of V codes
+  uint32_t k[KW];
+  uint32_t v[VW];
+  uint32_t ksc, vsc;  // NVFP4 block-scale bytes (K: this token's blocks; V: 4 tokens)
+  float4 ks, vs;      // per-token-head scales of the lane's 4 score tokens
+};
+
+// The cache is streamed once per decode step: nontemporal loads keep it from
+// displacing reusable lines and measure ~8% faster than plain loads on MI355X.
+__device__ __forceinline__ uint32_t ld_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+__device__ __forceinline__ float4 ld_nt_f4(const uint8_t* p) {
+  const float* f = reinterpret_cast<const float*>(p);
+  return float4{__builtin_nontemporal_load(f), __builtin_nontemporal_load(f + 1), __builtin_nontemporal_load(f + 2),
+                __builtin_nontemporal_load(f + 3)};
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ void zero_raw(Raw<FMT, D>& r) {
+#pragma unroll
+  for (int i = 0; i < Raw<FMT, D>::KW; ++i) r.k[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < Raw<FMT, D>::VW; ++i) r.v[i] = 0u;
+  r.ksc = r.vsc = 0u;
+  r.ks = r.vs = float4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int N>
+__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = ld_nt(p + 4 * i);
+}
+
+// Issue the loads of unit `sub` (16 tokens) of a chunk.  K: D/4 channels of
+// token row n starting at channel (D/4)*gq; V: channels (D/16)*n .. +D/16 of
+// tokens 4*gq .. 4*gq+3.
+template <int FMT, int D>
+__device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom& g, int P, int sub, int gq, int n,
+                                          Raw<FMT, D>& r) {
+  constexpr int DL = D / 4;
+  constexpr int NV = D / 16;
+  const int tk = sub * 16 + n;
+  const int quad = sub * 4 + gq;
+  if constexpr (FMT != 4) {
+    // coalesced 8-bit layout: piece h of all 64 lanes is one contiguous run
+    constexpr int B = DL < 16 ? DL : 16;
+    const uint8_t* kp = chunk + (int64_t)16 * D * sub + 16 * B * gq + B * n;
+    const uint8_t* vp = chunk + g.v_codes + (int64_t)16 * D * sub + 16 * B * gq + B * n;
+#pragma unroll
+    for (int h = 0; h < DL / B; ++h) load_dwords<B / 4>(kp + 64 * B * h, r.k + (B / 4) * h);
+#pragma unroll
+    for (int h = 0; h < (4 * NV) / B; ++h) load_dwords<B / 4>(vp + 64 * B * h, r.v + (B / 4) * h);
+    if constexpr (FMT == 2 || FMT == 3) {
+      r.ks = ld_nt_f4(chunk + g.k_scales + 4 * (sub * 16 + 4 * gq));
+      r.vs = ld_nt_f4(chunk + g.v_scales + 4 * (sub * 16 + 4 * gq));
+    }
+  } else {
+    load_dwords<Raw<FMT, D>::KW>(chunk + (int64_t)tk * (D / 2) + (DL / 2) * gq, r.k);
+    const uint8_t* sp = chunk + g.k_scales + (int64_t)tk * (D / 16) + (DL * gq) / 16;
+    if constexpr (DL >= 32)
+      r.ksc = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp));
+    else
+      r.ksc = __builtin_nontemporal_load(sp);
+    load_dwords<Raw<FMT, D>::VW>(chunk + g.v_codes + (int64_t)2 * D * quad + 4 * ((NV * n) / 2), r.v);
+    r.vsc = ld_nt(chunk + g.v_scales + (int64_t)((NV * n) / 16) * P + 4 * quad);
+  }
+}
+
+// K operand for QK MFMA kk: 8 channels (D/4)*gq + 8*kk .. +7 of token row n.
+template <int FMT, int D>
+__device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2_t ksc) {
+  if constexpr (FMT != 4) {
+    half2_t a, b, c, d;
+    if constexpr (FMT == 2) {
+      // biased: binary16 1152 + code; the bias is removed from the scores
+      i8x4_to_h_biased(r.k[2 * kk], a, b);
+      i8x4_to_h_biased(r.k[2 * kk + 1], c, d);
+    } else {
+      e4m3x4_to_h(r.k[2 * kk], a, b);
+      e4m3x4_to_h(r.k[2 * kk + 1], c, d);
+    }
+    return cat(a, b, c, d);
+  } else {
+    constexpr int DL = D / 4;
+    const uint32_t x = r.k[kk];
+    const uint32_t hl = e2m1x4_hibytes(x & 0x0F0F0F0Fu);         // channels 0,2,4,6
+    const uint32_t hh = e2m1x4_hibytes((x >> 4) & 0x0F0F0F0Fu);  // channels 1,3,5,7
+    const half_t sc = ksc[(DL >= 32) ? (8 * kk) / 16 : 0];
+    const half2_t s2 = {sc, sc};
+    return cat(as_h2(perm(hh, hl, 0x040C000Cu)) * s2, as_h2(perm(hh, hl, 0x050C010Cu)) * s2,
+               as_h2(perm(hh, hl, 0x060C020Cu)) * s2, as_h2(perm(hh, hl, 0x070C030Cu)) * s2);
+  }
+}
+
+// V operand for PV MFMA nn: channel (D/16)*n + nn of tokens 4*gq .. +3.
+template <int FMT, int D>
+__device__ __forceinline__ half4_t v_operand(const Raw<FMT, D>& r, int nn, half2_t s01, half2_t s23) {
+  if constexpr (FMT != 4) {
+    half2_t a, b;
+    if constexpr (FMT == 2)
+      i8x4_to_h(r.v[nn], a, b);
+    else
+      e4m3x4_to_h(r.v[nn], a, b);
+    return cat4(a, b);
+  } else {
+    const uint32_t w = r.v[nn / 2];
+    const uint32_t h = e2m1x4_hibytes((nn & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu));
+    return cat4(as_h2(perm(0u, h, 0x010C000Cu)) * s01, as_h2(perm(0u, h, 0x030C020Cu)) * s23);
+  }
+}
+
+// Online-softmax state and accumulators of one wavefront.
+template <int D>
+struct WaveState {
+  float4_t acc[D / 16];
+  float m_run, l_run;
+};
+
+// Lazy rescaling: the weights P = 2^(score - m_run) * v_scale fed to the PV
+// product are kept relative to a reference m_run that only moves when some
+// weight would exceed 2^kTau, so the accumulators are rescaled a handful of
+// times per split instead of every time the running maximum creeps up, and
+// the common path needs no cross-lane maximum.  P <= 2^kTau keeps the binary16
+// operands far from overflow.
+constexpr float kTau = 8.0f;
+constexpr float kTauPow = 256.0f;
+
+// Lane l+G (within its 16-lane row) receives lane l's value: row_shr:G.
+template <int G>
+__device__ __forceinline__ uint32_t row_shr(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, 0x110 + G, 0xF, 0xF, false);
+}
+
+template <int FMT, int D, int G>
+__device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, int tok0, int ctx, int n, int gq,
+                                             int l, const half8_t* qB, float kconst, float kbias,
+                                             WaveState<D>& st) {
+  constexpr int NK = D / 32;
+  constexpr int NV = D / 16;
+  constexpr bool PTH = (FMT == 2 || FMT == 3);
+
+  half2_t ksc01 = {0, 0}, ksc23 = {0, 0};
+  if constexpr (FMT == 4) e4m3x4_to_h(r.ksc, ksc01, ksc23);
+  float4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<FMT, D>(r, kk, ksc01), qB[kk], s, 0, 0, 0);
+
+  // scores in log2 units; a unit wholly inside the context and on a valid
+  // page (the common case, uniform across the wave) needs no token masks.
+  // Lanes n >= G hold no head: their values are computed but never used.
+  float lg[4], vsc[4];
+  const bool full = valid && (tok0 + 16 <= ctx);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float c = PTH ? r.ks[i] * kconst : kconst;
+    lg[i] = (s[i] - kbias) * c;
+    vsc[i] = PTH ? r.vs[i] : 1.0f;
+  }
+  if (!full) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!(valid && tok0 + 4 * gq + i < ctx)) lg[i] = kNegInf;
+  }
+  float p[4], pv[4];
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool live = lg[i] != kNegInf;
+    p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
+    // select, not multiply: a masked token's scale slot may hold anything
+    pv[i] = live ? p[i] * vsc[i] : 0.0f;
+    over |= !(pv[i] <= kTauPow);
+  }
+  over = over && (n < G);
+  if (__any(over)) {
+    // move the reference to the exact maximum of score + log2(v_scale)
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lg[i] != kNegInf && n < G) mx = fmaxf(mx, PTH ? lg[i] + __log2f(vsc[i]) : lg[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = (m_new > st.m_run) ? exp2f(st.m_run - m_new) : 1.0f;
+    st.l_run *= alpha;
+    float ar[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * gq + i;
+      ar[i] = __shfl(alpha, row < G ? row : (row < 2 * G ? row - G : 0));
+    }
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[nn][i] *= ar[i];
+    st.m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool live = lg[i] != kNegInf;
+      p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
+      pv[i] = live ? p[i] * vsc[i] : 0.0f;
+    }
+  }
+
+  half4_t ph, plo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.l_run += p[i];
+    const half_t hh = (half_t)pv[i];
+    ph[i] = hh;
+    plo[i] = (half_t)(pv[i] - (float)hh);
+  }
+  // rows G..2G-1 carry the binary16 remainder of rows 0..G-1
+  const uint2 lob = __builtin_bit_cast(uint2, plo);
+  uint2 shifted;
+  shifted.x = row_shr<G>(lob.x);
+  shifted.y = row_shr<G>(lob.y);
+  half4_t pA;
+  if (n < G)
+    pA = ph;
+  else if (n < 2 * G)
+    pA = __builtin_bit_cast(half4_t, shifted);
+  else
+    pA = half4_t{0, 0, 0, 0};
+
+  half2_t vs01 = {0, 0}, vs23 = {0, 0};
+  if constexpr (FMT == 4) e4m3x4_to_h(r.vsc, vs01, vs23);
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn)
+    st.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand<FMT, D>(r, nn, vs01, vs23), st.acc[nn], 0, 0, 0);
+}
+
+template <int FMT, int D, int G>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  constexpr int NK = D / 32;
+  constexpr int NV = D / 16;
+  constexpr int DL = D / 4;
+
+  __shared__ float lds_o[kWaves][2 * G][D];
+  __shared__ float lds_m[kWaves][16];
+  __shared__ float lds_l[kWaves][16];
+  __shared__ int s_pages[kPageChunk];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, gq = l >> 4;
+  const int P = a.P;
+  const int S = a.num_splits;
+
+  float* partials = reinterpret_cast<float*>(a.workspace);
+  const int64_t rec_floats = ws_record_floats(D);
+
+  // wave-uniform bounds (kept in scalar registers)
+  int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
+  const int n_pages = (ctx + P - 1) / P;
+  const int p_begin = split * a.pages_per_split;
+  const int p_end = min(p_begin + a.pages_per_split, n_pages);
+
+  // Q^T as the B operand: column n = head kvh*G + n, rows = channels DL*gq + 8kk + 0..7
+  half8_t qB[NK];
+  if (n < G) {
+    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + n) * D + DL * gq;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qB[kk] = *reinterpret_cast<const half8_t*>(qp + 8 * kk);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qB[kk] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  const float kconst = (FMT == 1 || FMT == 4) ? a.k_scale * a.qk_scale : a.qk_scale;
+  // INT8 keys enter the MFMA as binary16 1152 + code: remove 1152 * sum(q)
+  float kbias = 0.0f;
+  if constexpr (FMT == 2) {
+    float qs = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qs += (float)qB[kk][e];
+    qs += __shfl_xor(qs, 16);
+    qs += __shfl_xor(qs, 32);
+    kbias = 1152.0f * qs;
+  }
+  WaveState<D> st;
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn) st.acc[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
+  st.m_run = kNegInf;
+  st.l_run = 0.0f;
+
+  // This wave's pages: p_begin + w + 4*j, j < n_it.  Their block-table
+  // entries are fetched 64 at a time into one VGPR (lane j holds entry j) and
+  // read with readlane, so no load sits between consecutive pages.  Units of
+  // 16 tokens are double-buffered: the next unit's bytes are in flight while
+  // the current one is computed.
+  const int sp_shift = a.sp_shift;  // P / 16 == 1 << sp_shift
+  const int sp_mask = (1 << sp_shift) - 1;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_pages;
+  const uint8_t* head_base = a.cache + (int64_t)kvh * a.geom.chunk_bytes;
+  const int64_t page_stride = (int64_t)a.H * a.geom.chunk_bytes;
+
+  // The split's block-table entries are staged in LDS, kPageChunk at a time,
+  // by the whole workgroup; wave w then walks pages w, w+4, ... of the chunk.
+  // Reading a page index from LDS involves no vector-memory counter, so it
+  // never forces a wait on the data loads in flight.
+  for (int c0 = p_begin; c0 < p_end; c0 += kPageChunk) {
+    const int nc = min(kPageChunk, p_end - c0);
+    __syncthreads();
+    for (int i = tid; i < nc; i += 256) s_pages[i] = bt[c0 + i];
+    __syncthreads();
+    const int nj = w < nc ? (nc - w + kWaves - 1) / kWaves : 0;  // this wave's pages
+    const int nu = nj << sp_shift;
+    if (nu == 0) continue;
+    // the unit count is padded to a whole number of ring turns; padded units
+    // are masked out, so the loop body has no data-dependent branches
+    const int nu_pad = (nu + kDepth - 1) / kDepth * kDepth;
+    auto unit_page = [&](int u, bool& valid) {
+      const int page = __builtin_amdgcn_readfirstlane(s_pages[w + kWaves * (u >> sp_shift)]);
+      valid = page >= 0 && page < a.num_pages;
+      return head_base + (valid ? page : 0) * page_stride;
+    };
+    auto unit_tok0 = [&](int u) { return (c0 + w + kWaves * (u >> sp_shift)) * P + (u & sp_mask) * 16; };
+
+    // Units are prefetched kDepth-1 ahead into a ring of register buffers;
+    // the loop is unrolled by kDepth so every ring slot is a fixed set of
+    // registers.  There is no separate prologue: the ring starts zeroed and
+    // the first kDepth-1 steps process masked placeholder units, so the only
+    // loads pending at the loop header are the loop's own and the compiler
+    // waits for exactly the unit about to be used.  Loads stay unconditional
+    // (past the end they reload the last unit: in bounds, unused).
+    Raw<FMT, D> rr[kDepth];
+    bool vv[kDepth];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      zero_raw(rr[k]);
+      vv[k] = false;
+    }
+    for (int u = 0; u < nu_pad + kDepth; u += kDepth) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        const int ul = min(u + k, nu - 1);      // unit loaded now
+        const int up = u + k - (kDepth - 1);    // unit processed now
+        const int ls = k;                        // its ring slots
+        const int ps = (k + 1) % kDepth;
+        load_unit<FMT, D>(unit_page(ul, vv[ls]), a.geom, P, ul & sp_mask, gq, n, rr[ls]);
+        const bool live = vv[ps] && up >= 0 && up < nu;
+        process_unit<FMT, D, G>(rr[ps], live, unit_tok0(up < 0 ? 0 : up), ctx, n, gq, l, qB, kconst, kbias, st);
+      }
+    }
+  }
+
+  // ---- combine the four waves (and the hi/lo rows) in LDS
+  float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (gq == 0) {
+    lds_m[w][n] = st.m_run;
+    lds_l[w][n] = l_tot;
+  }
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * gq + i;
+      if (row < 2 * G) lds_o[w][row][NV * n + nn] = st.acc[nn][i];
+    }
+  __syncthreads();
+
+  const float post = (FMT == 1 || FMT == 4) ? a.v_scale : 1.0f;
+  float* rec = partials + (((int64_t)b * a.H + kvh) * S + split) * rec_floats;
+  for (int i = tid; i < G * D; i += 256) {
+    const int g = i / D, d = i % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, lds_m[ww][g]);
+    float L = 0.0f, O = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = exp2f(lds_m[ww][g] - M);
+        L += f * lds_l[ww][g];
+        O += f * (lds_o[ww][g][d] + lds_o[ww][g + G][d]);
+      }
+    }
+    if (S == 1) {
+      const float o = L > 0.0f ? O / L * post : 0.0f;
+      a.out[((int64_t)b * a.Hq + kvh * G + g) * D + d] = __builtin_bit_cast(uint16_t, (half_t)o);
+    } else {
+      if (d == 0) {
+        rec[g] = M;
+        rec[kMaxGroup + g] = L;
+      }
+      rec[2 * kMaxGroup + g * D + d] = O;
+    }
+  }
+}
+
+// Merge of the context splits of one (sequence, q head): m = max m_s,
+// l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l.  A separate launch:
+// the kernel boundary makes every split's partial visible on all XCDs
+// without device-wide cache maintenance inside the split kernel.  One
+// wavefront per output row: the split maxima and sums are read in parallel
+// and wave-reduced, then the weighted rows are summed with independent loads.
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int D, float post) {
+  __shared__ float wts[kMaxSplits];
+  const int kvh = blockIdx.x, b = blockIdx.y, g = blockIdx.z;
+  const int S = a.num_splits;
+  const int lane = threadIdx.x;
+  const int64_t rf = ws_record_floats(D);
+  const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
+
+  float M = kNegInf;
+  for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, recs[sp * rf + g]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+  float L = 0.0f;
+  for (int sp = lane; sp < S; sp += 64) {
+    const float ms = recs[sp * rf + g];
+    const float f = (M == kNegInf) ? 0.0f : exp2f(ms - M);
+    wts[sp] = f;
+    L += f * recs[sp * rf + kMaxGroup + g];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
+  __syncthreads();
+  const float inv = L > 0.0f ? post / L : 0.0f;
+  uint16_t* orow = a.out + ((int64_t)b * a.Hq + kvh * a.G + g) * D;
+  for (int d = lane; d < D; d += 64) {
+    const float* col = recs + 2 * kMaxGroup + g * D + d;
+    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+    int sp = 0;
+    for (; sp + 4 <= S; sp += 4) {
+      o0 += wts[sp] * col[sp * rf];
+      o1 += wts[sp + 1] * col[(sp + 1) * rf];
+      o2 += wts[sp + 2] * col[(sp + 2) * rf];
+      o3 += wts[sp + 3] * col[(sp + 3) * rf];
+    }
+    for (; sp < S; ++sp) o0 += wts[sp] * col[sp * rf];
+    const float o = ((o0 + o1) + (o2 + o3)) * inv;
+    orow[d] = __builtin_bit_cast(uint16_t, (half_t)o);
+  }
+}
+
+template <int FMT, int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.num_splits, (unsigned)a.H, (unsigned)a.B);
+  switch (a.G) {
+    case 1: decode_kernel<FMT, D, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: decode_kernel<FMT, D, 2><<<grid, 256, 0, s>>>(a); break;
+    case 4: decode_kernel<FMT, D, 4><<<grid, 256, 0, s>>>(a); break;
+    case 8: decode_kernel<FMT, D, 8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const DecodeArgs& a, hipStream_t s) {
+  switch (a.D) {
+    case 32: return launch_d<FMT, 32>(a, s);
+    case 64: return launch_d<FMT, 64>(a, s);
+    case 128: return launch_d<FMT, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  hipError_t e = hipErrorInvalidValue;
+  switch (fmt) {
+    case 1: e = launch_fmt<1>(a, s); break;
+    case 2: e = launch_fmt<2>(a, s); break;
+    case 3: e = launch_fmt<3>(a, s); break;
+    case 4: e = launch_fmt<4>(a, s); break;
+  }
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const float post = (fmt == 1 || fmt == 4) ? a.v_scale : 1.0f;
+  decode_merge_kernel<<<dim3((unsigned)a.H, (unsigned)a.B, (unsigned)a.G), 64, 0, s>>>(a, a.D, post);
+  return hipGetLastError();
+}
+
+
+}  // namespace kvq

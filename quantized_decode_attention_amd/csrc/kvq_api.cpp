@@ -1,0 +1,270 @@
+// kvq_api.cpp -- the C ABI of libkvq: argument validation, page geometry,
+// split planning and kernel dispatch.  See include/kvq.h for the contract.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool valid_scale(float s) { return isfinite(s) && s >= 0x1p-64f && s <= 0x1p64f; }
+
+// Layout check shared by every entry point.
+kvq_status check_layout(const kvq_layout* L) {
+  if (!L) return KVQ_ERR_INVALID_ARG;
+  if (L->num_kv_heads < 1 || L->num_pages < 1 || L->head_dim < 1 || L->page_size < 1)
+    return KVQ_ERR_INVALID_ARG;
+  switch (L->format) {
+    case KVQ_FP8_PER_TENSOR:
+    case KVQ_INT8_PTH:
+    case KVQ_FP8_PTH:
+    case KVQ_NVFP4:
+      if (L->head_dim != 32 && L->head_dim != 64 && L->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+      if (L->page_size < 16 || L->page_size > 256 || (L->page_size & (L->page_size - 1))) return KVQ_ERR_UNSUPPORTED;
+      break;
+    case KVQ_KVARN_K4V2_G128:
+      if (L->head_dim != 128 || L->page_size != 128) return KVQ_ERR_UNSUPPORTED;
+      break;
+    default:
+      return KVQ_ERR_UNSUPPORTED;
+  }
+  if (L->flags & ~KVQ_FLAG_NVFP4_4OVER6) return KVQ_ERR_INVALID_ARG;
+  if ((L->flags & KVQ_FLAG_NVFP4_4OVER6) && L->format != KVQ_NVFP4) return KVQ_ERR_INVALID_ARG;
+  if ((L->format == KVQ_FP8_PER_TENSOR || L->format == KVQ_NVFP4) &&
+      !(valid_scale(L->k_scale) && valid_scale(L->v_scale)))
+    return KVQ_ERR_INVALID_ARG;
+  return KVQ_OK;
+}
+
+ChunkGeom geometry(const kvq_layout* L) {
+  const int64_t D = L->head_dim, P = L->page_size;
+  ChunkGeom g{};
+  switch (L->format) {
+    case KVQ_FP8_PER_TENSOR:
+      g.v_codes = P * D;
+      g.k_scales = g.v_scales = 2 * P * D;
+      g.chunk_bytes = 2 * P * D;
+      break;
+    case KVQ_INT8_PTH:
+    case KVQ_FP8_PTH:
+      g.v_codes = P * D;
+      g.k_scales = 2 * P * D;
+      g.v_scales = 2 * P * D + 4 * P;
+      g.chunk_bytes = 2 * P * D + 8 * P;
+      break;
+    case KVQ_NVFP4:
+      g.v_codes = P * D / 2;
+      g.k_scales = P * D;
+      g.v_scales = P * D + P * D / 16;
+      g.chunk_bytes = P * D + P * D / 8;
+      break;
+    case KVQ_KVARN_K4V2_G128:
+      g.v_codes = P * D / 2;
+      g.k_scales = P * D / 2 + P * D / 4;  // start of the fp32 metadata
+      g.v_scales = g.k_scales + 4 * (2 * D + P);
+      g.chunk_bytes = P * D / 2 + P * D / 4 + 4 * (3 * D + 3 * P);
+      break;
+  }
+  return g;
+}
+
+// Device capability, cached per device id (0 = unknown, 1 = gfx950, 2 = other).
+std::atomic<int> g_dev_ok[64];
+
+kvq_status device_ok(int dev) {
+  if (dev < 0) return KVQ_ERR_DEVICE;
+  if (dev < 64) {
+    const int c = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (c) return c == 1 ? KVQ_OK : KVQ_ERR_DEVICE;
+  }
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || dev >= count) return KVQ_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KVQ_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
+kvq_status current_device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_DEVICE;
+  return device_ok(dev);
+}
+
+kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+// Context splits per (sequence, kv head): enough workgroups to give each of
+// the 256 compute units about four, while keeping at least 8 pages (two per
+// wavefront) in a split.  Empty trailing splits are dropped.
+void plan_splits(int batch, int H, int max_pages, int hint, int* splits, int* pages_per_split) {
+  const int64_t units = (int64_t)batch * H;
+  int s = hint;
+  if (s <= 0) {
+    const int64_t want = units > 0 ? (1024 + units - 1) / units : 1;
+    const int64_t cap = (max_pages + 7) / 8;
+    s = (int)(want < cap ? want : cap);
+  }
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > max_pages) s = max_pages;
+  if (s < 1) s = 1;
+  int pps = (max_pages + s - 1) / s;
+  if (pps < 1) pps = 1;
+  *pages_per_split = pps;
+  *splits = (max_pages + pps - 1) / pps;
+  if (*splits < 1) *splits = 1;
+}
+
+int64_t workspace_bytes_for(const kvq_layout* L, int batch, int splits) {
+  if (splits <= 1) return 0;
+  return (int64_t)batch * L->num_kv_heads * splits * ws_record_floats(L->head_dim) * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kvq_page_bytes(const kvq_layout* layout) {
+  if (check_layout(layout) != KVQ_OK) return -1;
+  return geometry(layout).chunk_bytes * layout->num_kv_heads;
+}
+
+kvq_status kvq_check_device(int hip_device) { return device_ok(hip_device); }
+
+kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const void* v,
+                              const int64_t* slot_mapping, int64_t n_tok, void* cache, void* stream) {
+  kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (n_tok < 0) return KVQ_ERR_INVALID_ARG;
+  if (layout->format == KVQ_KVARN_K4V2_G128 && n_tok % 128 != 0) return KVQ_ERR_INVALID_ARG;
+  if (n_tok > 0 && (!k || !v || !slot_mapping || !cache)) return KVQ_ERR_INVALID_ARG;
+  if ((st = current_device_ok()) != KVQ_OK) return st;
+  if (n_tok == 0) return KVQ_OK;
+  WriteArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.slots = slot_mapping;
+  a.n_tok = n_tok;
+  a.cache = static_cast<uint8_t*>(cache);
+  a.geom = geometry(layout);
+  a.H = layout->num_kv_heads;
+  a.D = layout->head_dim;
+  a.P = layout->page_size;
+  a.num_pages = layout->num_pages;
+  a.k_scale = layout->k_scale;
+  a.v_scale = layout->v_scale;
+  a.flags = layout->flags;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_UNSUPPORTED;  // not built yet
+  return from_hip(launch_quant_write(layout->format, a, s));
+}
+
+int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t max_pages_per_seq,
+                              int32_t num_splits) {
+  if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0) return -1;
+  int s, pps;
+  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits, &s, &pps);
+  return s;
+}
+
+int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                   int32_t max_pages_per_seq, int32_t num_splits) {
+  if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0 ||
+      num_q_heads < 1)
+    return -1;
+  int s, pps;
+  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits, &s, &pps);
+  return workspace_bytes_for(layout, batch, s);
+}
+
+kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, const void* q,
+                                int32_t num_q_heads, const int32_t* block_tables, int32_t max_pages_per_seq,
+                                const int32_t* context_lens, int32_t batch, float sm_scale,
+                                const void* kvarn_tail, void* out, void* workspace, int64_t workspace_bytes,
+                                int32_t num_splits, void* stream) {
+  kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  const int H = layout->num_kv_heads;
+  if (batch < 0 || num_q_heads < 1 || max_pages_per_seq < 1 || num_splits < 0 || !isfinite(sm_scale))
+    return KVQ_ERR_INVALID_ARG;
+  if (num_q_heads % H != 0) return KVQ_ERR_INVALID_ARG;
+  const int G = num_q_heads / H;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
+  if (kvarn_tail && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
+  if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
+  int splits, pps;
+  plan_splits(batch, H, max_pages_per_seq, num_splits, &splits, &pps);
+  const int64_t need = workspace_bytes_for(layout, batch, splits);
+  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;
+  if ((st = current_device_ok()) != KVQ_OK) return st;
+  if (batch == 0) return KVQ_OK;
+  DecodeArgs a{};
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.geom = geometry(layout);
+  a.H = H;
+  a.D = layout->head_dim;
+  a.P = layout->page_size;
+  a.num_pages = layout->num_pages;
+  a.q = static_cast<const uint16_t*>(q);
+  a.Hq = num_q_heads;
+  a.G = G;
+  a.block_tables = block_tables;
+  a.max_pages = max_pages_per_seq;
+  a.ctx_lens = context_lens;
+  a.B = batch;
+  a.qk_scale = sm_scale * 1.4426950408889634f;
+  a.k_scale = layout->k_scale;
+  a.v_scale = layout->v_scale;
+  a.tail = static_cast<const uint16_t*>(kvarn_tail);
+  a.out = static_cast<uint16_t*>(out);
+  a.workspace = static_cast<uint8_t*>(workspace);
+  a.num_splits = splits;
+  a.pages_per_split = pps;
+  a.sp_shift = __builtin_ctz(layout->page_size / 16);
+  if (layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_UNSUPPORTED;  // not built yet
+  return from_hip(launch_decode(layout->format, a, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int64_t* slot_mapping,
+                          int64_t n_tok, float* k_out, float* v_out, void* stream) {
+  kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (n_tok < 0) return KVQ_ERR_INVALID_ARG;
+  if (n_tok > 0 && (!cache || !slot_mapping || !k_out || !v_out)) return KVQ_ERR_INVALID_ARG;
+  if ((st = current_device_ok()) != KVQ_OK) return st;
+  if (n_tok == 0) return KVQ_OK;
+  WriteArgs a{};
+  a.slots = slot_mapping;
+  a.n_tok = n_tok;
+  a.cache = static_cast<uint8_t*>(const_cast<void*>(cache));
+  a.geom = geometry(layout);
+  a.H = layout->num_kv_heads;
+  a.D = layout->head_dim;
+  a.P = layout->page_size;
+  a.num_pages = layout->num_pages;
+  a.k_scale = layout->k_scale;
+  a.v_scale = layout->v_scale;
+  if (layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_UNSUPPORTED;  // not built yet
+  return from_hip(launch_dequant(layout->format, a, k_out, v_out, static_cast<hipStream_t>(stream)));
+}
+
+const char* kvq_status_string(kvq_status status) {
+  switch (status) {
+    case KVQ_OK: return "success";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported layout or shape";
+    case KVQ_ERR_WORKSPACE_TOO_SMALL: return "decode workspace too small";
+    case KVQ_ERR_DEVICE: return "current device is not an MI355X (gfx950)";
+    case KVQ_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// kvq_internal.h -- launch interfaces between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// Byte offsets inside one (page, kv head) chunk; see the layout in kvq.h.
+struct ChunkGeom {
+  int64_t chunk_bytes;
+  int64_t v_codes;   // start of the V codes
+  int64_t k_scales;  // start of the K scales (per-token-head) / K block scales (NVFP4)
+  int64_t v_scales;  // start of the V scales / V block scales
+};
+
+struct WriteArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int64_t* slots;
+  int64_t n_tok;
+  uint8_t* cache;
+  ChunkGeom geom;
+  int H, D, P, num_pages;
+  float k_scale, v_scale;
+  int flags;
+};
+
+struct DecodeArgs {
+  const uint8_t* cache;
+  ChunkGeom geom;
+  int H, D, P, num_pages;
+  const uint16_t* q;
+  int Hq, G;
+  const int32_t* block_tables;
+  int max_pages;
+  const int32_t* ctx_lens;
+  int B;
+  float qk_scale;  // sm_scale * log2(e)
+  float k_scale, v_scale;
+  const uint16_t* tail;  // KVarN incomplete-tile tokens, or null
+  uint16_t* out;
+  uint8_t* workspace;
+  int num_splits;
+  int pages_per_split;
+  int sp_shift;  // log2(P / 16)
+};
+
+// Workspace: one partial record (m[8], l[8], o[8][D]) per (sequence, kv head,
+// split); no workspace is needed when there is a single split.
+constexpr int kMaxGroup = 8;    // q heads per kv head served by one decode wave
+constexpr int kMaxSplits = 256; // context splits per (sequence, kv head)
+
+__host__ __device__ inline int64_t ws_record_floats(int D) { return 2 * kMaxGroup + (int64_t)kMaxGroup * D; }
+
+hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s);
+hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s);
+hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,250 @@
+// quant_write.hip -- quantise-on-write for FP8 per-tensor, INT8 / FP8
+// per-token-head and NVFP4 (gfx950).
+//
+// Write path of [P5] "NVFP4 KV Cache：Blackwell 上的 4-bit 缓存量化",
+// §KV 的写入与读取路径 (compute scales, round and clip, pack, write payload and
+// scale metadata into the page) and of [P4] "KV 量化", §写和读 (divide by the
+// scale, convert, keep the bits as bytes).
+//
+// Work mapping: one token-head row (D binary16 values of K or V) is handled by
+// a group of lanes inside a wavefront -- D/8 lanes of 8 values for the 8-bit
+// formats, D/16 lanes of one 16-value block for NVFP4 -- so each lane issues
+// 16-byte loads and the row max is a short cross-lane max.  Rows are ordered
+// [side][token][head], so a wavefront reads consecutive rows of the input.
+// This file is built with -ffp-contract=off: every binary32 operation below
+// rounds exactly as written.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kBlock = 256;
+
+// Maps a lane to its row; returns false when the row is out of range or its
+// slot is skipped (the whole lane group agrees).
+struct RowCtx {
+  int side;
+  int64_t r;  // row within its side: token * H + head
+  int h, t;
+  uint8_t* chunk;
+};
+
+__device__ __forceinline__ bool row_ctx(const WriteArgs& a, int64_t row, RowCtx& c) {
+  const int64_t per_side = a.n_tok * a.H;
+  if (row >= 2 * per_side) return false;
+  c.side = row >= per_side;
+  c.r = c.side ? row - per_side : row;
+  const int64_t tok = c.r / a.H;
+  c.h = (int)(c.r - tok * a.H);
+  const int64_t slot = a.slots[tok];
+  if (slot < 0 || slot >= (int64_t)a.num_pages * a.P) return false;
+  const int64_t page = slot / a.P;
+  c.t = (int)(slot - page * a.P);
+  c.chunk = a.cache + (page * a.H + c.h) * a.geom.chunk_bytes;
+  return true;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = W / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, W));
+  return v;
+}
+
+__device__ __forceinline__ void load_halves8(const uint16_t* p, float* x) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    half2_t h = as_h2(w[i]);
+    x[2 * i] = (float)h[0];
+    x[2 * i + 1] = (float)h[1];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit formats: FMT 1 = FP8 per-tensor, 2 = INT8 per-token-head,
+// 3 = FP8 per-token-head.
+// ---------------------------------------------------------------------------
+template <int FMT, int D>
+__global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = kBlock / LPR;
+  const int j = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  RowCtx c;
+  if (!row_ctx(a, row, c)) return;
+
+  float x[8];
+  load_halves8((c.side ? a.v : a.k) + c.r * D + 8 * j, x);
+
+  float s;
+  if constexpr (FMT == 1) {
+    s = c.side ? a.v_scale : a.k_scale;
+  } else {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = group_max<LPR>(amax);
+    // [P3] §可运行 fake-quant 实验: floor the max at 1e-8, then divide by the
+    // top code (127 for INT8, FP8_MAX = 448 for E4M3, [P1] §2.2)
+    s = fmaxf(amax, 1e-8f) / (FMT == 2 ? 127.0f : 448.0f);
+  }
+  const Recip rc = make_recip(s);
+
+  uint32_t code[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = div_rn(x[i], s, rc);
+    if constexpr (FMT == 2) {
+      const float q = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+      code[i] = (uint32_t)(int32_t)q & 0xFFu;
+    } else {
+      code[i] = e4m3_mag(fabsf(y)) | (sign_bit(x[i]) << 7);
+    }
+  }
+
+  // 16-token groups of K and V are laid out in the decode's operand order
+  // (see k8_offset / v8_offset)
+  if (c.side == 0) {
+    uint2 packed;
+    packed.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    *reinterpret_cast<uint2*>(c.chunk + k8_offset<D>(c.t, 8 * j)) = packed;
+  } else {
+    uint8_t* vp = c.chunk + a.geom.v_codes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vp[v8_offset<D>(c.t, 8 * j + i)] = (uint8_t)code[i];
+  }
+  if (FMT != 1 && j == 0) {
+    float* sp = reinterpret_cast<float*>(c.chunk + a.geom.k_scales) + c.side * a.P + c.t;
+    *sp = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 ([P5] §双层缩放怎样恢复动态范围): one lane per 16-value block.
+// ---------------------------------------------------------------------------
+
+// Codes of one block for block-scale code sb, with the squared reconstruction
+// error summed by the balanced tree over the block's index order.
+__device__ __forceinline__ float nvfp4_block(const float* x, float st, uint32_t sb, uint32_t* code) {
+  const float sbv = e4m3_val(sb);
+  float e2[16];
+  if (sbv == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      code[i] = 0;
+      e2[i] = x[i] * x[i];
+    }
+  } else {
+    const float d = st * sbv;
+    const Recip rc = make_recip(d);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float y = div_rn(x[i], d, rc);
+      const uint32_t m = e2m1_mag(fabsf(y));
+      const uint32_t sgn = sign_bit(x[i]);
+      code[i] = m | (sgn << 3);
+      const float v = sgn ? -e2m1_val(m) : e2m1_val(m);
+      const float e = x[i] - d * v;
+      e2[i] = e * e;
+    }
+  }
+#pragma unroll
+  for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * w) e2[i] = e2[i] + e2[i + w];
+  return e2[0];
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
+  constexpr int LPR = D / 16;
+  constexpr int RPB = kBlock / LPR;
+  const int j = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  RowCtx c;
+  if (!row_ctx(a, row, c)) return;
+
+  float x[16];
+  const uint16_t* src = (c.side ? a.v : a.k) + c.r * D + 16 * j;
+  load_halves8(src, x);
+  load_halves8(src + 8, x + 8);
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float st = c.side ? a.v_scale : a.k_scale;
+
+  // block scale: the block max lands near 6, the top of the E2M1 grid
+  uint32_t sb = e4m3_mag((amax / 6.0f) / st);
+  uint32_t code[16];
+  const float err6 = nvfp4_block(x, st, sb, code);
+  if (a.flags & 1) {
+    // 4over6 ([P5] §用一组数直观看缩放的作用): keep max/4 if strictly better
+    const uint32_t sb4 = e4m3_mag((amax / 4.0f) / st);
+    uint32_t code4[16];
+    const float err4 = nvfp4_block(x, st, sb4, code4);
+    if (err4 < err6) {
+      sb = sb4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = code4[i];
+    }
+  }
+
+  uint32_t byte[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) byte[i] = code[2 * i] | (code[2 * i + 1] << 4);
+  if (c.side == 0) {
+    uint2 packed;
+    packed.x = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
+    packed.y = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
+    *reinterpret_cast<uint2*>(c.chunk + (int64_t)c.t * (D / 2) + 8 * j) = packed;
+    c.chunk[a.geom.k_scales + (int64_t)c.t * (D / 16) + j] = (uint8_t)sb;
+  } else {
+    // V: byte (quad, channel pair, token) so that each byte belongs to one token
+    uint8_t* vp = c.chunk + a.geom.v_codes + 2 * D * (c.t / 4) + 32 * j + (c.t % 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vp[4 * i] = (uint8_t)byte[i];
+    c.chunk[a.geom.v_scales + (int64_t)j * a.P + c.t] = (uint8_t)sb;
+  }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
+  const int64_t rows = 2 * a.n_tok * a.H;
+  if (rows == 0) return hipSuccess;
+  auto grid = [&](int lpr) { return dim3((unsigned)((rows + kBlock / lpr - 1) / (kBlock / lpr))); };
+  if constexpr (FMT == 4) {
+    switch (a.D) {
+      case 32: quant_write_nvfp4<32><<<grid(2), kBlock, 0, s>>>(a); break;
+      case 64: quant_write_nvfp4<64><<<grid(4), kBlock, 0, s>>>(a); break;
+      case 128: quant_write_nvfp4<128><<<grid(8), kBlock, 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.D) {
+      case 32: quant_write_8bit<FMT, 32><<<grid(4), kBlock, 0, s>>>(a); break;
+      case 64: quant_write_8bit<FMT, 64><<<grid(8), kBlock, 0, s>>>(a); break;
+      case 128: quant_write_8bit<FMT, 128><<<grid(16), kBlock, 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s) {
+  switch (fmt) {
+    case 1: return launch_fmt<1>(a, s);
+    case 2: return launch_fmt<2>(a, s);
+    case 3: return launch_fmt<3>(a, s);
+    case 4: return launch_fmt<4>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -19,3 +19,14 @@ def pytest_configure(config):
 def O():
     import oracle
     return oracle.default()
+
+
+@pytest.fixture(scope="session")
+def K():
+    """The product library; built in-tree first if nothing is built yet."""
+    lib = os.path.join(ROOT, "quantized_decode_attention_amd", "libkvq.so")
+    if not os.path.exists(lib):
+        from quantized_decode_attention_amd import _build
+        _build.build()
+    import quantized_decode_attention_amd as K
+    return K

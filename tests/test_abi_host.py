@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+public header declares, sizes pages exactly as the oracle does, and rejects
+invalid requests before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(K):
+    syms = declared_symbols()
+    assert len(syms) >= 8
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), f"{s} declared in include/kvq.h but not exported"
+
+
+def _layouts():
+    for fmt in (1, 2, 3, 4):
+        for D in (32, 64, 128):
+            for P in (16, 32, 64, 128, 256):
+                yield fmt, 0, 3, D, P
+    yield 4, 1, 8, 128, 16
+    yield 5, 0, 8, 128, 128
+
+
+@pytest.mark.parametrize("fmt,flags,H,D,P", list(_layouts()))
+def test_page_bytes_match_oracle(K, fmt, flags, H, D, P):
+    lay = K.layout(fmt, H, D, P, 10, 0.5, 0.25, flags)
+    olay = oracle.layout(fmt, H, D, P, 10, 0.5, 0.25, flags)
+    assert K.kvq_page_bytes(lay) == oracle.default().page_bytes(olay) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(fmt=0), dict(fmt=6), dict(D=96), dict(D=256), dict(P=8), dict(P=24), dict(P=48), dict(P=512), dict(H=0),
+    dict(pages=0), dict(fmt=5, P=16), dict(fmt=5, D=64), dict(flags=1), dict(flags=2, fmt=4),
+    dict(fmt=1, ks=0.0), dict(fmt=1, ks=float("inf")), dict(fmt=4, vs=-1.0), dict(fmt=4, vs=1e-30),
+])
+def test_invalid_layouts_rejected(K, bad):
+    a = dict(fmt=2, H=4, D=128, P=16, pages=4, ks=1.0, vs=1.0, flags=0)
+    a.update(bad)
+    lay = K.layout(a["fmt"], a["H"], a["D"], a["P"], a["pages"], a["ks"], a["vs"], a["flags"])
+    assert K.kvq_page_bytes(lay) == -1
+    assert K.kvq_decode_workspace_bytes(lay, 2, 4, 4) == -1
+    st = K.lib.kvq_quantize_write(ctypes.byref(lay), None, None, None, 0, None, None)
+    assert st in (1, 2)
+
+
+def test_argument_errors_before_launch(K):
+    lay = K.layout(2, 4, 128, 16, 4)
+    L = K.lib
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert L.kvq_quantize_write(None, p, p, p, 1, p, None) == 1
+    assert L.kvq_quantize_write(ctypes.byref(lay), p, p, p, -1, p, None) == 1
+    assert L.kvq_quantize_write(ctypes.byref(lay), None, p, p, 1, p, None) == 1
+    klay = K.layout(5, 4, 128, 128, 4)
+    assert L.kvq_quantize_write(ctypes.byref(klay), p, p, p, 100, p, None) == 1  # not whole tiles
+    # decode: GQA group must divide and be <= 8
+    ws = K.kvq_decode_workspace_bytes(lay, 2, 8, 4)
+    assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 6, p, 4, p, 2, 0.1, None, p, p, ws, 0, None) == 1
+    assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 64, p, 4, p, 2, 0.1, None, p, p, 1 << 30, 0, None) == 2
+    assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 8, p, 4, p, 2, 0.1, p, p, p, ws, 0, None) == 1  # tail
+    assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 8, p, 4, p, 2, 0.1, None, p, p, ws - 1, 0, None) == 3
+    assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 8, p, 4, p, 2, float("nan"), None, p, p, ws, 0, None) == 1
+    assert L.kvq_dequantize(ctypes.byref(lay), None, p, 1, p, p, None) == 1
+
+
+def test_split_plan_and_workspace(K):
+    lay = K.layout(2, 8, 128, 16, 16384)
+    # one MI355X: about four workgroups per compute unit
+    assert K.kvq_decode_num_splits(lay, 8, 2048) == 16
+    assert K.kvq_decode_num_splits(lay, 32, 256) == 4
+    assert K.kvq_decode_num_splits(lay, 2, 1) == 1
+    assert K.kvq_decode_num_splits(lay, 2, 10, 3) == 3
+    assert K.kvq_decode_num_splits(lay, 2, 9, 4) == 3  # empty trailing split dropped
+    assert K.kvq_decode_workspace_bytes(lay, 8, 64, 2048, 1) == 0
+    for splits in (3, 16):
+        b = K.kvq_decode_workspace_bytes(lay, 8, 64, 2048, splits)
+        rec = (2 * 8 + 8 * 128) * 4
+        assert b == 8 * 8 * splits * rec
+
+
+def test_status_strings(K):
+    for st in range(6):
+        assert K.kvq_status_string(st)
+    assert "gfx950" in K.kvq_status_string(4)
+
+
+def test_device_check_without_gpu(K):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert K.kvq_check_device(0) == 4
+
+
+def test_single_hip_runtime_in_process(K):
+    """The binding loads libkvq.so against the HIP runtime torch already
+    carries: exactly one libamdhip64 is mapped."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    assert len(paths) == 1, paths

@@ -1,0 +1,189 @@
+"""GPU path vs the oracle through the C ABI: bit-exact cache bytes (codes and
+scales), bit-exact dequantisation, and decode attention within
+|o - o_ref| <= 2e-3 + 2^-10 |o_ref| of the binary64 oracle on the same cache."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import (assert_attn_close, dev, first_mismatch, gpu_decode, gpu_write, log, olayout,
+                      paged_problem)
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1)]
+FMT_IDS = ["fp8pt", "int8pth", "fp8pth", "nvfp4", "nvfp4_4over6"]
+
+
+def edge_rows(rng, n, H, D):
+    """Token rows with the cases the formats must handle: plain normal data,
+    an attention-sink token (x20), zero rows, single outliers, tiny and huge
+    magnitudes, binary16 subnormals, exact E4M3 / E2M1 boundary values."""
+    x = workloads.random_halves(rng, (n, H, D))
+    x[0] *= np.float16(20)
+    if n > 3:
+        x[1] = 0
+        x[2, :, 5] = np.float16(3000.0)
+        x[3] = (rng.standard_normal((H, D)) * 1e-5).astype(np.float16)
+    if n > 6:
+        x[4] = np.float16(-0.0)
+        x[5] = (np.arange(H * D).reshape(H, D) % 7 - 3).astype(np.float16) * np.float16(2.0 ** -24)
+        x[6] = rng.uniform(-60000, 60000, (H, D)).astype(np.float16)
+    if n > 8:
+        grid = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 448, 464], np.float16)
+        x[7] = rng.choice(grid, (H, D)) * rng.choice(np.float16([-1, 1]), (H, D))
+        x[8] = np.float16(-2.5)
+    return x
+
+
+def layout_for(K, fmt, flags, H, D, P, num_pages, k16=None, v16=None, saturate=False):
+    ks = vs = 1.0
+    if fmt in (1, 4) and k16 is not None:
+        top = 448.0 if fmt == 1 else 2688.0
+        if saturate:
+            top *= 1.5  # push some values beyond the representable range
+        ks = float(np.float32(np.abs(k16).max()) / np.float32(top)) or 1.0
+        vs = float(np.float32(np.abs(v16).max()) / np.float32(top)) or 1.0
+    return K.layout(fmt, H, D, P, num_pages, ks, vs, flags)
+
+
+@pytest.mark.parametrize("fmt,flags", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("D,P", [(128, 16), (64, 32), (32, 16), (128, 64)])
+def test_write_bytes_match_oracle(K, O, fmt, flags, D, P):
+    rng = np.random.default_rng(1000 * fmt + 10 * D + P + flags)
+    H, num_pages, n = 3, 7, 70
+    pool = num_pages * P
+    slots = rng.choice(pool, n, replace=False).astype(np.int64)
+    slots[10] = -1
+    slots[11] = pool + 5  # past the pool: skipped
+    k16 = edge_rows(rng, n, H, D)
+    v16 = edge_rows(rng, n, H, D)
+    for saturate in (False, True) if fmt in (1, 4) else (False,):
+        lay = layout_for(K, fmt, flags, H, D, P, num_pages, k16, v16, saturate)
+        log(f"write fmt={fmt} flags={flags} D={D} P={P} sat={saturate}")
+        ref = O.quantize_write(olayout(lay), k16, v16, slots)
+        got = gpu_write(K, lay, k16, v16, slots).cpu().numpy()
+        mm = first_mismatch(got, ref)
+        assert mm is None, f"cache byte {mm[0]}: gpu {mm[1]:#x} oracle {mm[2]:#x} ({mm[3]} bytes differ)"
+
+
+@pytest.mark.parametrize("fmt,flags", FORMATS, ids=FMT_IDS)
+def test_dequantize_matches_oracle(K, O, fmt, flags):
+    import torch
+    rng = np.random.default_rng(77 + fmt + flags)
+    H, D, P, num_pages, n = 2, 128, 16, 6, 90
+    slots = rng.choice(num_pages * P, n, replace=False).astype(np.int64)
+    k16 = edge_rows(rng, n, H, D)
+    v16 = edge_rows(rng, n, H, D)
+    lay = layout_for(K, fmt, flags, H, D, P, num_pages, k16, v16)
+    cache_ref = O.quantize_write(olayout(lay), k16, v16, slots)
+    kr, vr = O.dequantize(olayout(lay), cache_ref, slots)
+    kout = torch.full((n, H, D), 7.0, dtype=torch.float32, device="cuda")
+    vout = torch.full((n, H, D), 7.0, dtype=torch.float32, device="cuda")
+    K.kvq_dequantize(lay, dev(cache_ref), dev(slots), kout, vout)
+    torch.cuda.synchronize()
+    # one binary32 rounding of the exact binary64 value
+    assert np.array_equal(kout.cpu().numpy(), kr.astype(np.float32))
+    assert np.array_equal(vout.cpu().numpy(), vr.astype(np.float32))
+
+
+DECODE_CASES = []
+for fmt, flags in FORMATS:
+    for G in (1, 2, 4, 8):
+        for D, P in ((128, 16), (64, 32), (32, 16)):
+            DECODE_CASES.append((fmt, flags, G, D, P))
+
+
+@pytest.mark.parametrize("fmt,flags,G,D,P", DECODE_CASES)
+def test_decode_matches_oracle(K, O, fmt, flags, G, D, P):
+    rng = np.random.default_rng(fmt * 131 + flags * 7 + G * 17 + D + P)
+    B, H = 5, 2
+    ctx = np.array([0, 1, 17, 2 * P - 1, 9 * P + 3], np.int32)
+    bt, num_pages, slots = paged_problem(rng, B, H, G, D, P, ctx)
+    n = slots.shape[0]
+    k16 = workloads.random_halves(rng, (n, H, D))
+    v16 = workloads.random_halves(rng, (n, H, D))
+    k16[int(ctx[:4].sum())] *= np.float16(20)  # a sink in the last sequence
+    v16[int(ctx[:4].sum())] *= np.float16(20)
+    lay = layout_for(K, fmt, flags, H, D, P, num_pages, k16, v16)
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    q16 = workloads.random_halves(rng, (B, H * G, D))
+    sm = 1.0 / math.sqrt(D)
+    ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, sm)
+    cache_dev = dev(cache)
+    for splits in (0, 1, 3, 7):
+        log(f"decode fmt={fmt} flags={flags} G={G} D={D} P={P} splits={splits}")
+        got, _ = gpu_decode(K, lay, cache_dev, q16, bt, ctx, sm, num_splits=splits)
+        assert_attn_close(got, ref, f"splits={splits}")
+        # beyond the contract: apart from the final binary16 rounding the
+        # result tracks the binary64 oracle to ~1e-4
+        ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-4 + 1e-4 * np.abs(ref))
+    assert not np.any(got[0]), "empty context must give a zero row"
+
+
+@pytest.mark.parametrize("fmt,flags", FORMATS, ids=FMT_IDS)
+def test_decode_closed_forms(K, O, fmt, flags):
+    """ctx = 1 gives the token's value; identical keys give the mean value."""
+    import torch
+    rng = np.random.default_rng(5 + fmt + flags)
+    H, G, D, P = 1, 4, 128, 16
+    T = 48
+    bt = np.array([[2, 0, 1]], np.int32)
+    slots = bt[0, np.arange(T) // P].astype(np.int64) * P + np.arange(T) % P
+    k16 = np.repeat(workloads.random_halves(rng, (1, H, D)), T, axis=0)
+    v16 = workloads.random_halves(rng, (T, H, D))
+    lay = layout_for(K, fmt, flags, H, D, P, 3, k16, v16)
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    _, vh = O.dequantize(olayout(lay), cache, slots)
+    q16 = workloads.random_halves(rng, (1, G, D))
+    got, _ = gpu_decode(K, lay, dev(cache), q16, bt, [T], 0.3)
+    for h in range(G):
+        assert_attn_close(got[0, h], vh[:, 0].mean(axis=0), "identical keys")
+    got, _ = gpu_decode(K, lay, dev(cache), q16, bt, [1], 0.3)
+    for h in range(G):
+        assert_attn_close(got[0, h], vh[0, 0], "one token")
+
+
+def test_decode_invalid_pages(K, O):
+    """Block-table entries outside the pool are skipped without faulting."""
+    rng = np.random.default_rng(9)
+    B, H, G, D, P = 2, 2, 4, 128, 16
+    ctx = np.array([64, 64], np.int32)
+    bt, num_pages, slots = paged_problem(rng, B, H, G, D, P, ctx)
+    k16 = workloads.random_halves(rng, (slots.size, H, D))
+    v16 = workloads.random_halves(rng, (slots.size, H, D))
+    lay = K.layout(2, H, D, P, num_pages)
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    bad = bt.copy()
+    bad[0, 1] = -5
+    bad[1, 2] = num_pages + 100
+    got, _ = gpu_decode(K, lay, dev(cache), workloads.random_halves(rng, (B, H * G, D)), bad, ctx, 0.1,
+                        num_splits=2)
+    assert np.all(np.isfinite(got))
+
+
+def test_workspace_reuse_many_calls(K, O):
+    """Repeated calls on one workspace, with different batch sizes and split
+    counts, stay correct (the workspace carries nothing between calls)."""
+    import torch
+    rng = np.random.default_rng(21)
+    H, G, D, P = 2, 8, 128, 16
+    ctx = np.array([200, 31, 500, 64], np.int32)
+    bt, num_pages, slots = paged_problem(rng, 4, H, G, D, P, ctx)
+    k16 = workloads.random_halves(rng, (slots.size, H, D))
+    v16 = workloads.random_halves(rng, (slots.size, H, D))
+    lay = K.layout(3, H, D, P, num_pages)
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    q16 = workloads.random_halves(rng, (4, H * G, D))
+    ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, 0.09)
+    ws = K.DecodeWorkspace(lay, 4, H * G, bt.shape[1], 9)
+    cdev = dev(cache)
+    for it, (nb, splits) in enumerate([(4, 9), (4, 9), (2, 5), (4, 3), (3, 9), (4, 9)]):
+        out = torch.empty((nb, H * G, D), dtype=torch.float16, device="cuda")
+        K.kvq_decode_attention(lay, cdev, dev(q16[:nb]), dev(bt[:nb]), dev(ctx[:nb]), 0.09, out, ws.buffer, None,
+                               splits)
+        torch.cuda.synchronize()
+        assert_attn_close(out.cpu().numpy().astype(np.float64), ref[:nb], f"call {it}")

@@ -37,8 +37,10 @@ MUTANTS = [
     ("half_subnormal_exp", "v = ldexpf((float)m, -24);", "v = ldexpf((float)m, -25);", 0,
      [pins.pin_half_widening]),
     ("kvarn_alpha_without_c", "meta[i] = c[i] * s_q[i];", "meta[i] = s_q[i];", 0, [pins.pin_kvarn_tile]),
-    ("v8_row_major_store", "vc[4LL * D * (t / 4) + 4 * d + t % 4] = cv[d];", "vc[(int64_t)t * D + d] = cv[d];", 0,
+    ("v8_row_major_store", "vc[v8_off(D, t, d)] = cv[d];", "vc[(int64_t)t * D + d] = cv[d];", 0,
      [pins.pin_glossary_bytes]),
+    ("k8_offset_swizzle", "return 16LL * D * u + 64 * B * h + 16 * B * g + B * s + e;",
+     "return 16LL * D * u + 64 * B * h + 16 * B * s + B * g + e;", 0, [pins.pin_layout_bijective]),
     ("chunk_head_major", "return (uint8_t*)cache + (page * L->num_kv_heads + h) * kvqo_chunk_bytes(L);",
      "return (uint8_t*)cache + ((int64_t)h * L->num_pages + page) * kvqo_chunk_bytes(L);", 0,
      [pins.pin_layout_bijective]),

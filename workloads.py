@@ -7,8 +7,9 @@ arguments the way a calibration checkpoint would (host-side max|x| divided by
 the format's top value).  Both the CPU oracle and the GPU library consume the
 exact same binary16 arrays.
 
-Workloads (all drawn with numpy's PCG64 from the stated seed, cast to binary16
-with round-to-nearest-even):
+Workloads (drawn with numpy's PCG64: K and V in fixed chunks of 2^22 values, each
+from its own child of the stated seed's SeedSequence; cast to binary16 with
+round-to-nearest-even):
 
   glossary_int8   B=2, H_q=H_kv=4, T=16, D=32, page 16, seed 137.  q, k, v are
                   drawn with torch.manual_seed(137) / torch.randn in the order
@@ -20,7 +21,7 @@ with round-to-nearest-even):
                   with 10 of the 1024 (kv head, channel) columns scaled x10,
                   drawn separately for K and V.
   nvfp4_16k       B=16, 64q/8kv, T=16384, D=128, page 16, seed 4004; K, V ~
-                  Student-t with 4 degrees of freedom.
+                  Student-t with 4 degrees of freedom (drawn as Z / sqrt(chi2_4 / 4)).
   kvarn_16k       B=16, 64q/8kv, T=16384, D=128, page 128, seed 5005; K, V ~ N(0,1)
                   with 10 of the 1024 columns scaled x8.
 
@@ -85,15 +86,46 @@ class Workload:
         return 1.0, 1.0
 
 
-def _draw(rng, shape, dist):
-    if dist == "student_t4":
-        out = np.empty(shape, np.float32)
-        flat = out.reshape(-1)
-        step = 1 << 24
-        for i in range(0, flat.size, step):
-            flat[i:i + step] = rng.standard_t(4, size=min(step, flat.size - i))
-        return out
-    return rng.standard_normal(shape, dtype=np.float32)
+_CHUNK = 1 << 22  # elements per independently seeded chunk
+
+
+def _fill(ss, n, dist, out):
+    """Draw n binary32 values into out from seed sequence ss, in fixed chunks
+    (chunk i uses ss.spawn(...)[i]), so the values do not depend on how many
+    threads draw them."""
+    import concurrent.futures as cf
+    import os
+    kids = ss.spawn((n + _CHUNK - 1) // _CHUNK)
+
+    def one(i):
+        rng = np.random.default_rng(kids[i])
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        seg = out[lo:hi]
+        if dist == "student_t4":
+            # Student-t with 4 degrees of freedom as Z / sqrt(chi2_4 / 4) with
+            # chi2_4 = 2 * Gamma(2, 1): the textbook construction, in binary32
+            rng.standard_normal(out=seg, dtype=np.float32)
+            g = rng.standard_gamma(2.0, size=hi - lo, dtype=np.float32)
+            np.multiply(g, np.float32(0.5), out=g)
+            np.sqrt(g, out=g)
+            np.divide(seg, g, out=seg)
+        else:
+            rng.standard_normal(out=seg, dtype=np.float32)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, range(len(kids))))
+
+
+def _to_half(x):
+    """binary32 -> binary16, round-to-nearest-even (torch's multi-threaded cast)."""
+    import torch
+    return torch.from_numpy(x).to(torch.float16).numpy()
+
+
+def _absmax(x16):
+    import torch
+    return float(torch.from_numpy(x16).abs().max().float())
 
 
 def make(name: str, B: int | None = None, T: int | None = None, seed: int | None = None) -> Workload:
@@ -105,6 +137,9 @@ def make(name: str, B: int | None = None, T: int | None = None, seed: int | None
     seed = sp.seed if seed is None else seed
     assert T % sp.P == 0, "contexts are whole pages"
     H, D = sp.Hkv, sp.D
+    ss = np.random.SeedSequence(seed)
+    ss_k, ss_v, ss_rest = ss.spawn(3)
+    rng = np.random.default_rng(ss_rest)
     if sp.dist == "glossary":
         import torch
         g = torch.Generator().manual_seed(seed)
@@ -114,11 +149,14 @@ def make(name: str, B: int | None = None, T: int | None = None, seed: int | None
         q16 = q[:, :, 0, :].numpy().astype(np.float16)
         k16 = k.permute(0, 2, 1, 3).reshape(B * T, H, D).numpy().astype(np.float16)
         v16 = v.permute(0, 2, 1, 3).reshape(B * T, H, D).numpy().astype(np.float16)
-        rng = np.random.default_rng(seed)
     else:
-        rng = np.random.default_rng(seed)
-        k = _draw(rng, (B, T, H, D), sp.dist)
-        v = _draw(rng, (B, T, H, D), sp.dist)
+        n = B * T * H * D
+        k = np.empty(n, np.float32)
+        _fill(ss_k, n, sp.dist, k)
+        v = np.empty(n, np.float32)
+        _fill(ss_v, n, sp.dist, v)
+        k = k.reshape(B, T, H, D)
+        v = v.reshape(B, T, H, D)
         q16 = rng.standard_normal((B, sp.Hq, D), dtype=np.float32).astype(np.float16)
         if sp.dist == "sink20":
             k[:, 0] *= np.float32(20.0)
@@ -127,11 +165,13 @@ def make(name: str, B: int | None = None, T: int | None = None, seed: int | None
             f = np.float32(10.0 if sp.dist == "chan10" else 8.0)
             for x in (k, v):
                 cols = rng.choice(H * D, size=10, replace=False)
-                xv = x.reshape(B, T, H * D)
-                xv[:, :, cols] *= f
-        k16 = k.reshape(B * T, H, D).astype(np.float16)
+                mult = np.ones(H * D, np.float32)
+                mult[cols] = f
+                xv = x.reshape(B * T, H * D)
+                np.multiply(xv, mult, out=xv)
+        k16 = _to_half(k.reshape(B * T, H, D))
         del k
-        v16 = v.reshape(B * T, H, D).astype(np.float16)
+        v16 = _to_half(v.reshape(B * T, H, D))
         del v
     pages_per_seq = T // sp.P
     num_pages = B * pages_per_seq
@@ -139,10 +179,8 @@ def make(name: str, B: int | None = None, T: int | None = None, seed: int | None
     block_tables = perm.reshape(B, pages_per_seq)
     t = np.arange(T, dtype=np.int64)
     slots = (block_tables[:, t // sp.P].astype(np.int64) * sp.P + (t % sp.P)[None, :]).reshape(-1)
-    k_amax = float(np.abs(k16).max().astype(np.float32))
-    v_amax = float(np.abs(v16).max().astype(np.float32))
     return Workload(sp, B, T, k16, v16, q16, block_tables, np.full(B, T, np.int32), slots,
-                    num_pages, k_amax, v_amax)
+                    num_pages, _absmax(k16), _absmax(v16))
 
 
 def random_halves(rng, shape, scale=1.0, dist="normal"):
