@@ -12,9 +12,12 @@ pages.
 
 Also reported on the same line:
   write_mtok_s   whole-context quantise-on-write throughput (tokens/s / 1e6)
-  roofline       decode kernel: algorithmic KV bytes per launch / mean launch
-                 duration (HIP events around each decode launch in the timed
+  roofline       decode (split kernel, plus the merge kernel when the context
+                 is split): algorithmic KV bytes per launch / mean launch
+                 duration (HIP events around each decode call in the timed
                  region, on the launch stream) against 8 TB/s
+  copy           a 1 GiB device-to-device copy (read + write bytes / time):
+                 the achievable bandwidth beside the specification
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
   formats        the other formats' workloads (decode GB/s, write Mtok/s)
 
@@ -119,8 +122,35 @@ class Problem:
         end.record()
         torch.cuda.synchronize()
         total = start.elapsed_time(end)
-        dec = [a.elapsed_time(b) for a, b in ev]
-        return total / steps, sum(dec) / len(dec)
+        self.dec_ms = sorted(a.elapsed_time(b) for a, b in ev)
+        return total / steps, sum(self.dec_ms) / len(self.dec_ms)
+
+    def dec_percentiles_us(self):
+        d = self.dec_ms
+        pick = lambda f: round(d[min(len(d) - 1, int(f * len(d)))] * 1e3, 2)
+        return {"p10_us": pick(0.1), "p50_us": pick(0.5), "p90_us": pick(0.9)}
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """Device-to-device copy of a known size (read + write counted): the
+    achievable HBM reference beside the 8 TB/s specification, and the
+    calibration kernel for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+            "us": round(ms * 1e3, 2)}
 
 
 def cpu_baseline(name, fmt, flags, n_seq, threads):
@@ -233,11 +263,16 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": f"decode_kernel<{pb.fmt}, {sp.D}>", "mean_launch_us": round(ms_dec * 1e3, 2),
+            "kernel": f"decode_kernel<{pb.fmt}, {sp.D}, {sp.Hq // sp.Hkv}>"
+                      + (" + decode_merge_kernel" if pb.ws.num_splits > 1 else ""),
+            "algorithmic_bytes": pb.kv_bytes, "mean_launch_us": round(ms_dec * 1e3, 2),
+            **pb.dec_percentiles_us(),
         },
     }
     del pb
     torch.cuda.empty_cache()
+    result["copy"] = copy_bandwidth()
+    log(f"[bench] device copy: {result['copy']}")
 
     if not args.no_formats:
         fmts = {}

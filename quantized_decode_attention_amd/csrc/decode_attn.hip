@@ -39,7 +39,7 @@ namespace kvq {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kDepth = 4;  // 16-token units per wave: 1 in compute, kDepth-1 in flight
+constexpr int kDepth = 2;  // 16-token units per wave: 1 in compute, kDepth-1 in flight
 constexpr int kPageChunk = 256;  // block-table entries staged in LDS at a time
 constexpr float kNegInf = -INFINITY;
 

@@ -100,14 +100,17 @@ kvq_status current_device_ok() {
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-// Context splits per (sequence, kv head): enough workgroups to give each of
-// the 256 compute units about four, while keeping at least 8 pages (two per
-// wavefront) in a split.  Empty trailing splits are dropped.
+// Context splits per (sequence, kv head): enough workgroups for one resident
+// round on MI355X (256 compute units x 2 decode workgroups), while keeping at
+// least 8 pages (two per wavefront) in a split.  Empty trailing splits are
+// dropped.
+constexpr int64_t kTargetWorkgroups = 512;
+
 void plan_splits(int batch, int H, int max_pages, int hint, int* splits, int* pages_per_split) {
   const int64_t units = (int64_t)batch * H;
   int s = hint;
   if (s <= 0) {
-    const int64_t want = units > 0 ? (1024 + units - 1) / units : 1;
+    const int64_t want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
     const int64_t cap = (max_pages + 7) / 8;
     s = (int)(want < cap ? want : cap);
   }

@@ -79,9 +79,9 @@ def test_argument_errors_before_launch(K):
 
 def test_split_plan_and_workspace(K):
     lay = K.layout(2, 8, 128, 16, 16384)
-    # one MI355X: about four workgroups per compute unit
-    assert K.kvq_decode_num_splits(lay, 8, 2048) == 16
-    assert K.kvq_decode_num_splits(lay, 32, 256) == 4
+    # one MI355X: one resident round of 512 workgroups
+    assert K.kvq_decode_num_splits(lay, 8, 2048) == 8
+    assert K.kvq_decode_num_splits(lay, 32, 256) == 2
     assert K.kvq_decode_num_splits(lay, 2, 1) == 1
     assert K.kvq_decode_num_splits(lay, 2, 10, 3) == 3
     assert K.kvq_decode_num_splits(lay, 2, 9, 4) == 3  # empty trailing split dropped
