@@ -83,6 +83,10 @@ class Problem:
         self.K.kvq_quantize_write(self.lay, self.k, self.v, self.slots, self.caches[i % len(self.caches)])
 
     def append(self, i):
+        # KVarN quantises whole 128-token tiles; a new token waits in the
+        # caller's binary16 tail, so its step is the decode alone
+        if self.fmt == self.K.KVQ_KVARN_K4V2_G128:
+            return
         self.K.kvq_quantize_write(self.lay, self.k_new, self.v_new, self.slots_new, self.caches[i % len(self.caches)])
 
     def decode(self, i):
@@ -228,7 +232,7 @@ def main():
         sys.exit(1)
 
     main_fmt = {"int8_32k": (K.KVQ_INT8_PTH, 0), "fp8_sink_4k": (K.KVQ_FP8_PTH, 0),
-                "nvfp4_16k": (K.KVQ_NVFP4, 0)}[args.workload]
+                "nvfp4_16k": (K.KVQ_NVFP4, 0), "kvarn_16k": (K.KVQ_KVARN_K4V2_G128, 0)}[args.workload]
     pb = Problem(K, args.workload, *main_fmt)
     write_mtok, write_ms = pb.time_write()
     log(f"[bench] whole-context write: {write_mtok:.1f} Mtok/s ({write_ms:.3f} ms)")
@@ -277,7 +281,8 @@ def main():
     if not args.no_formats:
         fmts = {}
         others = [("fp8_sink_4k", K.KVQ_FP8_PER_TENSOR, 0), ("fp8_sink_4k", K.KVQ_FP8_PTH, 0),
-                  ("nvfp4_16k", K.KVQ_NVFP4, 0), ("nvfp4_16k", K.KVQ_NVFP4, K.KVQ_FLAG_NVFP4_4OVER6)]
+                  ("nvfp4_16k", K.KVQ_NVFP4, 0), ("nvfp4_16k", K.KVQ_NVFP4, K.KVQ_FLAG_NVFP4_4OVER6),
+                  ("kvarn_16k", K.KVQ_KVARN_K4V2_G128, 0)]
         for name, fmt, flags in others:
             if name == args.workload and fmt == main_fmt[0] and flags == main_fmt[1]:
                 continue
@@ -288,7 +293,8 @@ def main():
             fmts[key] = {"workload": name, "decode_gbs": round(p.kv_bytes / (ms_d * 1e-3) / 1e9, 1),
                          "decode_frac_of_peak": round(p.kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "decode_us": round(ms_d * 1e3, 2), "step_us": round(ms_s * 1e3, 2),
-                         "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits}
+                         "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits,
+                         "step": "decode" if fmt == K.KVQ_KVARN_K4V2_G128 else "append + decode"}
             log(f"[bench] {key}: {fmts[key]}")
             del p
             torch.cuda.empty_cache()

@@ -30,31 +30,12 @@
 //
 // Splits: each workgroup writes its partial (m, l, O) to the workspace and a
 // second, small kernel merges the partials of every (sequence, kv head).
-#include <math.h>
-
-#include "kvq_device.h"
-#include "kvq_internal.h"
+#include "decode_common.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kDepth = 2;  // 16-token units per wave: 1 in compute, kDepth-1 in flight
-constexpr int kPageChunk = 256;  // block-table entries staged in LDS at a time
-constexpr float kNegInf = -INFINITY;
-
-__device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d) {
-  half8_t r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
-__device__ __forceinline__ half4_t cat4(half2_t a, half2_t b) {
-  half4_t r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  return r;
-}
 
 // Raw bytes of one 16-token unit for one lane, as loaded from the chunk.
 template <int FMT, int D>
@@ -67,18 +48,6 @@ struct Raw {
   float4 ks, vs;      // per-token-head scales of the lane's 4 score tokens
 };
 
-// The cache is streamed once per decode step: nontemporal loads keep it from
-// displacing reusable lines and measure ~8% faster than plain loads on MI355X.
-__device__ __forceinline__ uint32_t ld_nt(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
-
-__device__ __forceinline__ float4 ld_nt_f4(const uint8_t* p) {
-  const float* f = reinterpret_cast<const float*>(p);
-  return float4{__builtin_nontemporal_load(f), __builtin_nontemporal_load(f + 1), __builtin_nontemporal_load(f + 2),
-                __builtin_nontemporal_load(f + 3)};
-}
-
 template <int FMT, int D>
 __device__ __forceinline__ void zero_raw(Raw<FMT, D>& r) {
 #pragma unroll
@@ -87,12 +56,6 @@ __device__ __forceinline__ void zero_raw(Raw<FMT, D>& r) {
   for (int i = 0; i < Raw<FMT, D>::VW; ++i) r.v[i] = 0u;
   r.ksc = r.vsc = 0u;
   r.ks = r.vs = float4{0.f, 0.f, 0.f, 0.f};
-}
-
-template <int N>
-__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* w) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) w[i] = ld_nt(p + 4 * i);
 }
 
 // Issue the loads of unit `sub` (16 tokens) of a chunk.  K: D/4 channels of
@@ -179,21 +142,6 @@ struct WaveState {
   float4_t acc[D / 16];
   float m_run, l_run;
 };
-
-// Lazy rescaling: the weights P = 2^(score - m_run) * v_scale fed to the PV
-// product are kept relative to a reference m_run that only moves when some
-// weight would exceed 2^kTau, so the accumulators are rescaled a handful of
-// times per split instead of every time the running maximum creeps up, and
-// the common path needs no cross-lane maximum.  P <= 2^kTau keeps the binary16
-// operands far from overflow.
-constexpr float kTau = 8.0f;
-constexpr float kTauPow = 256.0f;
-
-// Lane l+G (within its 16-lane row) receives lane l's value: row_shr:G.
-template <int G>
-__device__ __forceinline__ uint32_t row_shr(uint32_t v) {
-  return __builtin_amdgcn_update_dpp(0u, v, 0x110 + G, 0xF, 0xF, false);
-}
 
 template <int FMT, int D, int G>
 __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, int tok0, int ctx, int n, int gq,

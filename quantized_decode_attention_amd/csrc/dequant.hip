@@ -2,8 +2,15 @@
 //
 // x_hat = s * q ([P3] "KV Cache 量化 · LLM Glossary", §它改变缓存表示), and for
 // NVFP4 x_hat = s_t * s_b * q ([P5] "NVFP4 KV Cache：Blackwell 上的 4-bit 缓存
-// 量化", §双层缩放怎样恢复动态范围).  One thread per output element; this path
-// is not performance-critical.  Built with -ffp-contract=off.
+// 量化", §双层缩放怎样恢复动态范围).  KVarN ([P2] "KVarN：华为推出的原生 vLLM
+// KV-cache 量化后端", §技术原理): the rotated tile is rebuilt from the folded
+// metadata, K_tj = rho_t (alpha_j code + beta_j) and
+// V_tj = gamma_j (alpha_t code + beta_t), and rotated back with the normalised
+// Walsh-Hadamard transform (its own inverse), all in binary64 with one final
+// rounding to binary32.  One thread per output element; this path is not
+// performance-critical.  Built with -ffp-contract=off.
+#include <math.h>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -65,6 +72,39 @@ __global__ __launch_bounds__(256) void dequant_kernel(WriteArgs a, float* k_out,
   }
 }
 
+// One workgroup of 128 threads per (token, kv head); thread j owns channel j.
+__global__ __launch_bounds__(128) void dequant_kvarn_kernel(WriteArgs a, float* k_out, float* v_out,
+                                                            double inv_sqrt128) {
+  __shared__ double buf[2][2][128];  // [ping-pong][side][channel]
+  const int64_t row = blockIdx.x;
+  const int64_t tok = row / a.H;
+  const int h = (int)(row - tok * a.H);
+  const int j = threadIdx.x;
+  const int64_t slot = a.slots[tok];
+  if (slot < 0 || slot >= (int64_t)a.num_pages * 128) return;
+  const int64_t page = slot / 128;
+  const int t = (int)(slot - page * 128);
+  const uint8_t* chunk = a.cache + (page * a.H + h) * a.geom.chunk_bytes;
+  const float* meta = reinterpret_cast<const float*>(chunk + a.geom.k_scales);
+  const uint32_t kb = chunk[t * 64 + j / 2];
+  const uint32_t kc = (j & 1) ? kb >> 4 : kb & 15u;
+  const uint32_t vc = (chunk[a.geom.v_codes + 128 * (t / 4) + j] >> (2 * (t % 4))) & 3u;
+  buf[0][0][j] = (double)meta[256 + t] * ((double)meta[j] * (double)kc + (double)meta[128 + j]);
+  buf[0][1][j] = (double)meta[640 + j] * ((double)meta[384 + t] * (double)vc + (double)meta[512 + t]);
+  int cur = 0;
+  for (int hb = 1; hb < 128; hb <<= 1) {
+    __syncthreads();
+#pragma unroll
+    for (int sd = 0; sd < 2; ++sd) {
+      const double* y = buf[cur][sd];
+      buf[cur ^ 1][sd][j] = (j & hb) ? y[j - hb] - y[j] : y[j] + y[j + hb];
+    }
+    cur ^= 1;
+  }
+  k_out[row * 128 + j] = (float)(buf[cur][0][j] * inv_sqrt128);
+  v_out[row * 128 + j] = (float)(buf[cur][1][j] * inv_sqrt128);
+}
+
 }  // namespace
 
 hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s) {
@@ -77,6 +117,7 @@ hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_ou
     case 2: dequant_kernel<2><<<grid, threads, 0, s>>>(a, k_out, v_out); break;
     case 3: dequant_kernel<3><<<grid, threads, 0, s>>>(a, k_out, v_out); break;
     case 4: dequant_kernel<4><<<grid, threads, 0, s>>>(a, k_out, v_out); break;
+    case 5: dequant_kvarn_kernel<<<grid, 128, 0, s>>>(a, k_out, v_out, 1.0 / sqrt(128.0)); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

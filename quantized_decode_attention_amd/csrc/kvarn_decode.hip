@@ -1,0 +1,503 @@
+// kvarn_decode.hip -- paged GQA decode attention over a KVarN k4v2 g128 cache
+// (gfx950).
+//
+// [P2] "KVarN：华为推出的原生 vLLM KV-cache 量化后端", §技术原理: the cache holds
+// each 128-token tile of a kv head in a rotated basis, k~ = H k and v~ = H v
+// (H the normalised Walsh-Hadamard transform, orthogonal and its own
+// inverse), as codes plus folded scales:
+//   k~_tj = rho_t (alpha_j c_tj + beta_j),   v~_tj = gamma_j (alpha'_t c'_tj + beta'_t).
+// Rotation leaves dot products unchanged, so with q~ = H q
+//   q . k_t  = rho_t ( sum_j (q~_j alpha_j) c_tj + sum_j q~_j beta_j )
+//   sum_t p_t v_t = H [ gamma (.) ( sum_t (p_t alpha'_t) c'_t + sum_t p_t beta'_t ) ]
+// The first bracket is one MFMA product per 16 tokens with A = 4-bit codes
+// (exact in binary16) and B = q~ (.) alpha (per page, split into binary16
+// high and low halves in the MFMA's spare columns); the second is the usual P V product with the
+// per-token V scale folded into P and the per-channel gamma applied once per
+// page, since alpha, beta and gamma change from tile to tile.  Tokens of the
+// incomplete last tile are kept by the caller in binary16 and attended by the
+// merge kernel, which also rotates the output back ([P2] §配置与部署: the
+// decode path keeps a small fixed workspace for the unquantised tail).
+//
+// Decomposition as for the other formats: a workgroup of 4 wavefronts per
+// (sequence, kv head, context split), wave w walks pages w, w+4, ... of the
+// split; every page is one tile of 8 sub-pages of 16 tokens.  Each wave
+// stages the 3 KB metadata block of its current page in LDS (loaded one
+// sub-page ahead, like the codes) and reads the per-token and per-channel
+// scales from there.
+#include "decode_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int D = 128;
+constexpr int P = 128;
+constexpr int kUnits = P / 16;
+constexpr int kVCodes = P * D / 2;          // V codes [32][128] 2-bit
+constexpr int kMeta = kVCodes + P * D / 4;  // binary32 metadata
+constexpr int kMetaFloats = 3 * D + 3 * P;
+// metadata vectors (float offsets)
+constexpr int kKa = 0, kKb = 128, kKr = 256, kVa = 384, kVb = 512, kVg = 640;
+constexpr float kInvSqrt128 = (float)0.088388347648318440550;  // RN(1/sqrt(128))
+
+// Sixteen-token sub-page of one lane: K token row n, channels 32*gq .. +31
+// (16 bytes); V channels 8*n .. 8*n+7 of tokens 4*gq .. +3 (8 bytes).
+struct RawKv {
+  uint32_t k[4];
+  uint32_t v[2];
+};
+
+__device__ __forceinline__ void load_kv(const uint8_t* chunk, int u, int n, int gq, RawKv& r) {
+  load_dwords<4>(chunk + (16 * u + n) * 64 + 16 * gq, r.k);
+  load_dwords<2>(chunk + kVCodes + 128 * (4 * u + gq) + 8 * n, r.v);
+}
+
+// K operand of QK MFMA kk: the 8 codes of dword kk as binary16.  A code
+// placed under the 0x64 exponent byte reads 1024 + code; subtracting 1024 is
+// exact.  Slot order pairs nibbles (0,4), (1,5), (2,6), (3,7): slot i holds
+// channel 8*kk + slot_channel(i).
+__device__ __forceinline__ half8_t k_operand(uint32_t w) {
+  const uint32_t m = 0x000F000Fu, e = 0x64006400u;
+  const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
+  return cat(as_h2((w & m) | e) - k1024, as_h2(((w >> 4) & m) | e) - k1024, as_h2(((w >> 8) & m) | e) - k1024,
+             as_h2(((w >> 12) & m) | e) - k1024);
+}
+__host__ __device__ constexpr int slot_channel(int i) { return (i >> 1) + 4 * (i & 1); }
+
+// Beyond the binary16 bound on P * v_scale, the reference also keeps P itself
+// below 2^64: a KVarN per-token V scale can be 0.
+constexpr float kPMaxLog2 = 64.0f;
+constexpr float kPMax = 18446744073709551616.0f;  // 2^64
+
+// V codes of one dword (4 channels x 4 tokens) -> binary16 high bytes of the
+// code values, one word per token: hb[k] byte m = value of token k, channel m.
+// 0, 1, 2, 3 have binary16 high bytes 00, 3C, 40, 42 and zero low bytes.
+__device__ __forceinline__ void v_hibytes(uint32_t w, uint32_t (&hb)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) hb[k] = perm(0u, 0x42403C00u, (w >> (2 * k)) & 0x03030303u);
+}
+
+// V operand of PV MFMA for channel byte m of a dword: tokens 0..3.
+__device__ __forceinline__ half4_t v_operand(const uint32_t (&hb)[4], int m) {
+  const uint32_t sel = 0x0Cu | ((uint32_t)m << 8) | (0x0Cu << 16) | ((uint32_t)(4 + m) << 24);
+  return cat4(as_h2(perm(hb[1], hb[0], sel)), as_h2(perm(hb[3], hb[2], sel)));
+}
+
+struct KvState {
+  float4_t o[D / 16];     // output rows, rotated basis, gamma applied
+  float4_t accp[D / 16];  // this page's P V product, before gamma
+  float pb;               // this lane's share of sum_t p_t beta'_t
+  float m_run, l_run;
+};
+
+template <int G>
+__device__ __forceinline__ void process_unit(const RawKv& r, bool live, const float* mt, int u, int n, int gq,
+                                             const half8_t (&qB)[4], float qb, float qk, KvState& st) {
+  float4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(r.k[kk]), qB[kk], s, 0, 0, 0);
+
+  const float4 rho = *reinterpret_cast<const float4*>(mt + kKr + 16 * u + 4 * gq);
+  const float4 va = *reinterpret_cast<const float4*>(mt + kVa + 16 * u + 4 * gq);
+  const float4 vb = *reinterpret_cast<const float4*>(mt + kVb + 16 * u + 4 * gq);
+  const float rh[4] = {rho.x, rho.y, rho.z, rho.w};
+  const float vsc[4] = {va.x, va.y, va.z, va.w};
+  const float vbe[4] = {vb.x, vb.y, vb.z, vb.w};
+
+  // column n < G: high half of head n; column G + n: its low half
+  float lg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(row_shl<G>(__float_as_uint(s[i])));
+    lg[i] = live ? rh[i] * (s[i] + lo + qb) * qk : kNegInf;
+  }
+  float p[4], pv[4];
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
+    pv[i] = live ? p[i] * vsc[i] : 0.0f;
+    over |= !(pv[i] <= kTauPow) || !(p[i] <= kPMax);
+  }
+  over = over && (n < G);
+  if (__any(over)) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (live && n < G) mx = fmaxf(mx, fmaxf(lg[i] + __log2f(vsc[i]), lg[i] - kPMaxLog2));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = (m_new > st.m_run) ? exp2f(st.m_run - m_new) : 1.0f;
+    st.l_run *= alpha;
+    st.pb *= alpha;
+    float ar[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * gq + i;
+      ar[i] = __shfl(alpha, row < G ? row : (row < 2 * G ? row - G : 0));
+    }
+#pragma unroll
+    for (int nn = 0; nn < D / 16; ++nn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st.o[nn][i] *= ar[i];
+        st.accp[nn][i] *= ar[i];
+      }
+    st.m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
+      pv[i] = live ? p[i] * vsc[i] : 0.0f;
+    }
+  }
+
+  half4_t ph, plo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.l_run += p[i];
+    st.pb += p[i] * vbe[i];
+    const half_t hh = (half_t)pv[i];
+    ph[i] = hh;
+    plo[i] = (half_t)(pv[i] - (float)hh);
+  }
+  const uint2 lob = __builtin_bit_cast(uint2, plo);
+  uint2 shifted;
+  shifted.x = row_shr<G>(lob.x);
+  shifted.y = row_shr<G>(lob.y);
+  half4_t pA;
+  if (n < G)
+    pA = ph;
+  else if (n < 2 * G)
+    pA = __builtin_bit_cast(half4_t, shifted);
+  else
+    pA = half4_t{0, 0, 0, 0};
+
+  uint32_t hb0[4], hb1[4];
+  v_hibytes(r.v[0], hb0);
+  v_hibytes(r.v[1], hb1);
+#pragma unroll
+  for (int nn = 0; nn < 4; ++nn)
+    st.accp[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb0, nn), st.accp[nn], 0, 0, 0);
+#pragma unroll
+  for (int nn = 0; nn < 4; ++nn)
+    st.accp[4 + nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb1, nn), st.accp[4 + nn], 0, 0, 0);
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
+  constexpr int NV = D / 16;
+  __shared__ float lds_o[kWaves][2 * G][D];
+  __shared__ float lds_m[kWaves][16];
+  __shared__ float lds_l[kWaves][16];
+  __shared__ int s_pages[kPageChunk];
+  __shared__ __attribute__((aligned(16))) float s_meta[kWaves][kMetaFloats];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, gq = l >> 4;
+  const int S = a.num_splits;
+  const int64_t rec_floats = ws_record_floats(D);
+
+  int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
+  const int n_pages = ctx / P;  // complete tiles; the rest is the caller's tail
+  const int p_begin = split * a.pages_per_split;
+  const int p_end = min(p_begin + a.pages_per_split, n_pages);
+
+  // q~ = H q for head hh of this lane's column, channels 32*gq .. +31
+  const bool lo_col = n >= G && n < 2 * G;
+  const int hh = n < G ? n : n - G;
+  float qv[32];
+  if (n < 2 * G) {
+    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + hh) * D;
+    float x[D];
+#pragma unroll
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+      const half8_t v = *reinterpret_cast<const half8_t*>(qp + 8 * c8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * c8 + e] = (float)v[e];
+    }
+#pragma unroll
+    for (int hb = 1; hb < D; hb <<= 1)
+#pragma unroll
+      for (int j = 0; j < D; ++j)
+        if ((j & hb) == 0) {
+          const float p0 = x[j], p1 = x[j + hb];
+          x[j] = p0 + p1;
+          x[j + hb] = p0 - p1;
+        }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      float xv = x[c];
+#pragma unroll
+      for (int g4 = 1; g4 < 4; ++g4) xv = (gq == g4) ? x[32 * g4 + c] : xv;
+      qv[c] = xv * kInvSqrt128;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) qv[c] = 0.0f;
+  }
+
+  KvState st;
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn) {
+    st.o[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
+    st.accp[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  st.pb = 0.0f;
+  st.m_run = kNegInf;
+  st.l_run = 0.0f;
+
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_pages;
+  const uint8_t* head_base = a.cache + (int64_t)kvh * a.geom.chunk_bytes;
+  const int64_t page_stride = (int64_t)a.H * a.geom.chunk_bytes;
+  float* mt = s_meta[w];
+
+  for (int c0 = p_begin; c0 < p_end; c0 += kPageChunk) {
+    const int nc = min(kPageChunk, p_end - c0);
+    __syncthreads();
+    for (int i = tid; i < nc; i += 256) s_pages[i] = bt[c0 + i];
+    __syncthreads();
+    const int nj = w < nc ? (nc - w + kWaves - 1) / kWaves : 0;
+    if (nj == 0) continue;
+    auto page_ptr = [&](int j, bool& valid) {
+      const int page = __builtin_amdgcn_readfirstlane(s_pages[w + kWaves * j]);
+      valid = page >= 0 && page < a.num_pages;
+      return head_base + (valid ? page : 0) * page_stride;
+    };
+    // the current page's metadata travels with its first sub-page: both are
+    // requested while the previous page's last sub-page is computed
+    bool vcur;
+    const uint8_t* pc = page_ptr(0, vcur);
+    uint32_t mreg[12];
+    load_dwords<4>(pc + kMeta + 16 * l, mreg);
+    load_dwords<4>(pc + kMeta + 1024 + 16 * l, mreg + 4);
+    load_dwords<4>(pc + kMeta + 2048 + 16 * l, mreg + 8);
+    RawKv rr[2];
+    load_kv(pc, 0, n, gq, rr[0]);
+
+    for (int j = 0; j < nj; ++j) {
+      // publish this page's metadata to the wave's LDS block (same-wave LDS
+      // accesses complete in order, so the reads below see it)
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        *reinterpret_cast<uint4*>(mt + 256 * k + 4 * l) = uint4{mreg[4 * k], mreg[4 * k + 1], mreg[4 * k + 2],
+                                                                  mreg[4 * k + 3]};
+      // B operand q~ (.) alpha (high or low binary16 half) and the beta term
+      // sum_j q~_j beta_j, per column
+      half8_t qB[4];
+      float qb = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float4 a0 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk);
+        const float4 a1 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk);
+        const float4 b1 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk + 4);
+        const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float be[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = slot_channel(i);
+          const float x = qv[8 * kk + c] * al[c];
+          const half_t hi = (half_t)x;
+          qB[kk][i] = lo_col ? (half_t)(x - (float)hi) : hi;
+          qb += qv[8 * kk + c] * be[c];
+        }
+      }
+      qb += __shfl_xor(qb, 16);
+      qb += __shfl_xor(qb, 32);
+
+      const int jn = min(j + 1, nj - 1);
+      bool vnext;
+      const uint8_t* pn = page_ptr(jn, vnext);
+#pragma unroll
+      for (int u = 0; u < kUnits; ++u) {
+        if (u + 1 < kUnits) {
+          load_kv(pc, u + 1, n, gq, rr[(u + 1) & 1]);
+        } else {
+          load_dwords<4>(pn + kMeta + 16 * l, mreg);
+          load_dwords<4>(pn + kMeta + 1024 + 16 * l, mreg + 4);
+          load_dwords<4>(pn + kMeta + 2048 + 16 * l, mreg + 8);
+          load_kv(pn, 0, n, gq, rr[0]);
+        }
+        process_unit<G>(rr[u & 1], vcur, mt, u, n, gq, qB, qb, a.qk_scale, st);
+      }
+
+      // end of page: o += gamma (.) (accp + sum_t p_t beta'_t)
+      float pbh = st.pb + __shfl_xor(st.pb, 16);
+      pbh += __shfl_xor(pbh, 32);
+      const float4 g0 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n);
+      const float4 g1 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n + 4);
+      const float gam[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * gq + i;
+        const float v = __shfl(pbh, row < G ? row : 0);
+        pr[i] = row < G ? v : 0.0f;
+      }
+      if (vcur) {  // an invalid page's metadata may hold anything
+#pragma unroll
+        for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st.o[nn][i] += gam[nn] * (st.accp[nn][i] + pr[i]);
+      }
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) st.accp[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
+      st.pb = 0.0f;
+      pc = pn;
+      vcur = vnext;
+    }
+  }
+
+  // ---- combine the four waves (and the high/low rows) in LDS
+  float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (gq == 0) {
+    lds_m[w][n] = st.m_run;
+    lds_l[w][n] = l_tot;
+  }
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * gq + i;
+      if (row < 2 * G) lds_o[w][row][8 * n + nn] = st.o[nn][i];
+    }
+  __syncthreads();
+
+  float* rec = reinterpret_cast<float*>(a.workspace) + (((int64_t)b * a.H + kvh) * S + split) * rec_floats;
+  for (int i = tid; i < G * D; i += 256) {
+    const int g = i / D, d = i % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, lds_m[ww][g]);
+    float L = 0.0f, O = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = exp2f(lds_m[ww][g] - M);
+        L += f * lds_l[ww][g];
+        O += f * (lds_o[ww][g][d] + lds_o[ww][g + G][d]);
+      }
+    }
+    if (d == 0) {
+      rec[g] = M;
+      rec[kMaxGroup + g] = L;
+    }
+    rec[2 * kMaxGroup + g * D + d] = O;
+  }
+}
+
+// Block-wide reductions over the 128 threads of the merge kernel.
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(red[0], red[1]);
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1];
+}
+
+// Merge of one (sequence, q head): the split partials (rotated basis), the
+// binary16 tail tokens (original basis), and the rotation back:
+//   M = max(m_s, tail scores), L = sum 2^(m_s-M) l_s + sum_t 2^(s_t-M),
+//   o = ( H sum 2^(m_s-M) o_s + sum_t 2^(s_t-M) v_t ) / L.
+// 128 threads; thread d owns channel d (and tail token d for the scores).
+__global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
+  __shared__ float wts[kMaxSplits];
+  __shared__ float e_tail[P];
+  __shared__ float y[2][D];
+  __shared__ float red[2];
+  const int kvh = blockIdx.x, b = blockIdx.y, g = blockIdx.z, t = threadIdx.x;
+  const int S = a.num_splits;
+  const int64_t rf = ws_record_floats(D);
+  const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
+  const int n_tail = a.tail ? ctx % P : 0;
+  const int hq = kvh * a.G + g;
+
+  float mp = kNegInf;
+  for (int sp = t; sp < S; sp += 128) mp = fmaxf(mp, recs[sp * rf + g]);
+  // tail scores (log2 units), thread t = tail token t
+  float lg = kNegInf;
+  if (t < n_tail) {
+    const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + t) * D;
+    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + hq) * D;
+    float acc = 0.0f;
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+      const half8_t kv = *reinterpret_cast<const half8_t*>(kt + 8 * c8);
+      const half8_t qv = *reinterpret_cast<const half8_t*>(qp + 8 * c8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)kv[e] * (float)qv[e];
+    }
+    lg = acc * a.qk_scale;
+  }
+  const float M = block_max(fmaxf(mp, lg), red);
+  uint16_t* orow = a.out + ((int64_t)b * a.Hq + hq) * D;
+  if (M == kNegInf) {  // empty context
+    orow[t] = 0;
+    return;
+  }
+  float lp = 0.0f;
+  for (int sp = t; sp < S; sp += 128) {
+    const float ms = recs[sp * rf + g];
+    const float f = ms == kNegInf ? 0.0f : exp2f(ms - M);
+    wts[sp] = f;
+    lp += f * recs[sp * rf + kMaxGroup + g];
+  }
+  const float e = t < n_tail ? exp2f(lg - M) : 0.0f;
+  e_tail[t] = e;
+  const float L = block_sum(lp + e, red);  // includes the barrier for wts / e_tail
+
+  // rotated-basis output, channel t, then the inverse rotation
+  const float* col = recs + 2 * kMaxGroup + g * D + t;
+  float o = 0.0f;
+  for (int sp = 0; sp < S; ++sp) o += wts[sp] * col[sp * rf];
+  y[0][t] = o;
+  int cur = 0;
+  for (int hb = 1; hb < D; hb <<= 1) {
+    __syncthreads();
+    const float* yc = y[cur];
+    y[cur ^ 1][t] = (t & hb) ? yc[t - hb] - yc[t] : yc[t] + yc[t + hb];
+    cur ^= 1;
+  }
+  float out = y[cur][t] * kInvSqrt128;
+  // tail values in the original basis
+  float ot = 0.0f;
+  if (n_tail > 0) {
+    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P) * D + t;
+    for (int j = 0; j < n_tail; ++j) ot += e_tail[j] * (float)__builtin_bit_cast(half_t, vt[(int64_t)j * D]);
+  }
+  out = (out + ot) / L;
+  orow[t] = __builtin_bit_cast(uint16_t, (half_t)out);
+}
+
+}  // namespace
+
+hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.num_splits, (unsigned)a.H, (unsigned)a.B);
+  switch (a.G) {
+    case 1: kvarn_decode_kernel<1><<<grid, 256, 0, s>>>(a); break;
+    case 2: kvarn_decode_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 4: kvarn_decode_kernel<4><<<grid, 256, 0, s>>>(a); break;
+    case 8: kvarn_decode_kernel<8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  kvarn_merge_kernel<<<dim3((unsigned)a.H, (unsigned)a.B, (unsigned)a.G), 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

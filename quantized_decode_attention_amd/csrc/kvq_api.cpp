@@ -125,7 +125,7 @@ void plan_splits(int batch, int H, int max_pages, int hint, int* splits, int* pa
 }
 
 int64_t workspace_bytes_for(const kvq_layout* L, int batch, int splits) {
-  if (splits <= 1) return 0;
+  if (splits <= 1 && L->format != KVQ_KVARN_K4V2_G128) return 0;
   return (int64_t)batch * L->num_kv_heads * splits * ws_record_floats(L->head_dim) * 4;
 }
 
@@ -164,7 +164,7 @@ kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const voi
   a.v_scale = layout->v_scale;
   a.flags = layout->flags;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_UNSUPPORTED;  // not built yet
+  if (layout->format == KVQ_KVARN_K4V2_G128) return from_hip(launch_kvarn_write(a, s));
   return from_hip(launch_quant_write(layout->format, a, s));
 }
 
@@ -231,7 +231,8 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
   a.num_splits = splits;
   a.pages_per_split = pps;
   a.sp_shift = __builtin_ctz(layout->page_size / 16);
-  if (layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_UNSUPPORTED;  // not built yet
+  if (layout->format == KVQ_KVARN_K4V2_G128)
+    return from_hip(launch_kvarn_decode(a, static_cast<hipStream_t>(stream)));
   return from_hip(launch_decode(layout->format, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -254,7 +255,6 @@ kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int
   a.num_pages = layout->num_pages;
   a.k_scale = layout->k_scale;
   a.v_scale = layout->v_scale;
-  if (layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_UNSUPPORTED;  // not built yet
   return from_hip(launch_dequant(layout->format, a, k_out, v_out, static_cast<hipStream_t>(stream)));
 }
 

@@ -47,7 +47,8 @@ struct DecodeArgs {
 };
 
 // Workspace: one partial record (m[8], l[8], o[8][D]) per (sequence, kv head,
-// split); no workspace is needed when there is a single split.
+// split); no workspace is needed when there is a single split, except for
+// KVarN, whose merge kernel always runs (tail tokens, rotation back).
 constexpr int kMaxGroup = 8;    // q heads per kv head served by one decode wave
 constexpr int kMaxSplits = 256; // context splits per (sequence, kv head)
 
@@ -56,6 +57,7 @@ __host__ __device__ inline int64_t ws_record_floats(int D) { return 2 * kMaxGrou
 hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s);
 hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s);
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s);
 
 }  // namespace kvq

@@ -90,6 +90,10 @@ def test_split_plan_and_workspace(K):
         b = K.kvq_decode_workspace_bytes(lay, 8, 64, 2048, splits)
         rec = (2 * 8 + 8 * 128) * 4
         assert b == 8 * 8 * splits * rec
+    # KVarN always merges (binary16 tail, rotation back): a record even for one split
+    klay = K.layout(5, 8, 128, 128, 2048)
+    assert K.kvq_decode_workspace_bytes(klay, 16, 64, 128, 1) == 16 * 8 * 1 * (2 * 8 + 8 * 128) * 4
+    assert K.kvq_decode_num_splits(klay, 16, 128) == 4
 
 
 def test_status_strings(K):
