@@ -157,6 +157,44 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
             "us": round(ms * 1e3, 2)}
 
 
+# HBM traffic of one decode call, measured with rocprofv3 counters and kept in
+# a profile summary together with a digest of the decode kernel's sources: the
+# figure is reported only while those sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int8_32k_traffic.md")
+DECODE_SOURCES = ("decode_attn.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
+
+
+def decode_sources_digest():
+    import hashlib
+
+    from quantized_decode_attention_amd import _build
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(_build.CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    h.update(" ".join(_build.SOURCES["decode_attn.hip"] + _build.COMMON[:4]).encode())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """Bytes per decode call from the committed counter summary, or None when
+    there is none for this workload or the kernel changed since."""
+    if workload != "int8_32k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.strip().strip("`").split(" = ")
+            if len(parts) == 2:
+                vals[parts[0].strip()] = parts[1].strip()
+    if vals.get("decode_sources_sha256") != decode_sources_digest():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(name, fmt, flags, n_seq, threads):
     """The oracle on a bounded sample of the workload: quantise-write every
     token of n_seq sequences, then decode every q head of those sequences.
@@ -266,10 +304,12 @@ def main():
         "write_gbs": round((2 * w.B * w.T * sp.Hkv * sp.D * 2 + pb.cache_bytes) / (write_ms * 1e-3) / 1e9, 2),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
             "kernel": f"decode_kernel<{pb.fmt}, {sp.D}, {sp.Hq // sp.Hkv}>"
                       + (" + decode_merge_kernel" if pb.ws.num_splits > 1 else ""),
-            "algorithmic_bytes": pb.kv_bytes, "mean_launch_us": round(ms_dec * 1e3, 2),
+            "algorithmic_bytes": pb.kv_bytes, "traffic_unit": "HBM bytes per decode call (rocprofv3 "
+            "FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB copy)",
+            "mean_launch_us": round(ms_dec * 1e3, 2),
             **pb.dec_percentiles_us(),
         },
     }
