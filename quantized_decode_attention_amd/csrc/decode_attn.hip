@@ -185,6 +185,40 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     over |= !(pv[i] <= kTauPow);
   }
   over = over && (n < G);
+
+  // P (high/low halves) times V into the output rows.  Both sides of the
+  // rare rescale branch below run their own copy, so the accumulators are
+  // never merged between the branches (which costs a register copy of every
+  // accumulator on the common path).
+  auto accumulate = [&]() {
+    half4_t ph, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st.l_run += p[i];
+      const half_t hh = (half_t)pv[i];
+      ph[i] = hh;
+      plo[i] = (half_t)(pv[i] - (float)hh);
+    }
+    // rows G..2G-1 carry the binary16 remainder of rows 0..G-1
+    const uint2 lob = __builtin_bit_cast(uint2, plo);
+    uint2 shifted;
+    shifted.x = row_shr<G>(lob.x);
+    shifted.y = row_shr<G>(lob.y);
+    half4_t pA;
+    if (n < G)
+      pA = ph;
+    else if (n < 2 * G)
+      pA = __builtin_bit_cast(half4_t, shifted);
+    else
+      pA = half4_t{0, 0, 0, 0};
+    half2_t vs01 = {0, 0}, vs23 = {0, 0};
+    if constexpr (FMT == 4) e4m3x4_to_h(r.vsc, vs01, vs23);
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn)
+      st.acc[nn] =
+          __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand<FMT, D>(r, nn, vs01, vs23), st.acc[nn], 0, 0, 0);
+  };
+
   if (__any(over)) {
     // move the reference to the exact maximum of score + log2(v_scale)
     float mx = kNegInf;
@@ -213,34 +247,10 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
       p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
       pv[i] = live ? p[i] * vsc[i] : 0.0f;
     }
+    accumulate();
+  } else {
+    accumulate();
   }
-
-  half4_t ph, plo;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.l_run += p[i];
-    const half_t hh = (half_t)pv[i];
-    ph[i] = hh;
-    plo[i] = (half_t)(pv[i] - (float)hh);
-  }
-  // rows G..2G-1 carry the binary16 remainder of rows 0..G-1
-  const uint2 lob = __builtin_bit_cast(uint2, plo);
-  uint2 shifted;
-  shifted.x = row_shr<G>(lob.x);
-  shifted.y = row_shr<G>(lob.y);
-  half4_t pA;
-  if (n < G)
-    pA = ph;
-  else if (n < 2 * G)
-    pA = __builtin_bit_cast(half4_t, shifted);
-  else
-    pA = half4_t{0, 0, 0, 0};
-
-  half2_t vs01 = {0, 0}, vs23 = {0, 0};
-  if constexpr (FMT == 4) e4m3x4_to_h(r.vsc, vs01, vs23);
-#pragma unroll
-  for (int nn = 0; nn < NV; ++nn)
-    st.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand<FMT, D>(r, nn, vs01, vs23), st.acc[nn], 0, 0, 0);
 }
 
 template <int FMT, int D, int G>
@@ -405,50 +415,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the context splits of one (sequence, q head): m = max m_s,
-// l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l.  A separate launch:
-// the kernel boundary makes every split's partial visible on all XCDs
-// without device-wide cache maintenance inside the split kernel.  One
-// wavefront per output row: the split maxima and sums are read in parallel
-// and wave-reduced, then the weighted rows are summed with independent loads.
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int D, float post) {
-  __shared__ float wts[kMaxSplits];
-  const int kvh = blockIdx.x, b = blockIdx.y, g = blockIdx.z;
+// Merge of the context splits: m = max m_s, l = sum 2^(m_s - m) l_s,
+// o = sum 2^(m_s - m) o_s / l.  A separate launch: the kernel boundary makes
+// every split's partial visible on all XCDs without device-wide cache
+// maintenance inside the split kernel.  One thread per output element; every
+// split's (m, l, o) is requested before any is used, 8 splits at a time, so
+// the merge costs one memory round trip per 8 splits.
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int D, float post) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.B * a.Hq * D) return;
+  const int d = (int)(idx % D);
+  const int64_t bh = idx / D;
+  const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int kvh = hq / a.G, g = hq - kvh * a.G;
   const int S = a.num_splits;
-  const int lane = threadIdx.x;
   const int64_t rf = ws_record_floats(D);
   const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
-
-  float M = kNegInf;
-  for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, recs[sp * rf + g]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
-  float L = 0.0f;
-  for (int sp = lane; sp < S; sp += 64) {
-    const float ms = recs[sp * rf + g];
-    const float f = (M == kNegInf) ? 0.0f : exp2f(ms - M);
-    wts[sp] = f;
-    L += f * recs[sp * rf + kMaxGroup + g];
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
-  __syncthreads();
-  const float inv = L > 0.0f ? post / L : 0.0f;
-  uint16_t* orow = a.out + ((int64_t)b * a.Hq + kvh * a.G + g) * D;
-  for (int d = lane; d < D; d += 64) {
-    const float* col = recs + 2 * kMaxGroup + g * D + d;
-    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
-    int sp = 0;
-    for (; sp + 4 <= S; sp += 4) {
-      o0 += wts[sp] * col[sp * rf];
-      o1 += wts[sp + 1] * col[(sp + 1) * rf];
-      o2 += wts[sp + 2] * col[(sp + 2) * rf];
-      o3 += wts[sp + 3] * col[(sp + 3) * rf];
-    }
-    for (; sp < S; ++sp) o0 += wts[sp] * col[sp * rf];
-    const float o = ((o0 + o1) + (o2 + o3)) * inv;
-    orow[d] = __builtin_bit_cast(uint16_t, (half_t)o);
-  }
+  float M = kNegInf, L = 0.0f, O = 0.0f;
+  merge_splits(recs, rf, S, g, 2 * kMaxGroup + g * D + d, M, L, O);
+  const float o = L > 0.0f ? O / L * post : 0.0f;
+  a.out[idx] = __builtin_bit_cast(uint16_t, (half_t)o);
 }
 
 template <int FMT, int D>
@@ -487,7 +473,8 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s) {
   }
   if (e != hipSuccess || a.num_splits == 1) return e;
   const float post = (fmt == 1 || fmt == 4) ? a.v_scale : 1.0f;
-  decode_merge_kernel<<<dim3((unsigned)a.H, (unsigned)a.B, (unsigned)a.G), 64, 0, s>>>(a, a.D, post);
+  const int64_t outs = (int64_t)a.B * a.Hq * a.D;
+  decode_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, s>>>(a, a.D, post);
   return hipGetLastError();
 }
 

@@ -65,4 +65,37 @@ __device__ __forceinline__ uint32_t row_shl(uint32_t v) {
   return __builtin_amdgcn_update_dpp(0u, v, 0x100 + G, 0xF, 0xF, false);
 }
 
+// Online merge of split partial records into (M, L, O) for one output
+// element: record s holds m at float g, l at kMaxGroup + g and the output row
+// value at o_off.  Splits are read 8 at a time, all loads of a group issued
+// before any is used; empty splits have m = -inf and contribute nothing.
+__device__ __forceinline__ void merge_splits(const float* recs, int64_t rf, int S, int g, int64_t o_off,
+                                             float& M, float& L, float& O) {
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float m[8], l[8], o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool in = s0 + k < S;
+      const float* r = recs + (int64_t)(in ? s0 + k : s0) * rf;
+      m[k] = in ? r[g] : kNegInf;
+      l[k] = r[kMaxGroup + g];
+      o[k] = r[o_off];
+    }
+    float mc = M;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mc = fmaxf(mc, m[k]);
+    if (mc == kNegInf) continue;
+    const float sc = exp2f(M - mc);
+    L *= sc;
+    O *= sc;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float f = exp2f(m[k] - mc);
+      L += f * l[k];
+      O += f * o[k];
+    }
+    M = mc;
+  }
+}
+
 }  // namespace kvq

@@ -12,18 +12,18 @@
 // The first bracket is one MFMA product per 16 tokens with A = 4-bit codes
 // (exact in binary16) and B = q~ (.) alpha (per page, split into binary16
 // high and low halves in the MFMA's spare columns); the second is the usual P V product with the
-// per-token V scale folded into P and the per-channel gamma applied once per
-// page, since alpha, beta and gamma change from tile to tile.  Tokens of the
+// per-token V scale folded into P; gamma changes from tile to tile, so the
+// output is kept in the current page's gamma domain and rescaled once per page.  Tokens of the
 // incomplete last tile are kept by the caller in binary16 and attended by the
 // merge kernel, which also rotates the output back ([P2] §配置与部署: the
 // decode path keeps a small fixed workspace for the unquantised tail).
 //
 // Decomposition as for the other formats: a workgroup of 4 wavefronts per
 // (sequence, kv head, context split), wave w walks pages w, w+4, ... of the
-// split; every page is one tile of 8 sub-pages of 16 tokens.  Each wave
-// stages the 3 KB metadata block of its current page in LDS (loaded one
-// sub-page ahead, like the codes) and reads the per-token and per-channel
-// scales from there.
+// split; every page is one tile of 8 sub-pages of 16 tokens, kept 3 sub-pages
+// ahead in a register ring.  Each wave stages the 3 KB metadata block of its
+// current page in LDS (requested with the next page's first sub-page) and
+// reads the per-token and per-channel scales from there.
 #include "decode_common.h"
 
 namespace kvq {
@@ -32,6 +32,7 @@ namespace {
 constexpr int D = 128;
 constexpr int P = 128;
 constexpr int kUnits = P / 16;
+constexpr int kRing = 4;  // sub-page buffers per wave (kRing - 1 in flight)
 constexpr int kVCodes = P * D / 2;          // V codes [32][128] 2-bit
 constexpr int kMeta = kVCodes + P * D / 4;  // binary32 metadata
 constexpr int kMetaFloats = 3 * D + 3 * P;
@@ -51,17 +52,19 @@ __device__ __forceinline__ void load_kv(const uint8_t* chunk, int u, int n, int 
   load_dwords<2>(chunk + kVCodes + 128 * (4 * u + gq) + 8 * n, r.v);
 }
 
-// K operand of QK MFMA kk: the 8 codes of dword kk as binary16.  A code
-// placed under the 0x64 exponent byte reads 1024 + code; subtracting 1024 is
-// exact.  Slot order pairs nibbles (0,4), (1,5), (2,6), (3,7): slot i holds
-// channel 8*kk + slot_channel(i).
+// K operand of QK MFMA kk: the 8 codes of dword kk as binary16.  The low
+// nibbles (even channels) and high nibbles (odd channels) are separated into
+// bytes, each byte is placed under the 0x64 exponent byte by a byte permute
+// (binary16 1024 + code) and 1024 is subtracted exactly.  Slot i holds
+// channel 8*kk + slot_channel(i): slots 0..3 = channels 0, 2, 4, 6 and slots
+// 4..7 = channels 1, 3, 5, 7.
 __device__ __forceinline__ half8_t k_operand(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, e = 0x64006400u;
+  const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
   const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
-  return cat(as_h2((w & m) | e) - k1024, as_h2(((w >> 4) & m) | e) - k1024, as_h2(((w >> 8) & m) | e) - k1024,
-             as_h2(((w >> 12) & m) | e) - k1024);
+  return cat(as_h2(perm(0x64646464u, x, 0x04010400u)) - k1024, as_h2(perm(0x64646464u, x, 0x04030402u)) - k1024,
+             as_h2(perm(0x64646464u, y, 0x04010400u)) - k1024, as_h2(perm(0x64646464u, y, 0x04030402u)) - k1024);
 }
-__host__ __device__ constexpr int slot_channel(int i) { return (i >> 1) + 4 * (i & 1); }
+__host__ __device__ constexpr int slot_channel(int i) { return i < 4 ? 2 * i : 2 * (i - 4) + 1; }
 
 // Beyond the binary16 bound on P * v_scale, the reference also keeps P itself
 // below 2^64: a KVarN per-token V scale can be 0.
@@ -82,15 +85,18 @@ __device__ __forceinline__ half4_t v_operand(const uint32_t (&hb)[4], int m) {
   return cat4(as_h2(perm(hb[1], hb[0], sel)), as_h2(perm(hb[3], hb[2], sel)));
 }
 
+// The output rows are kept in the gamma domain of the page being read
+// (o = gamma (.) o'): moving to the next page rescales o' once by
+// gamma_old / gamma_new, so a page's P V product accumulates straight into o'.
 struct KvState {
-  float4_t o[D / 16];     // output rows, rotated basis, gamma applied
-  float4_t accp[D / 16];  // this page's P V product, before gamma
-  float pb;               // this lane's share of sum_t p_t beta'_t
+  float4_t o[D / 16];  // output rows o', rotated basis, current page's gamma domain
+  float pb;            // this lane's share of sum_t p_t beta'_t over the page
   float m_run, l_run;
 };
 
 template <int G>
-__device__ __forceinline__ void process_unit(const RawKv& r, bool live, const float* mt, int u, int n, int gq,
+// One sub-page of a valid page (invalid pages are skipped by the caller).
+__device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, int u, int n, int gq,
                                              const half8_t (&qB)[4], float qb, float qk, KvState& st) {
   float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -108,22 +114,59 @@ __device__ __forceinline__ void process_unit(const RawKv& r, bool live, const fl
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float lo = __uint_as_float(row_shl<G>(__float_as_uint(s[i])));
-    lg[i] = live ? rh[i] * (s[i] + lo + qb) * qk : kNegInf;
+    lg[i] = rh[i] * (s[i] + lo + qb) * qk;
   }
   float p[4], pv[4];
   bool over = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
-    pv[i] = live ? p[i] * vsc[i] : 0.0f;
+    p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
+    pv[i] = p[i] * vsc[i];
     over |= !(pv[i] <= kTauPow) || !(p[i] <= kPMax);
   }
   over = over && (n < G);
+
+  // P (high/low halves) times V into the output rows.  Both sides of the
+  // rare rescale branch below run their own copy, so the accumulators are
+  // never merged between the branches (which costs a register copy of every
+  // accumulator on the common path).
+  auto accumulate = [&]() {
+    half4_t ph, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st.l_run += p[i];
+      st.pb += p[i] * vbe[i];
+      const half_t hh = (half_t)pv[i];
+      ph[i] = hh;
+      plo[i] = (half_t)(pv[i] - (float)hh);
+    }
+    const uint2 lob = __builtin_bit_cast(uint2, plo);
+    uint2 shifted;
+    shifted.x = row_shr<G>(lob.x);
+    shifted.y = row_shr<G>(lob.y);
+    half4_t pA;
+    if (n < G)
+      pA = ph;
+    else if (n < 2 * G)
+      pA = __builtin_bit_cast(half4_t, shifted);
+    else
+      pA = half4_t{0, 0, 0, 0};
+    uint32_t hb0[4], hb1[4];
+    v_hibytes(r.v[0], hb0);
+    v_hibytes(r.v[1], hb1);
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn)
+      st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb0, nn), st.o[nn], 0, 0, 0);
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn)
+      st.o[4 + nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb1, nn), st.o[4 + nn], 0, 0, 0);
+  };
+
   if (__any(over)) {
     float mx = kNegInf;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (live && n < G) mx = fmaxf(mx, fmaxf(lg[i] + __log2f(vsc[i]), lg[i] - kPMaxLog2));
+      if (n < G) mx = fmaxf(mx, fmaxf(lg[i] + __log2f(vsc[i]), lg[i] - kPMaxLog2));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m_run, mx);
@@ -139,48 +182,17 @@ __device__ __forceinline__ void process_unit(const RawKv& r, bool live, const fl
 #pragma unroll
     for (int nn = 0; nn < D / 16; ++nn)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st.o[nn][i] *= ar[i];
-        st.accp[nn][i] *= ar[i];
-      }
+      for (int i = 0; i < 4; ++i) st.o[nn][i] *= ar[i];
     st.m_run = m_new;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
-      pv[i] = live ? p[i] * vsc[i] : 0.0f;
+      p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
+      pv[i] = p[i] * vsc[i];
     }
+    accumulate();
+  } else {
+    accumulate();
   }
-
-  half4_t ph, plo;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.l_run += p[i];
-    st.pb += p[i] * vbe[i];
-    const half_t hh = (half_t)pv[i];
-    ph[i] = hh;
-    plo[i] = (half_t)(pv[i] - (float)hh);
-  }
-  const uint2 lob = __builtin_bit_cast(uint2, plo);
-  uint2 shifted;
-  shifted.x = row_shr<G>(lob.x);
-  shifted.y = row_shr<G>(lob.y);
-  half4_t pA;
-  if (n < G)
-    pA = ph;
-  else if (n < 2 * G)
-    pA = __builtin_bit_cast(half4_t, shifted);
-  else
-    pA = half4_t{0, 0, 0, 0};
-
-  uint32_t hb0[4], hb1[4];
-  v_hibytes(r.v[0], hb0);
-  v_hibytes(r.v[1], hb1);
-#pragma unroll
-  for (int nn = 0; nn < 4; ++nn)
-    st.accp[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb0, nn), st.accp[nn], 0, 0, 0);
-#pragma unroll
-  for (int nn = 0; nn < 4; ++nn)
-    st.accp[4 + nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb1, nn), st.accp[4 + nn], 0, 0, 0);
 }
 
 template <int G>
@@ -191,6 +203,7 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   __shared__ float lds_l[kWaves][16];
   __shared__ int s_pages[kPageChunk];
   __shared__ __attribute__((aligned(16))) float s_meta[kWaves][kMetaFloats];
+  __shared__ __attribute__((aligned(16))) float s_q[G + 1][D];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, gq = l >> 4;
@@ -203,46 +216,37 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(p_begin + a.pages_per_split, n_pages);
 
-  // q~ = H q for head hh of this lane's column, channels 32*gq .. +31
+  // q~ = H q / sqrt(128) for the G heads, once per workgroup into LDS: wave w
+  // rotates heads w, w+4; lane l holds channels 2l and 2l+1, so the first
+  // butterfly stage is in-lane and the others pair lanes l and l ^ (h/2).
   const bool lo_col = n >= G && n < 2 * G;
-  const int hh = n < G ? n : n - G;
-  float qv[32];
-  if (n < 2 * G) {
-    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + hh) * D;
-    float x[D];
+  const int q_row = n < G ? n : (n < 2 * G ? n - G : G);  // row G of s_q is zero
+  for (int h2 = w; h2 < G; h2 += kWaves) {
+    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + h2) * D + 2 * l;
+    const half2_t q2 = *reinterpret_cast<const half2_t*>(qp);
+    float x0 = (float)q2[0], x1 = (float)q2[1];
+    const float s0 = x0 + x1, d0 = x0 - x1;
+    x0 = s0;
+    x1 = d0;
 #pragma unroll
-    for (int c8 = 0; c8 < D / 8; ++c8) {
-      const half8_t v = *reinterpret_cast<const half8_t*>(qp + 8 * c8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 * c8 + e] = (float)v[e];
+    for (int m = 1; m < 64; m <<= 1) {
+      const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
+      x0 = (l & m) ? p0 - x0 : x0 + p0;
+      x1 = (l & m) ? p1 - x1 : x1 + p1;
     }
-#pragma unroll
-    for (int hb = 1; hb < D; hb <<= 1)
-#pragma unroll
-      for (int j = 0; j < D; ++j)
-        if ((j & hb) == 0) {
-          const float p0 = x[j], p1 = x[j + hb];
-          x[j] = p0 + p1;
-          x[j + hb] = p0 - p1;
-        }
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      float xv = x[c];
-#pragma unroll
-      for (int g4 = 1; g4 < 4; ++g4) xv = (gq == g4) ? x[32 * g4 + c] : xv;
-      qv[c] = xv * kInvSqrt128;
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) qv[c] = 0.0f;
+    s_q[h2][2 * l] = x0 * kInvSqrt128;
+    s_q[h2][2 * l + 1] = x1 * kInvSqrt128;
   }
+  if (tid < D) s_q[G][tid] = 0.0f;
+  __syncthreads();
 
   KvState st;
 #pragma unroll
-  for (int nn = 0; nn < NV; ++nn) {
-    st.o[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
-    st.accp[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int nn = 0; nn < NV; ++nn) st.o[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float gcur[NV];  // gamma of the output's current domain, channels 8n + nn
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn) gcur[nn] = 1.0f;
+  bool have_gamma = false;
   st.pb = 0.0f;
   st.m_run = kNegInf;
   st.l_run = 0.0f;
@@ -272,8 +276,12 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
     load_dwords<4>(pc + kMeta + 16 * l, mreg);
     load_dwords<4>(pc + kMeta + 1024 + 16 * l, mreg + 4);
     load_dwords<4>(pc + kMeta + 2048 + 16 * l, mreg + 8);
-    RawKv rr[2];
-    load_kv(pc, 0, n, gq, rr[0]);
+    // ring of kRing sub-page buffers, kRing-1 sub-pages in flight ahead of
+    // the one being computed (the ring runs across page boundaries; 8 is a
+    // multiple of kRing, so sub-page u of every page uses slot u % kRing)
+    RawKv rr[kRing];
+#pragma unroll
+    for (int k = 0; k + 1 < kRing; ++k) load_kv(pc, k, n, gq, rr[k]);
 
     for (int j = 0; j < nj; ++j) {
       // publish this page's metadata to the wave's LDS block (same-wave LDS
@@ -282,68 +290,96 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
       for (int k = 0; k < 3; ++k)
         *reinterpret_cast<uint4*>(mt + 256 * k + 4 * l) = uint4{mreg[4 * k], mreg[4 * k + 1], mreg[4 * k + 2],
                                                                   mreg[4 * k + 3]};
-      // B operand q~ (.) alpha (high or low binary16 half) and the beta term
-      // sum_j q~_j beta_j, per column
-      half8_t qB[4];
-      float qb = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float4 a0 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk);
-        const float4 a1 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk + 4);
-        const float4 b0 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk);
-        const float4 b1 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk + 4);
-        const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float be[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int c = slot_channel(i);
-          const float x = qv[8 * kk + c] * al[c];
-          const half_t hi = (half_t)x;
-          qB[kk][i] = lo_col ? (half_t)(x - (float)hi) : hi;
-          qb += qv[8 * kk + c] * be[c];
-        }
-      }
-      qb += __shfl_xor(qb, 16);
-      qb += __shfl_xor(qb, 32);
-
       const int jn = min(j + 1, nj - 1);
       bool vnext;
       const uint8_t* pn = page_ptr(jn, vnext);
-#pragma unroll
-      for (int u = 0; u < kUnits; ++u) {
-        if (u + 1 < kUnits) {
-          load_kv(pc, u + 1, n, gq, rr[(u + 1) & 1]);
+      // sub-page u's loads: kRing-1 ahead, continuing into the next page (its
+      // metadata goes first)
+      auto issue = [&](int u) {
+        const int ahead = u + kRing - 1;
+        if (ahead < kUnits) {
+          load_kv(pc, ahead, n, gq, rr[ahead % kRing]);
         } else {
-          load_dwords<4>(pn + kMeta + 16 * l, mreg);
-          load_dwords<4>(pn + kMeta + 1024 + 16 * l, mreg + 4);
-          load_dwords<4>(pn + kMeta + 2048 + 16 * l, mreg + 8);
-          load_kv(pn, 0, n, gq, rr[0]);
+          if (ahead == kUnits) {
+            load_dwords<4>(pn + kMeta + 16 * l, mreg);
+            load_dwords<4>(pn + kMeta + 1024 + 16 * l, mreg + 4);
+            load_dwords<4>(pn + kMeta + 2048 + 16 * l, mreg + 8);
+          }
+          load_kv(pn, ahead - kUnits, n, gq, rr[ahead % kRing]);
         }
-        process_unit<G>(rr[u & 1], vcur, mt, u, n, gq, qB, qb, a.qk_scale, st);
-      }
-
-      // end of page: o += gamma (.) (accp + sum_t p_t beta'_t)
-      float pbh = st.pb + __shfl_xor(st.pb, 16);
-      pbh += __shfl_xor(pbh, 32);
-      const float4 g0 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n);
-      const float4 g1 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n + 4);
-      const float gam[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      float pr[4];
+        // keep the loads ahead of this sub-page's wait for its own data
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if (vcur) {  // wave-uniform; an invalid page's tokens carry no weight
+        // B operand q~ (.) alpha (high half in columns n < G, low half in
+        // columns G + n, zero beyond) and the beta term sum_j q~_j beta_j
+        half8_t qB[4];
+        float qb = 0.0f;
+        const float* qrow = s_q[q_row] + 32 * gq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * gq + i;
-        const float v = __shfl(pbh, row < G ? row : 0);
-        pr[i] = row < G ? v : 0.0f;
-      }
-      if (vcur) {  // an invalid page's metadata may hold anything
+        for (int kk = 0; kk < 4; ++kk) {
+          const float4 q0 = *reinterpret_cast<const float4*>(qrow + 8 * kk);
+          const float4 q1 = *reinterpret_cast<const float4*>(qrow + 8 * kk + 4);
+          const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+          const float4 a0 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk);
+          const float4 a1 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk + 4);
+          const float4 b0 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk);
+          const float4 b1 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk + 4);
+          const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const float be[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int c = slot_channel(i);
+            const float x = qv[c] * al[c];
+            const half_t hi = (half_t)x;
+            const half_t t = lo_col ? hi : (half_t)0.0f;
+            qB[kk][i] = (half_t)(x - (float)t);
+            qb += qv[c] * be[c];
+          }
+        }
+        qb += __shfl_xor(qb, 16);
+        qb += __shfl_xor(qb, 32);
+        // move the output into this page's gamma domain
+        {
+          const float4 g0 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n);
+          const float4 g1 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n + 4);
+          const float gn[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+          if (have_gamma) {
+#pragma unroll
+            for (int nn = 0; nn < NV; ++nn) {
+              const float r = gcur[nn] * __builtin_amdgcn_rcpf(gn[nn]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) st.o[nn][i] *= r;
+            }
+          }
+#pragma unroll
+          for (int nn = 0; nn < NV; ++nn) gcur[nn] = gn[nn];
+          have_gamma = true;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+          issue(u);
+          process_unit<G>(rr[u % kRing], mt, u, n, gq, qB, qb, a.qk_scale, st);
+        }
+        // end of page: o' += sum_t p_t beta'_t (every channel of the head)
+        float pbh = st.pb + __shfl_xor(st.pb, 16);
+        pbh += __shfl_xor(pbh, 32);
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * gq + i;
+          const float v = __shfl(pbh, row < G ? row : 0);
+          pr[i] = row < G ? v : 0.0f;
+        }
 #pragma unroll
         for (int nn = 0; nn < NV; ++nn)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) st.o[nn][i] += gam[nn] * (st.accp[nn][i] + pr[i]);
-      }
+          for (int i = 0; i < 4; ++i) st.o[nn][i] += pr[i];
+        st.pb = 0.0f;
+      } else {
 #pragma unroll
-      for (int nn = 0; nn < NV; ++nn) st.accp[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
-      st.pb = 0.0f;
+        for (int u = 0; u < kUnits; ++u) issue(u);
+      }
       pc = pn;
       vcur = vnext;
     }
@@ -361,7 +397,7 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * gq + i;
-      if (row < 2 * G) lds_o[w][row][8 * n + nn] = st.o[nn][i];
+      if (row < 2 * G) lds_o[w][row][8 * n + nn] = gcur[nn] * st.o[nn][i];
     }
   __syncthreads();
 
@@ -412,10 +448,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 //   M = max(m_s, tail scores), L = sum 2^(m_s-M) l_s + sum_t 2^(s_t-M),
 //   o = ( H sum 2^(m_s-M) o_s + sum_t 2^(s_t-M) v_t ) / L.
 // 128 threads; thread d owns channel d (and tail token d for the scores).
+// The partials are read in one round trip per 8 splits; the inverse rotation
+// runs as six in-wave butterfly stages and one exchange between the waves.
 __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
-  __shared__ float wts[kMaxSplits];
   __shared__ float e_tail[P];
-  __shared__ float y[2][D];
+  __shared__ float xch[D];
   __shared__ float red[2];
   const int kvh = blockIdx.x, b = blockIdx.y, g = blockIdx.z, t = threadIdx.x;
   const int S = a.num_splits;
@@ -426,59 +463,54 @@ __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
   const int n_tail = a.tail ? ctx % P : 0;
   const int hq = kvh * a.G + g;
 
-  float mp = kNegInf;
-  for (int sp = t; sp < S; sp += 128) mp = fmaxf(mp, recs[sp * rf + g]);
-  // tail scores (log2 units), thread t = tail token t
-  float lg = kNegInf;
-  if (t < n_tail) {
-    const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + t) * D;
-    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + hq) * D;
-    float acc = 0.0f;
-    for (int c8 = 0; c8 < D / 8; ++c8) {
-      const half8_t kv = *reinterpret_cast<const half8_t*>(kt + 8 * c8);
-      const half8_t qv = *reinterpret_cast<const half8_t*>(qp + 8 * c8);
+  float M = kNegInf, L = 0.0f, O = 0.0f;
+  merge_splits(recs, rf, S, g, 2 * kMaxGroup + g * D + t, M, L, O);
+
+  float ot = 0.0f;
+  if (n_tail > 0) {  // uniform across the block
+    // tail scores (log2 units), thread t = tail token t
+    float lg = kNegInf;
+    if (t < n_tail) {
+      const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + t) * D;
+      const uint16_t* qp = a.q + ((int64_t)b * a.Hq + hq) * D;
+      float acc = 0.0f;
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const half8_t kv = *reinterpret_cast<const half8_t*>(kt + 8 * c8);
+        const half8_t qv = *reinterpret_cast<const half8_t*>(qp + 8 * c8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)kv[e] * (float)qv[e];
+        for (int e = 0; e < 8; ++e) acc += (float)kv[e] * (float)qv[e];
+      }
+      lg = acc * a.qk_scale;
     }
-    lg = acc * a.qk_scale;
+    const float mt = block_max(lg, red);
+    const float e = t < n_tail ? exp2f(lg - mt) : 0.0f;
+    e_tail[t] = e;
+    const float lt = block_sum(e, red);  // its barriers also publish e_tail
+    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P) * D + t;
+    for (int j = 0; j < n_tail; ++j) ot += e_tail[j] * (float)__builtin_bit_cast(half_t, vt[(int64_t)j * D]);
+    const float mx = fmaxf(M, mt);
+    const float sp = exp2f(M - mx), st = exp2f(mt - mx);
+    L = L * sp + lt * st;
+    O *= sp;
+    ot *= st;
+    M = mx;
   }
-  const float M = block_max(fmaxf(mp, lg), red);
   uint16_t* orow = a.out + ((int64_t)b * a.Hq + hq) * D;
-  if (M == kNegInf) {  // empty context
+  if (M == kNegInf) {  // empty context (uniform)
     orow[t] = 0;
     return;
   }
-  float lp = 0.0f;
-  for (int sp = t; sp < S; sp += 128) {
-    const float ms = recs[sp * rf + g];
-    const float f = ms == kNegInf ? 0.0f : exp2f(ms - M);
-    wts[sp] = f;
-    lp += f * recs[sp * rf + kMaxGroup + g];
+  // inverse rotation of the split part across the 128 channels
+#pragma unroll
+  for (int hb = 1; hb < 64; hb <<= 1) {
+    const float p = __shfl_xor(O, hb);
+    O = (t & hb) ? p - O : O + p;
   }
-  const float e = t < n_tail ? exp2f(lg - M) : 0.0f;
-  e_tail[t] = e;
-  const float L = block_sum(lp + e, red);  // includes the barrier for wts / e_tail
-
-  // rotated-basis output, channel t, then the inverse rotation
-  const float* col = recs + 2 * kMaxGroup + g * D + t;
-  float o = 0.0f;
-  for (int sp = 0; sp < S; ++sp) o += wts[sp] * col[sp * rf];
-  y[0][t] = o;
-  int cur = 0;
-  for (int hb = 1; hb < D; hb <<= 1) {
-    __syncthreads();
-    const float* yc = y[cur];
-    y[cur ^ 1][t] = (t & hb) ? yc[t - hb] - yc[t] : yc[t] + yc[t + hb];
-    cur ^= 1;
-  }
-  float out = y[cur][t] * kInvSqrt128;
-  // tail values in the original basis
-  float ot = 0.0f;
-  if (n_tail > 0) {
-    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P) * D + t;
-    for (int j = 0; j < n_tail; ++j) ot += e_tail[j] * (float)__builtin_bit_cast(half_t, vt[(int64_t)j * D]);
-  }
-  out = (out + ot) / L;
+  xch[t] = O;
+  __syncthreads();
+  const float p = xch[t ^ 64];
+  O = (t & 64) ? p - O : O + p;
+  const float out = (O * kInvSqrt128 + ot) / L;
   orow[t] = __builtin_bit_cast(uint16_t, (half_t)out);
 }
 
