@@ -103,36 +103,41 @@ __device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2
       i8x4_to_h_biased(r.k[2 * kk], a, b);
       i8x4_to_h_biased(r.k[2 * kk + 1], c, d);
     } else {
-      e4m3x4_to_h(r.k[2 * kk], a, b);
-      e4m3x4_to_h(r.k[2 * kk + 1], c, d);
+      uint32_t p0, p1, p2, p3;
+      e4m3x4_to_h_hw(r.k[2 * kk], p0, p1);
+      e4m3x4_to_h_hw(r.k[2 * kk + 1], p2, p3);
+      a = as_h2(p0), b = as_h2(p1), c = as_h2(p2), d = as_h2(p3);
     }
     return cat(a, b, c, d);
   } else {
     constexpr int DL = D / 4;
-    const uint32_t x = r.k[kk];
-    const uint32_t hl = e2m1x4_hibytes(x & 0x0F0F0F0Fu);         // channels 0,2,4,6
-    const uint32_t hh = e2m1x4_hibytes((x >> 4) & 0x0F0F0F0Fu);  // channels 1,3,5,7
+    uint32_t h[4];
+    e2m1x8_to_h(r.k[kk], h);  // channels 0..7 in order
     const half_t sc = ksc[(DL >= 32) ? (8 * kk) / 16 : 0];
     const half2_t s2 = {sc, sc};
-    return cat(as_h2(perm(hh, hl, 0x040C000Cu)) * s2, as_h2(perm(hh, hl, 0x050C010Cu)) * s2,
-               as_h2(perm(hh, hl, 0x060C020Cu)) * s2, as_h2(perm(hh, hl, 0x070C030Cu)) * s2);
+    return cat(as_h2(h[0]) * s2, as_h2(h[1]) * s2, as_h2(h[2]) * s2, as_h2(h[3]) * s2);
   }
 }
 
 // V operand for PV MFMA nn: channel (D/16)*n + nn of tokens 4*gq .. +3.
+// NVFP4: the dword holds the channel pair (nn & ~1, nn | 1) of the 4 tokens,
+// one token per byte; `pairs` are its conversions, (even, odd) per token.
 template <int FMT, int D>
-__device__ __forceinline__ half4_t v_operand(const Raw<FMT, D>& r, int nn, half2_t s01, half2_t s23) {
+__device__ __forceinline__ half4_t v_operand(const Raw<FMT, D>& r, int nn, half2_t s01, half2_t s23,
+                                             const uint32_t (&pairs)[4]) {
   if constexpr (FMT != 4) {
     half2_t a, b;
-    if constexpr (FMT == 2)
+    if constexpr (FMT == 2) {
       i8x4_to_h(r.v[nn], a, b);
-    else
-      e4m3x4_to_h(r.v[nn], a, b);
+    } else {
+      uint32_t p0, p1;
+      e4m3x4_to_h_hw(r.v[nn], p0, p1);
+      a = as_h2(p0), b = as_h2(p1);
+    }
     return cat4(a, b);
   } else {
-    const uint32_t w = r.v[nn / 2];
-    const uint32_t h = e2m1x4_hibytes((nn & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu));
-    return cat4(as_h2(perm(0u, h, 0x010C000Cu)) * s01, as_h2(perm(0u, h, 0x030C020Cu)) * s23);
+    const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+    return cat4(as_h2(perm(pairs[1], pairs[0], sel)) * s01, as_h2(perm(pairs[3], pairs[2], sel)) * s23);
   }
 }
 
@@ -213,10 +218,14 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
       pA = half4_t{0, 0, 0, 0};
     half2_t vs01 = {0, 0}, vs23 = {0, 0};
     if constexpr (FMT == 4) e4m3x4_to_h(r.vsc, vs01, vs23);
+    uint32_t pairs[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int nn = 0; nn < NV; ++nn)
-      st.acc[nn] =
-          __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand<FMT, D>(r, nn, vs01, vs23), st.acc[nn], 0, 0, 0);
+    for (int nn = 0; nn < NV; ++nn) {
+      if constexpr (FMT == 4)
+        if ((nn & 1) == 0) e2m1x8_to_h(r.v[nn / 2], pairs);
+      st.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand<FMT, D>(r, nn, vs01, vs23, pairs),
+                                                         st.acc[nn], 0, 0, 0);
+    }
   };
 
   if (__any(over)) {

@@ -174,4 +174,36 @@ __device__ __forceinline__ uint32_t e2m1x4_hibytes(uint32_t n) {
   return mag | ((n & 0x08080808u) << 4);
 }
 
+// ---------------------------------------------------------------------------
+// gfx950 hardware conversions, issued directly: the compiler's lowering of the
+// matching builtins repacks the two binary16 results when they are used one by
+// one (the high half is replaced by a copy of the low half).  With scale 1.0
+// both conversions are exact for every finite code.  The surrounding s_nop
+// covers the one-wait-state forwarding hazard of the scaled conversions on
+// either side, which the compiler cannot see inside an asm statement.
+// ---------------------------------------------------------------------------
+
+// Eight E2M1 codes (two per byte, low nibble first) -> four binary16 pairs in
+// code order.
+__device__ __forceinline__ void e2m1x8_to_h(uint32_t w, uint32_t (&h)[4]) {
+  asm("s_nop 1\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %0, %4, 1.0\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %1, %4, 1.0 op_sel:[1,0,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %2, %4, 1.0 op_sel:[0,1,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %3, %4, 1.0 op_sel:[1,1,0]\n\t"
+      "s_nop 1"
+      : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+      : "v"(w));
+}
+
+// Four E4M3 codes -> two binary16 pairs in code order.
+__device__ __forceinline__ void e4m3x4_to_h_hw(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  asm("s_nop 1\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %0, %2, 1.0\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %1, %2, 1.0 op_sel:[1,0,0]\n\t"
+      "s_nop 1"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(w));
+}
+
 }  // namespace kvq

@@ -7,28 +7,6 @@
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// E4M3 pairs -> binary16 with a binary32 scale: out[2i], out[2i+1] for the
-// bytes (i, i) of word i (low word).
-__global__ void k_cvt_fp8_f16(const float* scales, int n_scales, uint16_t* out) {
-  const int c = threadIdx.x;  // code 0..255
-  const int si = blockIdx.x;
-  if (c >= 256 || si >= n_scales) return;
-  const uint32_t src = (uint32_t)c | ((uint32_t)c << 8);
-  const half2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, scales[si], false);
-  out[((int64_t)si * 256 + c) * 2] = __builtin_bit_cast(uint16_t, h[0]);
-  out[((int64_t)si * 256 + c) * 2 + 1] = __builtin_bit_cast(uint16_t, h[1]);
-}
-
-// E2M1 nibble pairs -> binary16 with a binary32 scale: byte = lo | hi << 4.
-__global__ void k_cvt_fp4_f16(const float* scales, int n_scales, uint16_t* out) {
-  const int c = threadIdx.x;  // byte 0..255
-  const int si = blockIdx.x;
-  if (c >= 256 || si >= n_scales) return;
-  const half2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)c, scales[si], 0);
-  out[((int64_t)si * 256 + c) * 2] = __builtin_bit_cast(uint16_t, h[0]);
-  out[((int64_t)si * 256 + c) * 2 + 1] = __builtin_bit_cast(uint16_t, h[1]);
-}
-
 // binary32 -> E4M3 with the gfx950 packed conversion (input pre-clamped to
 // +-448 by the caller's data).
 __global__ void k_cvt_f32_fp8(const float* x, int64_t n, uint8_t* out) {
@@ -46,13 +24,55 @@ __global__ void k_cvt_f32_fp4(const float* x, int64_t n, uint8_t* out) {
   out[i] = (uint8_t)(r & 0xF);
 }
 
+// E2M1 pairs -> binary16, issued directly as the library does (the
+// compiler's lowering of the builtin repacks the two results when they are
+// used one by one), byte selector k = 0..3.
+template <int K>
+__device__ __forceinline__ uint32_t cvt_fp4_byte(uint32_t w, float scale) {
+  uint32_t r;
+  if constexpr (K == 0)
+    asm volatile("v_cvt_scalef32_pk_f16_fp4 %0, %1, %2\n\ts_nop 1" : "=v"(r) : "v"(w), "v"(scale));
+  else if constexpr (K == 1)
+    asm volatile("v_cvt_scalef32_pk_f16_fp4 %0, %1, %2 op_sel:[1,0,0]\n\ts_nop 1" : "=v"(r) : "v"(w), "v"(scale));
+  else if constexpr (K == 2)
+    asm volatile("v_cvt_scalef32_pk_f16_fp4 %0, %1, %2 op_sel:[0,1,0]\n\ts_nop 1" : "=v"(r) : "v"(w), "v"(scale));
+  else
+    asm volatile("v_cvt_scalef32_pk_f16_fp4 %0, %1, %2 op_sel:[1,1,0]\n\ts_nop 1" : "=v"(r) : "v"(w), "v"(scale));
+  return r;
+}
+
+__global__ void k_cvt_fp4_f16_asm(const uint32_t* src, int n, float scale, uint32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = src[i];
+  out[4 * (int64_t)i + 0] = cvt_fp4_byte<0>(w, scale);
+  out[4 * (int64_t)i + 1] = cvt_fp4_byte<1>(w, scale);
+  out[4 * (int64_t)i + 2] = cvt_fp4_byte<2>(w, scale);
+  out[4 * (int64_t)i + 3] = cvt_fp4_byte<3>(w, scale);
+}
+
+// E4M3 pairs -> binary16, issued directly: word i -> out[2i] (bytes 0, 1),
+// out[2i + 1] (bytes 2, 3).
+__global__ void k_cvt_fp8_f16_asm(const uint32_t* src, int n, uint32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t lo, hi;
+  asm("s_nop 1\n\tv_cvt_scalef32_pk_f16_fp8 %0, %2, 1.0\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %1, %2, 1.0 op_sel:[1,0,0]\n\ts_nop 1"
+      : "=&v"(lo), "=&v"(hi) : "v"(src[i]));
+  out[2 * (int64_t)i] = lo;
+  out[2 * (int64_t)i + 1] = hi;
+}
+
 extern "C" {
-int probe_cvt_fp8_f16(const float* scales, int n_scales, uint16_t* out) {
-  k_cvt_fp8_f16<<<n_scales, 256>>>(scales, n_scales, out);
+int probe_cvt_fp8_f16_asm(const uint32_t* src, int n, uint32_t* out) {
+  if (n <= 0) return 0;
+  k_cvt_fp8_f16_asm<<<(n + 255) / 256, 256>>>(src, n, out);
   return (int)hipGetLastError();
 }
-int probe_cvt_fp4_f16(const float* scales, int n_scales, uint16_t* out) {
-  k_cvt_fp4_f16<<<n_scales, 256>>>(scales, n_scales, out);
+int probe_cvt_fp4_f16_asm(const uint32_t* src, int n, float scale, uint32_t* out) {
+  if (n <= 0) return 0;
+  k_cvt_fp4_f16_asm<<<(n + 255) / 256, 256>>>(src, n, scale, out);
   return (int)hipGetLastError();
 }
 int probe_cvt_f32_fp8(const float* x, int64_t n, uint8_t* out) {

@@ -75,17 +75,51 @@ def test_cvt_f32_to_e2m1_matches_oracle(PL, O):
     assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:8]]
 
 
-def test_cvt_e4m3_to_f16_unit_scale_exact(PL, O):
-    """E4M3 -> binary16 with scale 1 gives the exact value of every finite code."""
+def _all_byte_positions(rng):
+    """Every byte value at every byte position of a word, the other bytes random."""
+    words = rng.integers(0, 2 ** 32, 1024, dtype=np.uint64).astype(np.uint32)
+    for pos in range(4):
+        for b in range(256):
+            w = int(words[pos * 256 + b]) & ~(0xFF << (8 * pos))
+            words[pos * 256 + b] = w | (b << (8 * pos))
+    return words
+
+
+def test_cvt_e4m3_to_f16_exact(PL, O):
+    """E4M3 -> binary16 (scale 1), as the decode issues it: exact value of
+    every finite code, in code order, in both halves."""
     import torch
-    scales = torch.tensor([1.0], dtype=torch.float32, device="cuda")
-    out = torch.zeros(512, dtype=torch.int16, device="cuda")
+    words = _all_byte_positions(np.random.default_rng(2))
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    out = torch.zeros(words.size * 2, dtype=torch.int32, device="cuda")
     log("probe cvt e4m3->f16")
-    assert PL.probe_cvt_fp8_f16(_ptr(scales), 1, _ptr(out)) == 0
+    assert PL.probe_cvt_fp8_f16_asm(_ptr(src), words.size, _ptr(out)) == 0
     torch.cuda.synchronize()
-    got = out.cpu().numpy().view(np.float16).astype(np.float64).reshape(256, 2)
-    for c in range(256):
-        if (c & 0x7F) == 0x7F:
-            continue  # NaN codes
-        v = O.e4m3_decode(c)
-        assert got[c, 0] == v and got[c, 1] == v, (c, got[c], v)
+    got = out.cpu().numpy().view(np.float16).astype(np.float64).reshape(words.size, 4)
+    dec = np.array([O.e4m3_decode(c) for c in range(256)])
+    for i, w in enumerate(words):
+        for k in range(4):
+            c = (int(w) >> (8 * k)) & 0xFF
+            if (c & 0x7F) == 0x7F:
+                assert np.isnan(got[i, k])
+            else:
+                assert got[i, k] == dec[c] and np.signbit(got[i, k]) == np.signbit(dec[c]), (hex(int(w)), k)
+
+
+def test_cvt_e2m1_to_f16_exact(PL, O):
+    """E2M1 pairs -> binary16 (scale 1), as the decode issues them: every
+    byte at every position gives (low nibble, high nibble) exactly."""
+    import torch
+    words = _all_byte_positions(np.random.default_rng(3))
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    out = torch.zeros(words.size * 4, dtype=torch.int32, device="cuda")
+    log("probe cvt e2m1->f16")
+    assert PL.probe_cvt_fp4_f16_asm(_ptr(src), words.size, ctypes.c_float(1.0), _ptr(out)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.float16).astype(np.float64).reshape(words.size, 4, 2)
+    dec = np.array([O.e2m1_decode(c) for c in range(16)])
+    for i, w in enumerate(words):
+        for k in range(4):
+            b = (int(w) >> (8 * k)) & 0xFF
+            for e, c in enumerate((b & 15, b >> 4)):
+                assert got[i, k, e] == dec[c] and np.signbit(got[i, k, e]) == np.signbit(dec[c]), (hex(int(w)), k, e)
