@@ -6,10 +6,11 @@
 // scale metadata into the page) and of [P4] "KV 量化", §写和读 (divide by the
 // scale, convert, keep the bits as bytes).
 //
-// Work mapping: one token-head row (D binary16 values of K or V) is handled by
-// a group of lanes inside a wavefront -- D/8 lanes of 8 values for the 8-bit
-// formats, D/16 lanes of one 16-value block for NVFP4 -- so each lane issues
-// 16-byte loads and the row max is a short cross-lane max.  Rows are ordered
+// Work mapping.  8-bit formats: one workgroup per (16 consecutive tokens, kv
+// head); a run of tokens that fills one aligned 16-token group of a page is
+// quantised by lanes of 16 values and written as contiguous 16-byte stores,
+// any other slot pattern row by row (D/8 lanes of 8 values).  NVFP4: D/16
+// lanes of one 16-value block per token-head row; rows are ordered
 // [side][token][head], so a wavefront reads consecutive rows of the input.
 // This file is built with -ffp-contract=off: every binary32 operation below
 // rounds exactly as written.
@@ -67,12 +68,29 @@ __device__ __forceinline__ void load_halves8(const uint16_t* p, float* x) {
 // 8-bit formats: FMT 1 = FP8 per-tensor, 2 = INT8 per-token-head,
 // 3 = FP8 per-token-head.
 // ---------------------------------------------------------------------------
+// Row scale of the 8-bit formats ([P3] §可运行 fake-quant 实验: floor the max
+// at 1e-8, then divide by the top code: 127 for INT8, FP8_MAX = 448 for E4M3,
+// [P1] §2.2).
+template <int FMT>
+__device__ __forceinline__ float row_scale(float amax) {
+  return fmaxf(amax, 1e-8f) / (FMT == 2 ? 127.0f : 448.0f);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode8(float x, float s, Recip rc) {
+  const float y = div_rn(x, s, rc);
+  if constexpr (FMT == 2) {
+    const float q = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+    return (uint32_t)(int32_t)q & 0xFFu;
+  } else {
+    return e4m3_mag(fabsf(y)) | (sign_bit(x) << 7);
+  }
+}
+
+// One token-head row by D/8 lanes (lane j: channels 8j .. 8j+7), any slot.
 template <int FMT, int D>
-__global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
+__device__ __forceinline__ void write_row_8bit(const WriteArgs& a, int64_t row, int j) {
   constexpr int LPR = D / 8;
-  constexpr int RPB = kBlock / LPR;
-  const int j = threadIdx.x % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   RowCtx c;
   if (!row_ctx(a, row, c)) return;
 
@@ -86,24 +104,12 @@ __global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = group_max<LPR>(amax);
-    // [P3] §可运行 fake-quant 实验: floor the max at 1e-8, then divide by the
-    // top code (127 for INT8, FP8_MAX = 448 for E4M3, [P1] §2.2)
-    s = fmaxf(amax, 1e-8f) / (FMT == 2 ? 127.0f : 448.0f);
+    s = row_scale<FMT>(group_max<LPR>(amax));
   }
   const Recip rc = make_recip(s);
-
   uint32_t code[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float y = div_rn(x[i], s, rc);
-    if constexpr (FMT == 2) {
-      const float q = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
-      code[i] = (uint32_t)(int32_t)q & 0xFFu;
-    } else {
-      code[i] = e4m3_mag(fabsf(y)) | (sign_bit(x[i]) << 7);
-    }
-  }
+  for (int i = 0; i < 8; ++i) code[i] = encode8<FMT>(x[i], s, rc);
 
   // 16-token groups of K and V are laid out in the decode's operand order
   // (see k8_offset / v8_offset)
@@ -120,6 +126,99 @@ __global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
   if (FMT != 1 && j == 0) {
     float* sp = reinterpret_cast<float*>(c.chunk + a.geom.k_scales) + c.side * a.P + c.t;
     *sp = s;
+  }
+}
+
+// Whether tokens 16g .. 16g+15 fill one aligned 16-token group of a page, in
+// order: then the group's K and V bytes are contiguous runs of the cache.
+// Returns the group's first slot, or -1.  Uniform across the workgroup.
+__device__ __forceinline__ int64_t group_slot(const WriteArgs& a, int64_t g, int* s_ok, int64_t* s_slot0) {
+  const int tid = threadIdx.x;
+  if (tid == 0) *s_ok = 1;
+  __syncthreads();
+  if (tid < 16) {
+    const int64_t tok = 16 * g + tid;
+    bool ok = tok < a.n_tok;
+    int64_t sl = ok ? a.slots[tok] : -1;
+    const int64_t s0 = ok ? a.slots[16 * g] : -1;
+    ok = ok && s0 >= 0 && s0 < (int64_t)a.num_pages * a.P && (s0 & 15) == 0 && sl == s0 + tid;
+    if (!ok) *s_ok = 0;
+    if (tid == 0) *s_slot0 = s0;
+  }
+  __syncthreads();
+  return *s_ok ? *s_slot0 : -1;
+}
+
+// One workgroup per (16 consecutive tokens, kv head): 128 lanes per side,
+// lane (token s, chunk q) quantises channels 16q .. 16q+15 of token s.  When
+// the 16 tokens fill one aligned page group (a prefill-style run) the codes
+// are assembled in LDS in the cache's byte order and written as contiguous
+// 16-byte stores; otherwise every row goes through the per-row path.
+template <int FMT, int D>
+__global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
+  constexpr int GB = 16 * D;  // bytes of one 16-token group, one side
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][GB];
+  __shared__ float s_scale[2][16];
+  __shared__ int s_ok;
+  __shared__ int64_t s_slot0;
+  const int64_t g = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t slot0 = group_slot(a, g, &s_ok, &s_slot0);
+
+  if (slot0 < 0) {
+    // general slots: rows (side, token 16g + i, head h), D/8 lanes each
+    constexpr int LPR = D / 8;
+    for (int t = tid; t < 32 * LPR; t += kBlock) {
+      const int rr = t / LPR, side = rr / 16, i = rr % 16;
+      const int64_t tok = 16 * g + i;
+      if (tok >= a.n_tok) continue;
+      write_row_8bit<FMT, D>(a, (int64_t)side * a.n_tok * a.H + tok * a.H + h, t % LPR);
+    }
+    return;
+  }
+
+  constexpr int QPR = D / 16;               // lanes per token row
+  constexpr int LPS = 16 * QPR;             // lanes per side
+  const int side = tid / LPS;               // D = 128: 128 lanes per side
+  const bool active = tid < 2 * LPS;
+  const int lt = tid % LPS, sidx = lt / QPR, q = lt % QPR;
+  if (active) {
+    const uint16_t* src = (side ? a.v : a.k) + ((16 * g + sidx) * a.H + h) * (int64_t)D + 16 * q;
+    float x[16];
+    load_halves8(src, x);
+    load_halves8(src + 8, x + 8);
+    float s;
+    if constexpr (FMT == 1) {
+      s = side ? a.v_scale : a.k_scale;
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      s = row_scale<FMT>(group_max<QPR>(amax));
+      if (q == 0) s_scale[side][sidx] = s;
+    }
+    const Recip rc = make_recip(s);
+    uint8_t* dst = s_codes[side];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 16 * q + i;
+      const int off = side == 0 ? (int)k8_offset<D>(sidx, d) : (int)v8_offset<D>(sidx, d);
+      dst[off] = (uint8_t)encode8<FMT>(x[i], s, rc);
+    }
+  }
+  __syncthreads();
+  const int64_t page = slot0 / a.P;
+  const int t0 = (int)(slot0 - page * a.P);
+  uint8_t* chunk = a.cache + (page * a.H + h) * a.geom.chunk_bytes;
+  for (int i = tid; i < 2 * GB / 16; i += kBlock) {
+    const int sd = i / (GB / 16), o = 16 * (i % (GB / 16));
+    uint8_t* base = chunk + (sd ? a.geom.v_codes : 0) + (int64_t)D * t0;
+    *reinterpret_cast<uint4*>(base + o) = *reinterpret_cast<const uint4*>(&s_codes[sd][o]);
+  }
+  if (FMT != 1 && tid < 32) {
+    float* sp = reinterpret_cast<float*>(chunk + a.geom.k_scales) + (tid / 16) * a.P + t0 + (tid % 16);
+    *sp = s_scale[tid / 16][tid % 16];
   }
 }
 
@@ -225,10 +324,13 @@ hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   } else {
+    const int64_t groups = (a.n_tok + 15) / 16;
+    if (groups > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
+    const dim3 g2((unsigned)groups, (unsigned)a.H);
     switch (a.D) {
-      case 32: quant_write_8bit<FMT, 32><<<grid(4), kBlock, 0, s>>>(a); break;
-      case 64: quant_write_8bit<FMT, 64><<<grid(8), kBlock, 0, s>>>(a); break;
-      case 128: quant_write_8bit<FMT, 128><<<grid(16), kBlock, 0, s>>>(a); break;
+      case 32: quant_write_8bit<FMT, 32><<<g2, kBlock, 0, s>>>(a); break;
+      case 64: quant_write_8bit<FMT, 64><<<g2, kBlock, 0, s>>>(a); break;
+      case 128: quant_write_8bit<FMT, 128><<<g2, kBlock, 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -69,6 +69,43 @@ def test_write_bytes_match_oracle(K, O, fmt, flags, D, P):
         assert mm is None, f"cache byte {mm[0]}: gpu {mm[1]:#x} oracle {mm[2]:#x} ({mm[3]} bytes differ)"
 
 
+def run_slots(rng, P, num_pages, n_runs):
+    """Slot mappings as a prefill writes them: runs of consecutive slots that
+    fill pages in order (aligned 16-token groups), plus runs that start
+    mid-group, a group with two tokens swapped, a skipped slot and ragged
+    run ends.  Every slot is written at most once."""
+    pages = rng.permutation(num_pages)
+    slots = []
+    for r in range(n_runs):
+        pg = int(pages[r])
+        start = 0 if r % 3 else 5  # every third run starts off a 16-token group
+        n = P - start if r % 4 else P // 2 + 3
+        slots.append(pg * P + start + np.arange(n))
+    s = np.concatenate(slots).astype(np.int64)
+    s[[36, 37]] = s[[37, 36]]  # two tokens swapped: a group out of order
+    s[40] = -1                  # skipped
+    return s
+
+
+@pytest.mark.parametrize("fmt,flags", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("D,P", [(128, 16), (64, 32), (32, 64), (128, 128)])
+def test_write_runs_match_oracle(K, O, fmt, flags, D, P):
+    """Prefill-style slot runs (the coalesced group path) and the breaks in
+    them (the per-row path) give the oracle's bytes."""
+    rng = np.random.default_rng(3000 + 100 * fmt + D + P + flags)
+    H, num_pages = 3, 9
+    slots = run_slots(rng, P, num_pages, 7)
+    n = slots.size
+    k16 = edge_rows(rng, n, H, D)
+    v16 = edge_rows(rng, n, H, D)
+    lay = layout_for(K, fmt, flags, H, D, P, num_pages, k16, v16)
+    log(f"write runs fmt={fmt} flags={flags} D={D} P={P} n={n}")
+    ref = O.quantize_write(olayout(lay), k16, v16, slots)
+    got = gpu_write(K, lay, k16, v16, slots).cpu().numpy()
+    mm = first_mismatch(got, ref)
+    assert mm is None, f"cache byte {mm[0]}: gpu {mm[1]:#x} oracle {mm[2]:#x} ({mm[3]} bytes differ)"
+
+
 @pytest.mark.parametrize("fmt,flags", FORMATS, ids=FMT_IDS)
 def test_dequantize_matches_oracle(K, O, fmt, flags):
     import torch
