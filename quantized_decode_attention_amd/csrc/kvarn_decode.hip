@@ -11,12 +11,13 @@
 //   sum_t p_t v_t = H [ gamma (.) ( sum_t (p_t alpha'_t) c'_t + sum_t p_t beta'_t ) ]
 // The first bracket is one MFMA product per 16 tokens with A = 4-bit codes
 // (exact in binary16) and B = q~ (.) alpha (per page, split into binary16
-// high and low halves in the MFMA's spare columns); the second is the usual P V product with the
-// per-token V scale folded into P; gamma changes from tile to tile, so the
-// output is kept in the current page's gamma domain and rescaled once per page.  Tokens of the
-// incomplete last tile are kept by the caller in binary16 and attended by the
-// merge kernel, which also rotates the output back ([P2] §配置与部署: the
-// decode path keeps a small fixed workspace for the unquantised tail).
+// high and low halves in the MFMA's spare columns).  The second is the usual
+// P V product with the per-token V scale folded into P; gamma changes from
+// tile to tile, so the output is kept in the current page's gamma domain and
+// rescaled once per page.  Tokens of the incomplete last tile are kept by the
+// caller in binary16 and attended by the merge kernel, which also rotates the
+// output back ([P2] §配置与部署: the decode path keeps a small fixed
+// workspace for the unquantised tail).
 //
 // Decomposition as for the other formats: a workgroup of 4 wavefronts per
 // (sequence, kv head, context split), wave w walks pages w, w+4, ... of the
@@ -94,8 +95,8 @@ struct KvState {
   float m_run, l_run;
 };
 
-template <int G>
 // One sub-page of a valid page (invalid pages are skipped by the caller).
+template <int G>
 __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, int u, int n, int gq,
                                              const half8_t (&qB)[4], float qb, float qk, KvState& st) {
   float4_t s = {0.f, 0.f, 0.f, 0.f};

@@ -9,9 +9,8 @@
 // Work mapping.  8-bit formats: one workgroup per (16 consecutive tokens, kv
 // head); a run of tokens that fills one aligned 16-token group of a page is
 // quantised by lanes of 16 values and written as contiguous 16-byte stores,
-// any other slot pattern row by row (D/8 lanes of 8 values).  NVFP4: D/16
-// lanes of one 16-value block per token-head row; rows are ordered
-// [side][token][head], so a wavefront reads consecutive rows of the input.
+// any other slot pattern row by row (D/8 lanes of 8 values).  NVFP4 uses the
+// same group / per-row split with one lane per 16-value block.
 // This file is built with -ffp-contract=off: every binary32 operation below
 // rounds exactly as written.
 #include "kvq_device.h"
@@ -258,31 +257,18 @@ __device__ __forceinline__ float nvfp4_block(const float* x, float st, uint32_t 
   return e2[0];
 }
 
-template <int D>
-__global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
-  constexpr int LPR = D / 16;
-  constexpr int RPB = kBlock / LPR;
-  const int j = threadIdx.x % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  RowCtx c;
-  if (!row_ctx(a, row, c)) return;
-
-  float x[16];
-  const uint16_t* src = (c.side ? a.v : a.k) + c.r * D + 16 * j;
-  load_halves8(src, x);
-  load_halves8(src + 8, x + 8);
-
+// Codes and block-scale code of one 16-value block (lane j of a row): the
+// block max lands near 6, the top of the E2M1 grid; with 4over6 ([P5]
+// §用一组数直观看缩放的作用) the max/4 candidate is kept if strictly better.
+// byte[i] packs values 2i (low nibble) and 2i+1.
+__device__ __forceinline__ uint32_t nvfp4_encode_block(const float* x, float st, int flags, uint32_t* byte) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  const float st = c.side ? a.v_scale : a.k_scale;
-
-  // block scale: the block max lands near 6, the top of the E2M1 grid
   uint32_t sb = e4m3_mag((amax / 6.0f) / st);
   uint32_t code[16];
   const float err6 = nvfp4_block(x, st, sb, code);
-  if (a.flags & 1) {
-    // 4over6 ([P5] §用一组数直观看缩放的作用): keep max/4 if strictly better
+  if (flags & 1) {
     const uint32_t sb4 = e4m3_mag((amax / 4.0f) / st);
     uint32_t code4[16];
     const float err4 = nvfp4_block(x, st, sb4, code4);
@@ -292,10 +278,22 @@ __global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
       for (int i = 0; i < 16; ++i) code[i] = code4[i];
     }
   }
-
-  uint32_t byte[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) byte[i] = code[2 * i] | (code[2 * i + 1] << 4);
+  return sb;
+}
+
+// One token-head row by D/16 lanes (lane j: block j), any slot.
+template <int D>
+__device__ __forceinline__ void write_row_nvfp4(const WriteArgs& a, int64_t row, int j) {
+  RowCtx c;
+  if (!row_ctx(a, row, c)) return;
+  float x[16];
+  const uint16_t* src = (c.side ? a.v : a.k) + c.r * D + 16 * j;
+  load_halves8(src, x);
+  load_halves8(src + 8, x + 8);
+  uint32_t byte[8];
+  const uint32_t sb = nvfp4_encode_block(x, c.side ? a.v_scale : a.k_scale, a.flags, byte);
   if (c.side == 0) {
     uint2 packed;
     packed.x = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
@@ -311,22 +309,86 @@ __global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
   }
 }
 
+// One workgroup per (16 consecutive tokens, kv head), as for the 8-bit
+// formats: an aligned run is assembled in LDS (K codes, V codes, K block
+// scales: one contiguous run each; V block scales: D/16 runs of 16 bytes) and
+// written with 16-byte stores; other slot patterns go row by row.
+template <int D>
+__global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
+  constexpr int NB = D / 16;         // blocks per row
+  constexpr int CB = 16 * D / 2;     // code bytes of 16 tokens, one side
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][CB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][16 * NB];
+  __shared__ int s_ok;
+  __shared__ int64_t s_slot0;
+  const int64_t g = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t slot0 = group_slot(a, g, &s_ok, &s_slot0);
+
+  if (slot0 < 0) {
+    for (int t = tid; t < 32 * NB; t += kBlock) {
+      const int rr = t / NB, side = rr / 16, i = rr % 16;
+      const int64_t tok = 16 * g + i;
+      if (tok >= a.n_tok) continue;
+      write_row_nvfp4<D>(a, (int64_t)side * a.n_tok * a.H + tok * a.H + h, t % NB);
+    }
+    return;
+  }
+
+  // lane (side, token s, block q); 2 * 16 * NB <= 256 lanes
+  if (tid < 32 * NB) {
+    const int side = tid / (16 * NB), lt = tid % (16 * NB), sidx = lt / NB, q = lt % NB;
+    const uint16_t* src = (side ? a.v : a.k) + ((16 * g + sidx) * a.H + h) * (int64_t)D + 16 * q;
+    float x[16];
+    load_halves8(src, x);
+    load_halves8(src + 8, x + 8);
+    uint32_t byte[8];
+    const uint32_t sb = nvfp4_encode_block(x, side ? a.v_scale : a.k_scale, a.flags, byte);
+    if (side == 0) {
+      uint8_t* kp = s_codes[0] + sidx * (D / 2) + 8 * q;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kp[i] = (uint8_t)byte[i];
+      s_sc[0][sidx * NB + q] = (uint8_t)sb;
+    } else {
+      uint8_t* vp = s_codes[1] + 2 * D * (sidx / 4) + 32 * q + (sidx % 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vp[4 * i] = (uint8_t)byte[i];
+      s_sc[1][q * 16 + sidx] = (uint8_t)sb;  // [block][token]
+    }
+  }
+  __syncthreads();
+  const int64_t page = slot0 / a.P;
+  const int t0 = (int)(slot0 - page * a.P);
+  uint8_t* chunk = a.cache + (page * a.H + h) * a.geom.chunk_bytes;
+  for (int i = tid; i < 2 * CB / 16; i += kBlock) {
+    const int sd = i / (CB / 16), o = 16 * (i % (CB / 16));
+    uint8_t* base = chunk + (sd ? a.geom.v_codes : 0) + (int64_t)t0 * (D / 2);
+    *reinterpret_cast<uint4*>(base + o) = *reinterpret_cast<const uint4*>(&s_codes[sd][o]);
+  }
+  // K block scales: 16 * NB contiguous bytes; V block scales: NB runs of 16
+  if (tid < NB)
+    *reinterpret_cast<uint4*>(chunk + a.geom.k_scales + (int64_t)t0 * NB + 16 * tid) =
+        *reinterpret_cast<const uint4*>(&s_sc[0][16 * tid]);
+  else if (tid < 2 * NB)
+    *reinterpret_cast<uint4*>(chunk + a.geom.v_scales + (int64_t)(tid - NB) * a.P + t0) =
+        *reinterpret_cast<const uint4*>(&s_sc[1][16 * (tid - NB)]);
+}
+
 template <int FMT>
 hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
-  const int64_t rows = 2 * a.n_tok * a.H;
-  if (rows == 0) return hipSuccess;
-  auto grid = [&](int lpr) { return dim3((unsigned)((rows + kBlock / lpr - 1) / (kBlock / lpr))); };
+  if (a.n_tok == 0) return hipSuccess;
+  const int64_t groups = (a.n_tok + 15) / 16;
+  if (groups > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
+  const dim3 g2((unsigned)groups, (unsigned)a.H);
   if constexpr (FMT == 4) {
     switch (a.D) {
-      case 32: quant_write_nvfp4<32><<<grid(2), kBlock, 0, s>>>(a); break;
-      case 64: quant_write_nvfp4<64><<<grid(4), kBlock, 0, s>>>(a); break;
-      case 128: quant_write_nvfp4<128><<<grid(8), kBlock, 0, s>>>(a); break;
+      case 32: quant_write_nvfp4<32><<<g2, kBlock, 0, s>>>(a); break;
+      case 64: quant_write_nvfp4<64><<<g2, kBlock, 0, s>>>(a); break;
+      case 128: quant_write_nvfp4<128><<<g2, kBlock, 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
-    const int64_t groups = (a.n_tok + 15) / 16;
-    if (groups > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
-    const dim3 g2((unsigned)groups, (unsigned)a.H);
     switch (a.D) {
       case 32: quant_write_8bit<FMT, 32><<<g2, kBlock, 0, s>>>(a); break;
       case 64: quant_write_8bit<FMT, 64><<<g2, kBlock, 0, s>>>(a); break;
