@@ -44,7 +44,8 @@ enum {
   O_INT8_PTH = 2,        /* [P1] §2.2; [P3] §它改变缓存表示 formula */
   O_FP8_PTH = 3,         /* [P1] §2.2 pseudo-code */
   O_NVFP4 = 4,           /* [P1] §2.3; [P5] §双层缩放怎样恢复动态范围 */
-  O_KVARN_K4V2_G128 = 5  /* [P2] §技术原理, §配置与部署 */
+  O_KVARN_K4V2_G128 = 5, /* [P2] §技术原理, §配置与部署 */
+  O_INT4_PTH = 6         /* [P4] §scale 和数据放在一起 (int4_per_token_head) */
 };
 enum { O_FLAG_NVFP4_4OVER6 = 1 }; /* [P5] §用一组数直观看缩放的作用 */
 
@@ -177,6 +178,23 @@ static void quant_row_int8(const float* x, int D, uint8_t* codes, float* s_out) 
   *s_out = s;
 }
 
+/* INT4 per-token-head.  [P4] §scale 和数据放在一起 lists int4_per_token_head
+ * beside the INT8 and FP8 modes: half-width data (two values per byte) and one
+ * fp32 scale per token-head side.  The pages give no INT4 formula; reading:
+ * the INT8 rule at 4 bits, s = max(max|x|, 1e-8) / 7, q = clip(rne(x / s),
+ * -7, 7) (symmetric, like INT8's +-127), stored as two's-complement nibbles. */
+static void quant_row_int4(const float* x, int D, uint8_t* codes, float* s_out) {
+  float a = 0.0f;
+  for (int d = 0; d < D; d++) a = fmaxf(a, fabsf(x[d]));
+  float s = fmaxf(a, 1e-8f) / 7.0f;
+  for (int d = 0; d < D; d++) {
+    float y = x[d] / s;
+    float r = clampf(rintf(y), -7.0f, 7.0f);
+    codes[d] = (uint8_t)((int)r & 15);
+  }
+  *s_out = s;
+}
+
 /* FP8 per-token-head, [P1] §2.2: scale = max|x| / FP8_MAX with FP8_MAX = 448
  * (E4M3), codes = E4M3(x / scale).  The 1e-8 floor on the max is borrowed
  * from the INT8 script so an all-zero row has a finite scale. */
@@ -259,6 +277,7 @@ int kvqo_quantize_row(int format, int flags, float scale, const uint16_t* x16, i
   float s;
   switch (format) {
     case O_INT8_PTH: quant_row_int8(x, D, codes, &s); memcpy(scales, &s, 4); return O_OK;
+    case O_INT4_PTH: quant_row_int4(x, D, codes, &s); memcpy(scales, &s, 4); return O_OK;
     case O_FP8_PTH: quant_row_fp8_pth(x, D, codes, &s); memcpy(scales, &s, 4); return O_OK;
     case O_FP8_PER_TENSOR: quant_row_fp8_pt(x, D, scale, codes); return O_OK;
     case O_NVFP4:
@@ -435,6 +454,11 @@ void kvqo_kvarn_tile(const uint16_t* x16, int64_t stride, int side, float* y_rot
  *                                            nibble d%2
  *    K block scales [P][D/16]  at P*D:       byte t*D/16 + d/16
  *    V block scales [D/16][P]  after:        byte (d/16)*P + t
+ *  INT4 per-token-head (two's-complement nibbles, low nibble first):
+ *    K codes  [P][D/2]      at 0:            byte t*D/2 + d/2, nibble d%2
+ *    V codes  [P/4][D/2][4] at P*D/2:        byte 2*D*(t/4) + 4*(d/2) + t%4,
+ *                                            nibble d%2
+ *    K scales fp32 [P] at P*D, V scales fp32 [P] after
  *  KVarN k4v2 (P = D = 128):
  *    K codes  [P][D/2] 4-bit at 0:           byte t*D/2 + d/2, nibble d%2
  *    V codes  [P/4][D] 2-bit at P*D/2:       byte D*(t/4) + d, bits 2(t%4)+1..2(t%4)
@@ -450,6 +474,7 @@ static int valid_layout(const kvqo_layout* L) {
     case O_INT8_PTH:
     case O_FP8_PTH:
     case O_NVFP4:
+    case O_INT4_PTH:
       return D > 0 && D % 32 == 0 && D <= 4096 && P > 0 && P % 16 == 0;
     case O_KVARN_K4V2_G128:
       return D == 128 && P == 128;
@@ -469,6 +494,7 @@ int64_t kvqo_chunk_bytes(const kvqo_layout* L) {
     case O_FP8_PER_TENSOR: return 2 * P * D;
     case O_INT8_PTH:
     case O_FP8_PTH: return 2 * P * D + 2 * 4 * P;
+    case O_INT4_PTH: return 2 * (P * D / 2) + 2 * 4 * P;
     case O_NVFP4: return 2 * (P * D / 2) + 2 * (P * D / 16);
     case O_KVARN_K4V2_G128: return P * D / 2 + P * D / 4 + 4 * (3 * D + 3 * P);
   }
@@ -531,8 +557,22 @@ static void store_row(const kvqo_layout* L, uint8_t* ch, int t, const float* xk,
       quant_row_nvfp4(xv, D, L->v_scale, f, cv, bv);
       break;
     }
+    case O_INT4_PTH:
+      quant_row_int4(xk, D, ck, &sk);
+      quant_row_int4(xv, D, cv, &sv);
+      break;
   }
-  if (L->format == O_NVFP4) {
+  if (L->format == O_INT4_PTH) {
+    uint8_t* kc = ch;
+    uint8_t* vc = ch + (int64_t)P * D / 2;
+    float* ksc = (float*)(ch + (int64_t)P * D);
+    for (int d = 0; d < D; d++) {
+      put_nibble(kc + (int64_t)t * D / 2 + d / 2, d % 2, ck[d]);
+      put_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 4, d % 2, cv[d]);
+    }
+    ksc[t] = sk;
+    ksc[P + t] = sv;
+  } else if (L->format == O_NVFP4) {
     uint8_t* kc = ch;
     uint8_t* vc = ch + (int64_t)P * D / 2;
     uint8_t* ks = ch + (int64_t)P * D;
@@ -611,6 +651,21 @@ static void load_row(const kvqo_layout* L, const uint8_t* ch, int t, double* k, 
         /* x_hat = s_t * s_b * q, [P5] §双层缩放怎样恢复动态范围 */
         k[d] = (double)L->k_scale * sbk * kvqo_e2m1_decode(a);
         v[d] = (double)L->v_scale * sbv * kvqo_e2m1_decode(b);
+      }
+      break;
+    }
+    case O_INT4_PTH: {
+      const uint8_t* kc = ch;
+      const uint8_t* vc = ch + (int64_t)P * D / 2;
+      float tmp[2];
+      memcpy(&tmp[0], ch + (int64_t)P * D + 4LL * t, 4);
+      memcpy(&tmp[1], ch + (int64_t)P * D + 4LL * (P + t), 4);
+      for (int d = 0; d < D; d++) {
+        int a = get_nibble(kc + (int64_t)t * D / 2 + d / 2, d % 2);
+        int b = get_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 4, d % 2);
+        /* two's-complement nibble -> -8..7 */
+        k[d] = (double)((a ^ 8) - 8) * (double)tmp[0];
+        v[d] = (double)((b ^ 8) - 8) * (double)tmp[1];
       }
       break;
     }

@@ -183,6 +183,50 @@ def pin_int8_pth(O, rng=None):
             assert abs(q[i]) == 127
 
 
+def pin_int4_pth(O, rng=None):
+    """INT4 per-token-head (reading: the INT8 rule at 4 bits): brute-force
+    nearest code in [-7, 7] with ties to even, the half-step bound, the top
+    code, and the cache round trip through the signed nibbles."""
+    rng = rng or np.random.default_rng(12)
+    for D in (32, 128):
+        for x16 in _rows(rng, D):
+            codes, sb = O.quantize_row(oracle.INT4_PTH, x16)
+            assert np.all(codes < 16)
+            q = ((codes.astype(np.int64) ^ 8) - 8)  # two's-complement nibble
+            s = sb[:4].view(np.float32)[0]
+            x = x16.astype(np.float64)
+            assert np.isfinite(s) and s > 0
+            assert s == F32(max(F32(np.abs(x16.astype(np.float32)).max()), F32(1e-8))) / F32(7)
+            assert np.all(np.abs(q) <= 7)
+            if not np.any(x):
+                assert not np.any(q)
+                continue
+            y = (x16.astype(np.float32) / F32(s)).astype(np.float64)
+            cand = np.arange(-7, 8)
+            dist = np.abs(y[:, None] - cand[None, :])
+            best = dist.min(axis=1, keepdims=True)
+            tie_ok = (dist == best) & (cand[None, :] % 2 == 0)
+            single = (dist == best).sum(axis=1) == 1
+            brute = np.where(single, cand[np.argmin(dist, axis=1)], cand[np.argmax(tie_ok, axis=1)])
+            assert np.array_equal(q, brute)
+            assert np.all(np.abs(x - float(s) * q) <= float(s) * (0.5 + 2.0 ** -17))
+            assert abs(q[np.argmax(np.abs(x))]) == 7
+    # round trip through the paged cache: x_hat = q * s with the signed codes
+    D, P, H = 64, 16, 2
+    k = workloads.random_halves(rng, (20, H, D))
+    v = workloads.random_halves(rng, (20, H, D), 3.0)
+    slots = rng.choice(3 * P, 20, replace=False).astype(np.int64)
+    lay = oracle.layout(oracle.INT4_PTH, H, D, P, 3)
+    cache = O.quantize_write(lay, k, v, slots)
+    kh, vh = O.dequantize(lay, cache, slots)
+    for src, got in ((k, kh), (v, vh)):
+        for i in range(20):
+            for h in range(H):
+                codes, sb = O.quantize_row(oracle.INT4_PTH, src[i, h])
+                q = ((codes.astype(np.int64) ^ 8) - 8)
+                assert np.array_equal(got[i, h], q * float(sb[:4].view(np.float32)[0]))
+
+
 def pin_fp8_pth(O, rng=None):
     rng = rng or np.random.default_rng(4)
     for D in (32, 128):
@@ -293,6 +337,9 @@ def pin_page_bytes(O):
         assert O.chunk_bytes(lay) == P * 2 * D
         lay = oracle.layout(oracle.NVFP4, 8, D, P, 4)
         assert O.chunk_bytes(lay) == P * 2 * (D // 2 + D // 16)
+        div = int(g["int4_head_size_divisor"][0][0])
+        lay = oracle.layout(oracle.INT4_PTH, 8, D, P, 4)
+        assert O.chunk_bytes(lay) == P * ((D // div + D // div) * 1 + 2 * sb)
     # NVFP4: 4.5 bits per value from the 16-value micro-block
     nb = golden("nvfp4_bits.txt")
     lay = oracle.layout(oracle.NVFP4, 1, 128, 16, 1)
@@ -349,7 +396,7 @@ def pin_layout_bijective(O, rng=None):
     """Every token-head row owns its own nibbles; a full page covers the chunk
     exactly once."""
     rng = rng or np.random.default_rng(7)
-    for fmt in (oracle.INT8_PTH, oracle.FP8_PTH, oracle.FP8_PER_TENSOR, oracle.NVFP4):
+    for fmt in (oracle.INT8_PTH, oracle.FP8_PTH, oracle.FP8_PER_TENSOR, oracle.NVFP4, oracle.INT4_PTH):
         D, P, H = 64, 16, 2
         lay = oracle.layout(fmt, H, D, P, 2, 0.05, 0.05)
         k = workloads.random_halves(rng, (P, H, D))
@@ -548,7 +595,7 @@ def pin_attention_kvarn(O, rng=None):
 
 
 ALL_PINS = [
-    pin_half_widening, pin_e4m3_decode, pin_e4m3_encode, pin_e2m1_encode, pin_int8_pth, pin_fp8_pth,
+    pin_half_widening, pin_e4m3_decode, pin_e4m3_encode, pin_e2m1_encode, pin_int8_pth, pin_int4_pth, pin_fp8_pth,
     pin_fp8_pt, pin_nvfp4, pin_page_bytes, pin_glossary_bytes, pin_layout_bijective, pin_kvarn_rotation,
     pin_kvarn_tile, pin_attention, pin_attention_kvarn,
 ]

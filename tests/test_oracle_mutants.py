@@ -41,6 +41,12 @@ MUTANTS = [
      [pins.pin_glossary_bytes]),
     ("k8_offset_swizzle", "return 16LL * D * u + 64 * B * h + 16 * B * g + B * s + e;",
      "return 16LL * D * u + 64 * B * h + 16 * B * s + B * g + e;", 0, [pins.pin_layout_bijective]),
+    ("int4_k_nibble_order", "put_nibble(kc + (int64_t)t * D / 2 + d / 2, d % 2, ck[d]);",
+     "put_nibble(kc + (int64_t)t * D / 2 + d / 2, 1 - d % 2, ck[d]);", 0, [pins.pin_int4_pth]),
+    ("int4_step_8", "float s = fmaxf(a, 1e-8f) / 7.0f;", "float s = fmaxf(a, 1e-8f) / 8.0f;", 0,
+     [pins.pin_int4_pth]),
+    ("int4_unsigned_decode", "k[d] = (double)((a ^ 8) - 8) * (double)tmp[0];", "k[d] = (double)a * (double)tmp[0];", 0,
+     [pins.pin_int4_pth]),
     ("chunk_head_major", "return (uint8_t*)cache + (page * L->num_kv_heads + h) * kvqo_chunk_bytes(L);",
      "return (uint8_t*)cache + ((int64_t)h * L->num_pages + page) * kvqo_chunk_bytes(L);", 0,
      [pins.pin_layout_bijective]),
