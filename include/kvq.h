@@ -39,6 +39,10 @@
  *     V codes  [P/4][D/2][4] at P*D/2    byte 2*D*(t/4) + 4*(d/2) + t%4
  *     K block scales E4M3 [P][D/16]  at P*D     byte t*D/16 + d/16
  *     V block scales E4M3 [D/16][P]  after them byte (d/16)*P + t
+ *   INT4 per-token-head (two's-complement nibbles, low nibble = even channel):
+ *     K codes  [P][D/2]     at 0         byte t*D/2 + d/2
+ *     V codes  [P/4][D/2][4] at P*D/2    byte 2*D*(t/4) + 4*(d/2) + t%4
+ *     K scales fp32 [P] at P*D, then V scales fp32 [P]
  *   KVarN k4v2 g128 (P = D = 128):
  *     K codes 4-bit [P][D/2] at 0        byte t*D/2 + d/2, low nibble = even d
  *     V codes 2-bit [P/4][D] at P*D/2    byte D*(t/4) + d, bits 2(t%4)+1..2(t%4)
@@ -46,7 +50,8 @@
  *     (rotated tile rebuilt as K = rho_t (alpha_d code + beta_d),
  *      V = gamma_d (alpha_t code + beta_t); see kvq_quantize_write)
  *   Codes: INT8 = two's-complement byte; FP8 = OCP E4M3 ("fn", max 448);
- *   NVFP4 = E2M1 nibble (sign bit 3) with E4M3 block scales.
+ *   NVFP4 = E2M1 nibble (sign bit 3) with E4M3 block scales; INT4 =
+ *   two's-complement nibble, -7..7.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -60,13 +65,15 @@ extern "C" {
 
 /* Storage formats.  Values 1..4 follow the mode numbering of vLLM's
  * KVQuantMode listed in [P1] §二 (NONE = 0 is not a cache format here);
- * 5 is KVarN's k4v2 g128 preset ([P2] §配置与部署). */
+ * 5 is KVarN's k4v2 g128 preset ([P2] §配置与部署); 6 is vLLM's
+ * int4_per_token_head mode ([P4] §scale 和数据放在一起). */
 typedef enum {
   KVQ_FP8_PER_TENSOR = 1,  /* [P1] §2.1, [P4] §FP8 per-tensor */
   KVQ_INT8_PTH = 2,        /* per-token-head INT8, [P3] §它改变缓存表示 */
   KVQ_FP8_PTH = 3,         /* per-token-head FP8, [P1] §2.2 */
   KVQ_NVFP4 = 4,           /* [P5] §双层缩放怎样恢复动态范围 */
-  KVQ_KVARN_K4V2_G128 = 5  /* [P2] §技术原理 */
+  KVQ_KVARN_K4V2_G128 = 5, /* [P2] §技术原理 */
+  KVQ_INT4_PTH = 6         /* per-token-head INT4, [P4] §scale 和数据放在一起 */
 } kvq_format;
 
 /* NVFP4 only: per block, keep the max/4 block scale instead of max/6 when its
@@ -126,6 +133,9 @@ kvq_status kvq_check_device(int hip_device);
  *                     -127, 127); s stored in-page ([P3] formula and script).
  *   FP8 per-token-head: s = max(max|x|, 1e-8) / 448, code = E4M3(x / s)
  *                     ([P1] §2.2 with FP8_MAX = 448).
+ *   INT4 per-token-head: s = max(max|x|, 1e-8) / 7, code = clip(rne(x / s),
+ *                     -7, 7), s stored in-page (the INT8 rule at 4 bits: the
+ *                     page lists the mode and its half-width layout only).
  *   NVFP4:            per 16 channels, s_b = E4M3((max|x| / 6) / s_t),
  *                     code = E2M1(x / (s_t * s_b)) (ties to even, saturating
  *                     at 6); a block whose s_b decodes to 0 stores zero codes.

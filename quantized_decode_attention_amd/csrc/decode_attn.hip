@@ -1,5 +1,5 @@
 // decode_attn.hip -- dequant-fused paged GQA decode attention for FP8
-// per-tensor, INT8 / FP8 per-token-head and NVFP4 caches (gfx950).
+// per-tensor, INT8 / FP8 / INT4 per-token-head and NVFP4 caches (gfx950).
 //
 // Computes O = softmax(q K^T * sm_scale) V for every (sequence, q head) with
 // the cache read through block tables ([P5] "NVFP4 KV Cache：Blackwell 上的
@@ -37,11 +37,21 @@ namespace {
 
 constexpr int kDepth = 2;  // 16-token units per wave: 1 in compute, kDepth-1 in flight
 
+// Formats with 4-bit codes in the nibble layout (NVFP4, INT4 per-token-head)
+// and formats with per-token-head fp32 scales.
+template <int FMT> constexpr bool kNibble = FMT == 4 || FMT == 6;
+template <int FMT> constexpr bool kPth = FMT == 2 || FMT == 3 || FMT == 6;
+
+// INT4 keys enter the QK product with their channels in the order
+// 0, 2, 4, 6, 1, 3, 5, 7 within each group of 8 (the byte permute unpack);
+// the query columns are permuted to match.
+__host__ __device__ constexpr int int4_slot_channel(int i) { return i < 4 ? 2 * i : 2 * (i - 4) + 1; }
+
 // Raw bytes of one 16-token unit for one lane, as loaded from the chunk.
 template <int FMT, int D>
 struct Raw {
-  static constexpr int KW = (FMT == 4) ? D / 32 : D / 16;  // dwords of K codes
-  static constexpr int VW = (FMT == 4) ? D / 32 : D / 16;  // dwords of V codes
+  static constexpr int KW = kNibble<FMT> ? D / 32 : D / 16;  // dwords of K codes
+  static constexpr int VW = kNibble<FMT> ? D / 32 : D / 16;  // dwords of V codes
   uint32_t k[KW];
   uint32_t v[VW];
   uint32_t ksc, vsc;  // NVFP4 block-scale bytes (K: this token's blocks; V: 4 tokens)
@@ -68,7 +78,7 @@ __device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom&
   constexpr int NV = D / 16;
   const int tk = sub * 16 + n;
   const int quad = sub * 4 + gq;
-  if constexpr (FMT != 4) {
+  if constexpr (!kNibble<FMT>) {
     // coalesced 8-bit layout: piece h of all 64 lanes is one contiguous run
     constexpr int B = DL < 16 ? DL : 16;
     const uint8_t* kp = chunk + (int64_t)16 * D * sub + 16 * B * gq + B * n;
@@ -83,20 +93,33 @@ __device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom&
     }
   } else {
     load_dwords<Raw<FMT, D>::KW>(chunk + (int64_t)tk * (D / 2) + (DL / 2) * gq, r.k);
-    const uint8_t* sp = chunk + g.k_scales + (int64_t)tk * (D / 16) + (DL * gq) / 16;
-    if constexpr (DL >= 32)
-      r.ksc = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp));
-    else
-      r.ksc = __builtin_nontemporal_load(sp);
     load_dwords<Raw<FMT, D>::VW>(chunk + g.v_codes + (int64_t)2 * D * quad + 4 * ((NV * n) / 2), r.v);
-    r.vsc = ld_nt(chunk + g.v_scales + (int64_t)((NV * n) / 16) * P + 4 * quad);
+    if constexpr (FMT == 4) {
+      const uint8_t* sp = chunk + g.k_scales + (int64_t)tk * (D / 16) + (DL * gq) / 16;
+      if constexpr (DL >= 32)
+        r.ksc = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp));
+      else
+        r.ksc = __builtin_nontemporal_load(sp);
+      r.vsc = ld_nt(chunk + g.v_scales + (int64_t)((NV * n) / 16) * P + 4 * quad);
+    } else {
+      r.ks = ld_nt_f4(chunk + g.k_scales + 4 * (sub * 16 + 4 * gq));
+      r.vs = ld_nt_f4(chunk + g.v_scales + 4 * (sub * 16 + 4 * gq));
+    }
   }
 }
 
 // K operand for QK MFMA kk: 8 channels (D/4)*gq + 8*kk .. +7 of token row n.
 template <int FMT, int D>
 __device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2_t ksc) {
-  if constexpr (FMT != 4) {
+  if constexpr (FMT == 6) {
+    // two's-complement nibble ^ 8 = code + 8; under the 0x64 exponent byte it
+    // reads 1032 + code, and subtracting 1032 is exact
+    const uint32_t w = r.k[kk] ^ 0x88888888u;
+    const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+    const half2_t k1032 = {(half_t)1032.0f, (half_t)1032.0f};
+    return cat(as_h2(perm(0x64646464u, x, 0x04010400u)) - k1032, as_h2(perm(0x64646464u, x, 0x04030402u)) - k1032,
+               as_h2(perm(0x64646464u, y, 0x04010400u)) - k1032, as_h2(perm(0x64646464u, y, 0x04030402u)) - k1032);
+  } else if constexpr (FMT != 4) {
     half2_t a, b, c, d;
     if constexpr (FMT == 2) {
       // biased: binary16 1152 + code; the bias is removed from the scores
@@ -125,7 +148,13 @@ __device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2
 template <int FMT, int D>
 __device__ __forceinline__ half4_t v_operand(const Raw<FMT, D>& r, int nn, half2_t s01, half2_t s23,
                                              const uint32_t (&pairs)[4]) {
-  if constexpr (FMT != 4) {
+  if constexpr (FMT == 6) {
+    // the channel's nibble of each of the 4 token bytes, as for the keys
+    const uint32_t w = r.v[nn / 2] ^ 0x88888888u;
+    const uint32_t x = (nn & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
+    const half2_t k1032 = {(half_t)1032.0f, (half_t)1032.0f};
+    return cat4(as_h2(perm(0x64646464u, x, 0x04010400u)) - k1032, as_h2(perm(0x64646464u, x, 0x04030402u)) - k1032);
+  } else if constexpr (FMT != 4) {
     half2_t a, b;
     if constexpr (FMT == 2) {
       i8x4_to_h(r.v[nn], a, b);
@@ -154,7 +183,7 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
                                              WaveState<D>& st) {
   constexpr int NK = D / 32;
   constexpr int NV = D / 16;
-  constexpr bool PTH = (FMT == 2 || FMT == 3);
+  constexpr bool PTH = kPth<FMT>;
 
   half2_t ksc01 = {0, 0}, ksc23 = {0, 0};
   if constexpr (FMT == 4) e4m3x4_to_h(r.ksc, ksc01, ksc23);
@@ -293,7 +322,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (n < G) {
     const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + n) * D + DL * gq;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qB[kk] = *reinterpret_cast<const half8_t*>(qp + 8 * kk);
+    for (int kk = 0; kk < NK; ++kk) {
+      const half8_t qv = *reinterpret_cast<const half8_t*>(qp + 8 * kk);
+      if constexpr (FMT == 6) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qB[kk][i] = qv[int4_slot_channel(i)];
+      } else {
+        qB[kk] = qv;
+      }
+    }
   } else {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) qB[kk] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
@@ -479,6 +516,7 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s) {
     case 2: e = launch_fmt<2>(a, s); break;
     case 3: e = launch_fmt<3>(a, s); break;
     case 4: e = launch_fmt<4>(a, s); break;
+    case 6: e = launch_fmt<6>(a, s); break;
   }
   if (e != hipSuccess || a.num_splits == 1) return e;
   const float post = (fmt == 1 || fmt == 4) ? a.v_scale : 1.0f;

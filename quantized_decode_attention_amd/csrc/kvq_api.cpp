@@ -25,6 +25,7 @@ kvq_status check_layout(const kvq_layout* L) {
     case KVQ_INT8_PTH:
     case KVQ_FP8_PTH:
     case KVQ_NVFP4:
+    case KVQ_INT4_PTH:
       if (L->head_dim != 32 && L->head_dim != 64 && L->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
       if (L->page_size < 16 || L->page_size > 256 || (L->page_size & (L->page_size - 1))) return KVQ_ERR_UNSUPPORTED;
       break;
@@ -57,6 +58,12 @@ ChunkGeom geometry(const kvq_layout* L) {
       g.k_scales = 2 * P * D;
       g.v_scales = 2 * P * D + 4 * P;
       g.chunk_bytes = 2 * P * D + 8 * P;
+      break;
+    case KVQ_INT4_PTH:
+      g.v_codes = P * D / 2;
+      g.k_scales = P * D;
+      g.v_scales = P * D + 4 * P;
+      g.chunk_bytes = P * D + 8 * P;
       break;
     case KVQ_NVFP4:
       g.v_codes = P * D / 2;

@@ -1,4 +1,4 @@
-// quant_write.hip -- quantise-on-write for FP8 per-tensor, INT8 / FP8
+// quant_write.hip -- quantise-on-write for FP8 per-tensor, INT8 / FP8 / INT4
 // per-token-head and NVFP4 (gfx950).
 //
 // Write path of [P5] "NVFP4 KV Cache：Blackwell 上的 4-bit 缓存量化",
@@ -9,8 +9,9 @@
 // Work mapping.  8-bit formats: one workgroup per (16 consecutive tokens, kv
 // head); a run of tokens that fills one aligned 16-token group of a page is
 // quantised by lanes of 16 values and written as contiguous 16-byte stores,
-// any other slot pattern row by row (D/8 lanes of 8 values).  NVFP4 uses the
-// same group / per-row split with one lane per 16-value block.
+// any other slot pattern row by row (D/8 lanes of 8 values).  The 4-bit
+// formats (NVFP4, INT4 per-token-head) use the same group / per-row split with
+// one lane per 16 values.
 // This file is built with -ffp-contract=off: every binary32 operation below
 // rounds exactly as written.
 #include "kvq_device.h"
@@ -283,9 +284,35 @@ __device__ __forceinline__ uint32_t nvfp4_encode_block(const float* x, float st,
   return sb;
 }
 
-// One token-head row by D/16 lanes (lane j: block j), any slot.
-template <int D>
-__device__ __forceinline__ void write_row_nvfp4(const WriteArgs& a, int64_t row, int j) {
+// INT4 per-token-head codes of one lane's 16 values: the INT8 rule at 4 bits,
+// s = max(max|x|, 1e-8) / 7 over the whole row (NB lanes), q = clip(rne(x /
+// s), -7, 7) as a two's-complement nibble.  byte[i] packs values 2i (low
+// nibble) and 2i+1.  Returns s.
+template <int NB>
+__device__ __forceinline__ float int4_encode_block(const float* x, uint32_t* byte) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float s = fmaxf(group_max<NB>(amax), 1e-8f) / 7.0f;
+  const Recip rc = make_recip(s);
+  uint32_t nib[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float q = fminf(fmaxf(__builtin_rintf(div_rn(x[i], s, rc)), -7.0f), 7.0f);
+    nib[i] = (uint32_t)(int32_t)q & 15u;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) byte[i] = nib[2 * i] | (nib[2 * i + 1] << 4);
+  return s;
+}
+
+// One token-head row of a 4-bit format (FMT 4 = NVFP4, 6 = INT4
+// per-token-head) by D/16 lanes (lane j: values 16j .. 16j+15), any slot.
+// Both share the code layout; NVFP4 stores an E4M3 scale per block, INT4 one
+// fp32 scale per row.
+template <int FMT, int D>
+__device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, int j) {
+  constexpr int NB = D / 16;
   RowCtx c;
   if (!row_ctx(a, row, c)) return;
   float x[16];
@@ -293,32 +320,41 @@ __device__ __forceinline__ void write_row_nvfp4(const WriteArgs& a, int64_t row,
   load_halves8(src, x);
   load_halves8(src + 8, x + 8);
   uint32_t byte[8];
-  const uint32_t sb = nvfp4_encode_block(x, c.side ? a.v_scale : a.k_scale, a.flags, byte);
+  uint32_t sb = 0;
+  float s = 0.0f;
+  if constexpr (FMT == 4)
+    sb = nvfp4_encode_block(x, c.side ? a.v_scale : a.k_scale, a.flags, byte);
+  else
+    s = int4_encode_block<NB>(x, byte);
   if (c.side == 0) {
     uint2 packed;
     packed.x = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
     packed.y = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
     *reinterpret_cast<uint2*>(c.chunk + (int64_t)c.t * (D / 2) + 8 * j) = packed;
-    c.chunk[a.geom.k_scales + (int64_t)c.t * (D / 16) + j] = (uint8_t)sb;
+    if constexpr (FMT == 4) c.chunk[a.geom.k_scales + (int64_t)c.t * NB + j] = (uint8_t)sb;
   } else {
     // V: byte (quad, channel pair, token) so that each byte belongs to one token
     uint8_t* vp = c.chunk + a.geom.v_codes + 2 * D * (c.t / 4) + 32 * j + (c.t % 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) vp[4 * i] = (uint8_t)byte[i];
-    c.chunk[a.geom.v_scales + (int64_t)j * a.P + c.t] = (uint8_t)sb;
+    if constexpr (FMT == 4) c.chunk[a.geom.v_scales + (int64_t)j * a.P + c.t] = (uint8_t)sb;
   }
+  if constexpr (FMT == 6)
+    if (j == 0) reinterpret_cast<float*>(c.chunk + a.geom.k_scales)[c.side * a.P + c.t] = s;
 }
 
 // One workgroup per (16 consecutive tokens, kv head), as for the 8-bit
-// formats: an aligned run is assembled in LDS (K codes, V codes, K block
-// scales: one contiguous run each; V block scales: D/16 runs of 16 bytes) and
-// written with 16-byte stores; other slot patterns go row by row.
-template <int D>
-__global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
+// formats: an aligned run is assembled in LDS (K codes and V codes: one
+// contiguous run each; NVFP4 K block scales: one run, V block scales: D/16
+// runs of 16 bytes; INT4: 16 fp32 scales per side) and written with 16-byte
+// stores; other slot patterns go row by row.
+template <int FMT, int D>
+__global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
   constexpr int NB = D / 16;         // blocks per row
   constexpr int CB = 16 * D / 2;     // code bytes of 16 tokens, one side
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][CB];
   __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][16 * NB];
+  __shared__ float s_rs[2][16];
   __shared__ int s_ok;
   __shared__ int64_t s_slot0;
   const int64_t g = blockIdx.x;
@@ -331,7 +367,7 @@ __global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
       const int rr = t / NB, side = rr / 16, i = rr % 16;
       const int64_t tok = 16 * g + i;
       if (tok >= a.n_tok) continue;
-      write_row_nvfp4<D>(a, (int64_t)side * a.n_tok * a.H + tok * a.H + h, t % NB);
+      write_row_4bit<FMT, D>(a, (int64_t)side * a.n_tok * a.H + tok * a.H + h, t % NB);
     }
     return;
   }
@@ -344,7 +380,13 @@ __global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
     load_halves8(src, x);
     load_halves8(src + 8, x + 8);
     uint32_t byte[8];
-    const uint32_t sb = nvfp4_encode_block(x, side ? a.v_scale : a.k_scale, a.flags, byte);
+    uint32_t sb = 0;
+    if constexpr (FMT == 4) {
+      sb = nvfp4_encode_block(x, side ? a.v_scale : a.k_scale, a.flags, byte);
+    } else {
+      const float s = int4_encode_block<NB>(x, byte);
+      if (q == 0) s_rs[side][sidx] = s;
+    }
     if (side == 0) {
       uint8_t* kp = s_codes[0] + sidx * (D / 2) + 8 * q;
 #pragma unroll
@@ -366,13 +408,19 @@ __global__ __launch_bounds__(kBlock) void quant_write_nvfp4(WriteArgs a) {
     uint8_t* base = chunk + (sd ? a.geom.v_codes : 0) + (int64_t)t0 * (D / 2);
     *reinterpret_cast<uint4*>(base + o) = *reinterpret_cast<const uint4*>(&s_codes[sd][o]);
   }
-  // K block scales: 16 * NB contiguous bytes; V block scales: NB runs of 16
-  if (tid < NB)
-    *reinterpret_cast<uint4*>(chunk + a.geom.k_scales + (int64_t)t0 * NB + 16 * tid) =
-        *reinterpret_cast<const uint4*>(&s_sc[0][16 * tid]);
-  else if (tid < 2 * NB)
-    *reinterpret_cast<uint4*>(chunk + a.geom.v_scales + (int64_t)(tid - NB) * a.P + t0) =
-        *reinterpret_cast<const uint4*>(&s_sc[1][16 * (tid - NB)]);
+  if constexpr (FMT == 4) {
+    // K block scales: 16 * NB contiguous bytes; V block scales: NB runs of 16
+    if (tid < NB)
+      *reinterpret_cast<uint4*>(chunk + a.geom.k_scales + (int64_t)t0 * NB + 16 * tid) =
+          *reinterpret_cast<const uint4*>(&s_sc[0][16 * tid]);
+    else if (tid < 2 * NB)
+      *reinterpret_cast<uint4*>(chunk + a.geom.v_scales + (int64_t)(tid - NB) * a.P + t0) =
+          *reinterpret_cast<const uint4*>(&s_sc[1][16 * (tid - NB)]);
+  } else {
+    if (tid < 32)
+      reinterpret_cast<float*>(chunk + a.geom.k_scales)[(tid / 16) * a.P + t0 + (tid % 16)] =
+          s_rs[tid / 16][tid % 16];
+  }
 }
 
 template <int FMT>
@@ -381,11 +429,11 @@ hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
   const int64_t groups = (a.n_tok + 15) / 16;
   if (groups > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
   const dim3 g2((unsigned)groups, (unsigned)a.H);
-  if constexpr (FMT == 4) {
+  if constexpr (FMT == 4 || FMT == 6) {
     switch (a.D) {
-      case 32: quant_write_nvfp4<32><<<g2, kBlock, 0, s>>>(a); break;
-      case 64: quant_write_nvfp4<64><<<g2, kBlock, 0, s>>>(a); break;
-      case 128: quant_write_nvfp4<128><<<g2, kBlock, 0, s>>>(a); break;
+      case 32: quant_write_4bit<FMT, 32><<<g2, kBlock, 0, s>>>(a); break;
+      case 64: quant_write_4bit<FMT, 64><<<g2, kBlock, 0, s>>>(a); break;
+      case 128: quant_write_4bit<FMT, 128><<<g2, kBlock, 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -407,6 +455,7 @@ hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s) {
     case 2: return launch_fmt<2>(a, s);
     case 3: return launch_fmt<3>(a, s);
     case 4: return launch_fmt<4>(a, s);
+    case 6: return launch_fmt<6>(a, s);
   }
   return hipErrorInvalidValue;
 }

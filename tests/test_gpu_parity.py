@@ -13,8 +13,8 @@ from gpu_util import (assert_attn_close, dev, first_mismatch, gpu_decode, gpu_wr
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1)]
-FMT_IDS = ["fp8pt", "int8pth", "fp8pth", "nvfp4", "nvfp4_4over6"]
+FORMATS = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (6, 0)]
+FMT_IDS = ["fp8pt", "int8pth", "fp8pth", "nvfp4", "nvfp4_4over6", "int4pth"]
 
 
 def edge_rows(rng, n, H, D):
