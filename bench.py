@@ -75,6 +75,7 @@ class Problem:
         self.out = torch.empty((w.B, sp.Hq, sp.D), dtype=torch.float16, device="cuda")
         self.sm = 1.0 / math.sqrt(sp.D)
         self.K = K
+        self.kvarn = fmt == K.KVQ_KVARN_K4V2_G128
         torch.cuda.synchronize()
         log(f"[bench] {name} fmt={fmt} flags={flags}: inputs ready in {time.time() - t0:.1f}s, "
             f"cache {self.cache_bytes / 1e6:.1f} MB x {n} copies, {self.ws.num_splits} splits")
@@ -82,16 +83,58 @@ class Problem:
     def write_all(self, i):
         self.K.kvq_quantize_write(self.lay, self.k, self.v, self.slots, self.caches[i % len(self.caches)])
 
+    def prepare_incremental(self, n_steps):
+        """KVarN decode steps: contexts start n_steps tokens short of the full
+        length; step i appends one token per sequence through the binary16
+        tail (kvq_kvarn_append, completing a tile when it fills) and decodes
+        over the complete tiles plus the tail.  Every cache copy has its own
+        tail, prefilled with the tile that holds the first position, so each
+        copy stays consistent whichever steps it serves."""
+        import numpy as np
+        import torch
+        w, sp, P = self.w, self.sp, self.sp.P
+        n_steps = max(1, min(n_steps, w.T - 1))
+        c0 = w.T - n_steps
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        t0 = c0 // P * P  # first position of the tile holding c0
+        tail = np.zeros((w.B, 2, sp.Hkv, P, sp.D), np.float16)
+        for b in range(w.B):
+            rows = b * w.T + t0 + np.arange(P)
+            tail[b, 0] = w.k16[rows].transpose(1, 0, 2)
+            tail[b, 1] = w.v16[rows].transpose(1, 0, 2)
+        self.tails = [d(tail) for _ in self.caches]
+        pos = c0 + np.arange(n_steps)
+        rows = (np.arange(w.B)[None, :] * w.T + pos[:, None]).reshape(-1)
+        self.k_steps = d(w.k16[rows].reshape(n_steps, w.B, sp.Hkv, sp.D))
+        self.v_steps = d(w.v16[rows].reshape(n_steps, w.B, sp.Hkv, sp.D))
+        self.pos_steps = d(np.repeat(pos[:, None], w.B, axis=1).astype(np.int32))
+        self.ctx_steps = d(np.repeat(pos[:, None] + 1, w.B, axis=1).astype(np.int32))
+        self.seq = d(np.arange(w.B, dtype=np.int32))
+        ctx = pos + 1
+        tile_bytes = (ctx // P) * self.page_bytes
+        tail_bytes = (ctx % P) * sp.Hkv * 2 * sp.D * 2
+        self.step_kv_bytes = w.B * (tile_bytes + tail_bytes)  # per step: pages + binary16 tail
+        self.n_inc = n_steps
+        self.step_no = 0
+
     def append(self, i):
-        # KVarN quantises whole 128-token tiles; a new token waits in the
-        # caller's binary16 tail, so its step is the decode alone
-        if self.fmt == self.K.KVQ_KVARN_K4V2_G128:
+        c = self.caches[i % len(self.caches)]
+        if self.kvarn:
+            j = self.step_no
+            self.K.kvq_kvarn_append(self.lay, self.k_steps[j], self.v_steps[j], self.seq, self.pos_steps[j],
+                                    self.tails[i % len(self.caches)], self.bt, c)
             return
-        self.K.kvq_quantize_write(self.lay, self.k_new, self.v_new, self.slots_new, self.caches[i % len(self.caches)])
+        self.K.kvq_quantize_write(self.lay, self.k_new, self.v_new, self.slots_new, c)
 
     def decode(self, i):
-        self.K.kvq_decode_attention(self.lay, self.caches[i % len(self.caches)], self.q, self.bt, self.ctx, self.sm,
-                                    self.out, self.ws.buffer)
+        c = self.caches[i % len(self.caches)]
+        if self.kvarn:
+            j = self.step_no
+            self.K.kvq_decode_attention(self.lay, c, self.q, self.bt, self.ctx_steps[j], self.sm, self.out,
+                                        self.ws.buffer, self.tails[i % len(self.caches)])
+            self.step_no += 1
+            return
+        self.K.kvq_decode_attention(self.lay, c, self.q, self.bt, self.ctx, self.sm, self.out, self.ws.buffer)
 
     def time_write(self, reps=6):
         import torch
@@ -109,8 +152,12 @@ class Problem:
         return n_tok / (ms * 1e-3) / 1e6, ms
 
     def time_steps(self, steps, warmup):
-        """Timed decode steps; returns (ms per step, mean decode launch ms)."""
+        """Timed decode steps; returns (ms per step, mean decode launch ms).
+        The step index keeps counting across warm-up and timed steps."""
         import torch
+        if self.kvarn:
+            self.prepare_incremental(warmup + steps)
+            torch.cuda.synchronize()
         for i in range(warmup):
             self.append(i)
             self.decode(i)
@@ -119,13 +166,15 @@ class Problem:
         torch.cuda.synchronize()
         start.record()
         for i in range(steps):
-            self.append(i)
+            self.append(warmup + i)
             ev[i][0].record()
-            self.decode(i)
+            self.decode(warmup + i)
             ev[i][1].record()
         end.record()
         torch.cuda.synchronize()
         total = start.elapsed_time(end)
+        if self.kvarn:  # mean KV bytes (tiles + binary16 tail) of the timed steps
+            self.kv_bytes = int(self.step_kv_bytes[warmup:warmup + steps].mean())
         self.dec_ms = sorted(a.elapsed_time(b) for a, b in ev)
         return total / steps, sum(self.dec_ms) / len(self.dec_ms)
 
@@ -334,7 +383,8 @@ def main():
                          "decode_frac_of_peak": round(p.kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "decode_us": round(ms_d * 1e3, 2), "step_us": round(ms_s * 1e3, 2),
                          "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits,
-                         "step": "decode" if fmt == K.KVQ_KVARN_K4V2_G128 else "append + decode"}
+                         "step": ("append to the binary16 tail (tile quantised when complete) + decode over "
+                                  "tiles and tail" if fmt == K.KVQ_KVARN_K4V2_G128 else "append + decode")}
             log(f"[bench] {key}: {fmts[key]}")
             del p
             torch.cuda.empty_cache()

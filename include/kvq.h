@@ -157,6 +157,33 @@ kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const voi
                               const int64_t* slot_mapping, int64_t n_tok, void* cache,
                               void* stream);
 
+/* KVarN incremental write ([P2] §配置与部署: decode keeps the tokens of the
+ * incomplete last tile unquantised in a small fixed buffer; a tile is
+ * quantised once it is complete).  For decode steps and short appends.
+ *   k, v          binary16 [n_tok][H][128], new tokens.
+ *   seq           int32 [n_tok]: the sequence of each token, in [0, batch).
+ *   pos           int32 [n_tok]: the token's position in its sequence (the
+ *                 sequence's length before this token).
+ *   tail          binary16 [batch][2][H][128][128], the same buffer
+ *                 kvq_decode_attention reads: token i is copied to row
+ *                 pos[i] % 128 of sequence seq[i] (keys, then values).
+ *   block_tables  int32 [batch][max_pages_per_seq] as for decode.
+ *   cache         the paged cache.
+ * A token at position 127 mod 128 completes its tile: rows 0..127 of the
+ * sequence's tail are then quantised into page
+ * block_tables[seq][pos / 128], with exactly the bytes kvq_quantize_write
+ * gives for those 128 tokens.  Within one call, the tokens of a sequence must
+ * lie in one tile and have distinct positions (a token of the next tile would
+ * overwrite a tail row before the tile is quantised); entries with a sequence
+ * outside [0, batch), a negative position or a page outside the pool are
+ * skipped.  Two launches on `stream` (copy, then tile completion).
+ * Errors: KVQ_ERR_INVALID_ARG for a non-KVarN layout, NULL pointers or
+ * negative sizes; KVQ_ERR_DEVICE off gfx950. */
+kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void* v, const int32_t* seq,
+                            const int32_t* pos, int64_t n_tok, void* tail, int32_t batch,
+                            const int32_t* block_tables, int32_t max_pages_per_seq, void* cache,
+                            void* stream);
+
 /* Bytes of workspace kvq_decode_attention needs for this problem (host-only;
  * -1 if invalid): one partial record of binary32 (max, sum, output row) per
  * (sequence, kv head, context split), 0 when a single split is used.

@@ -68,6 +68,7 @@ def _load():
         "kvq_decode_num_splits": (I32, [LP, I32, I32, I32]),
         "kvq_decode_attention": (ctypes.c_int, [LP, P, P, I32, P, I32, P, I32, F32, P, P, P, I64, I32, P]),
         "kvq_dequantize": (ctypes.c_int, [LP, P, P, I64, P, P, P]),
+        "kvq_kvarn_append": (ctypes.c_int, [LP, P, P, P, P, I64, P, I32, P, I32, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sigs.items():
@@ -158,6 +159,17 @@ def kvq_decode_attention(lay: KvqLayout, cache, q, block_tables, context_lens, s
         _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
         0 if workspace is None else workspace.numel(), num_splits, _stream(stream)),
         "kvq_decode_attention")
+
+
+def kvq_kvarn_append(lay: KvqLayout, k, v, seq, pos, tail, block_tables, cache, stream=None):
+    """k, v: float16 [n, H, 128]; seq, pos: int32 [n]; tail: float16 [B, 2, H, 128, 128];
+    block_tables: int32 [B, max_pages]; cache: uint8."""
+    import torch
+    _check(_lib.kvq_kvarn_append(
+        ctypes.byref(lay), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
+        _ptr(seq, torch.int32, "seq"), _ptr(pos, torch.int32, "pos"), seq.shape[0],
+        _ptr(tail, torch.float16, "tail"), tail.shape[0], _ptr(block_tables, torch.int32, "block_tables"),
+        block_tables.shape[1], _ptr(cache, torch.uint8, "cache"), _stream(stream)), "kvq_kvarn_append")
 
 
 def kvq_dequantize(lay: KvqLayout, cache, slot_mapping, k_out, v_out, stream=None):

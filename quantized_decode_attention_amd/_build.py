@@ -1,5 +1,9 @@
 """Build libkvq.so in-tree with hipcc for gfx950.
 
+Run as a script (python quantized_decode_attention_amd/_build.py) or load it by
+path (load_build_module()): importing it through the package would first load
+the library being rebuilt.
+
 Every HIP source is compiled with packed-FP32 instruction selection disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops); the quantisation sources
 also with -ffp-contract=off so binary32 arithmetic rounds exactly as written.

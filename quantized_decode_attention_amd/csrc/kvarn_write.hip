@@ -123,17 +123,13 @@ __device__ __forceinline__ float quantise_group(const float (&y)[N], uint8_t* co
   return s;
 }
 
-__global__ __launch_bounds__(128) void kvarn_write_kernel(WriteArgs a) {
-  __shared__ float tile[N * LDP];
+// One tile-head side, by the 128 threads of a workgroup: token rows at
+// src + t * row_stride (binary16), codes and metadata into chunk.  `tile` is
+// the workgroup's LDS.
+__device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stride, uint8_t* chunk, int side,
+                                           float* tile) {
   uint8_t* cb = reinterpret_cast<uint8_t*>(tile);  // codes [token][channel], after the last pass
-
-  const int ti = blockIdx.x, h = blockIdx.y, side = blockIdx.z, t = threadIdx.x;
-  // only the first slot of a tile is read: the tile fills that page in order
-  const int64_t s0 = a.slots[(int64_t)ti * N];
-  if (s0 < 0 || s0 >= (int64_t)a.num_pages * N) return;
-  uint8_t* chunk = a.cache + ((s0 / N) * a.H + h) * a.geom.chunk_bytes;
-  const uint16_t* src = (side ? a.v : a.k) + ((int64_t)ti * N * a.H + h) * N;
-  const int64_t row_stride = (int64_t)a.H * N;
+  const int t = threadIdx.x;
 
   // stage 1: the tile, binary16 -> binary32 (exact), coalesced 16-byte loads
 #pragma unroll 4
@@ -225,6 +221,49 @@ __global__ __launch_bounds__(128) void kvarn_write_kernel(WriteArgs a) {
   }
 }
 
+__global__ __launch_bounds__(128) void kvarn_write_kernel(WriteArgs a) {
+  __shared__ float tile[N * LDP];
+  const int ti = blockIdx.x, h = blockIdx.y, side = blockIdx.z;
+  // only the first slot of a tile is read: the tile fills that page in order
+  const int64_t s0 = a.slots[(int64_t)ti * N];
+  if (s0 < 0 || s0 >= (int64_t)a.num_pages * N) return;
+  uint8_t* chunk = a.cache + ((s0 / N) * a.H + h) * a.geom.chunk_bytes;
+  const uint16_t* src = (side ? a.v : a.k) + ((int64_t)ti * N * a.H + h) * N;
+  kvarn_tile(src, (int64_t)a.H * N, chunk, side, tile);
+}
+
+// Incremental path ([P2] §配置与部署: the decode keeps the not yet quantised
+// tokens of the last tile in a small fixed buffer).  Append: token i goes to
+// row pos[i] % 128 of its sequence's binary16 tail.
+__global__ __launch_bounds__(64) void kvarn_append_kernel(KvarnAppendArgs a) {
+  const int64_t i = blockIdx.x;  // token
+  const int hs = blockIdx.y;     // head * 2 + side
+  const int h = hs >> 1, side = hs & 1;
+  const int b = a.seq[i], pos = a.pos[i];
+  if (b < 0 || b >= a.batch || pos < 0) return;
+  const uint16_t* src = (side ? a.v : a.k) + (i * a.H + h) * N;
+  uint16_t* dst = a.tail + ((((int64_t)b * 2 + side) * a.H + h) * N + (pos & (N - 1))) * N;
+  if (threadIdx.x < N / 8)
+    reinterpret_cast<uint4*>(dst)[threadIdx.x] = reinterpret_cast<const uint4*>(src)[threadIdx.x];
+}
+
+// Tile completion: a token at position 127 mod 128 completes its sequence's
+// tile, which is quantised from the tail into the page of that tile.
+__global__ __launch_bounds__(128) void kvarn_complete_kernel(KvarnAppendArgs a) {
+  __shared__ float tile[N * LDP];
+  const int64_t i = blockIdx.x;
+  const int h = blockIdx.y, side = blockIdx.z;
+  const int b = a.seq[i], pos = a.pos[i];
+  if (b < 0 || b >= a.batch || pos < 0 || (pos & (N - 1)) != N - 1) return;
+  const int pi = pos / N;
+  if (pi >= a.max_pages) return;
+  const int page = a.block_tables[(int64_t)b * a.max_pages + pi];
+  if (page < 0 || page >= a.num_pages) return;
+  uint8_t* chunk = a.cache + ((int64_t)page * a.H + h) * a.chunk_bytes;
+  const uint16_t* src = a.tail + (((int64_t)b * 2 + side) * a.H + h) * N * N;
+  kvarn_tile(src, N, chunk, side, tile);
+}
+
 }  // namespace
 
 hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s) {
@@ -232,6 +271,16 @@ hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
   kvarn_write_kernel<<<dim3((unsigned)tiles, (unsigned)a.H, 2u), 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kvarn_append(const KvarnAppendArgs& a, hipStream_t s) {
+  if (a.n_tok == 0) return hipSuccess;
+  if (a.n_tok > 0x7FFFFFFF || a.H > 32767) return hipErrorInvalidValue;
+  kvarn_append_kernel<<<dim3((unsigned)a.n_tok, (unsigned)(2 * a.H)), 64, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  kvarn_complete_kernel<<<dim3((unsigned)a.n_tok, (unsigned)a.H, 2u), 128, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -175,6 +175,33 @@ kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const voi
   return from_hip(launch_quant_write(layout->format, a, s));
 }
 
+kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void* v, const int32_t* seq,
+                            const int32_t* pos, int64_t n_tok, void* tail, int32_t batch, const int32_t* block_tables,
+                            int32_t max_pages_per_seq, void* cache, void* stream) {
+  kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
+  if (n_tok < 0 || batch < 0 || max_pages_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+  if (n_tok > 0 && (!k || !v || !seq || !pos || !tail || !block_tables || !cache)) return KVQ_ERR_INVALID_ARG;
+  if ((st = current_device_ok()) != KVQ_OK) return st;
+  if (n_tok == 0 || batch == 0) return KVQ_OK;
+  KvarnAppendArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.seq = seq;
+  a.pos = pos;
+  a.n_tok = n_tok;
+  a.tail = static_cast<uint16_t*>(tail);
+  a.batch = batch;
+  a.block_tables = block_tables;
+  a.max_pages = max_pages_per_seq;
+  a.cache = static_cast<uint8_t*>(cache);
+  a.chunk_bytes = geometry(layout).chunk_bytes;
+  a.H = layout->num_kv_heads;
+  a.num_pages = layout->num_pages;
+  return from_hip(launch_kvarn_append(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t max_pages_per_seq,
                               int32_t num_splits) {
   if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0) return -1;

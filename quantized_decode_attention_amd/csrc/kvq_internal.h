@@ -54,7 +54,24 @@ constexpr int kMaxSplits = 256; // context splits per (sequence, kv head)
 
 __host__ __device__ inline int64_t ws_record_floats(int D) { return 2 * kMaxGroup + (int64_t)kMaxGroup * D; }
 
+// KVarN incremental append (tail rows and tile completion).
+struct KvarnAppendArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seq;
+  const int32_t* pos;
+  int64_t n_tok;
+  uint16_t* tail;  // [batch][2][H][128][128] binary16
+  int batch;
+  const int32_t* block_tables;
+  int max_pages;
+  uint8_t* cache;
+  int64_t chunk_bytes;
+  int H, num_pages;
+};
+
 hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s);
+hipError_t launch_kvarn_append(const KvarnAppendArgs& a, hipStream_t s);
 hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s);
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s);

@@ -26,7 +26,11 @@ def K():
     """The product library; built in-tree first if nothing is built yet."""
     lib = os.path.join(ROOT, "quantized_decode_attention_amd", "libkvq.so")
     if not os.path.exists(lib):
-        from quantized_decode_attention_amd import _build
+        import importlib.util
+        path = os.path.join(ROOT, "quantized_decode_attention_amd", "_build.py")
+        spec = importlib.util.spec_from_file_location("kvq_build", path)
+        _build = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(_build)
         _build.build()
     import quantized_decode_attention_amd as K
     return K

@@ -212,3 +212,67 @@ def test_kvarn_decode_invalid_pages(K, O):
     log("kvarn decode invalid pages")
     got, _ = gpu_decode(K, lay, dev(cache), q16, bad, ctx, 0.1, tail16=tail, num_splits=2)
     assert np.all(np.isfinite(got))
+
+
+def test_kvarn_incremental_append_matches_oracle(K, O):
+    """Tokens appended step by step (a 50-token chunk, then one token per
+    sequence per call) give the same pages as one whole-tile write, the tail
+    holds the raw tokens of the incomplete tile, and decode over pages + tail
+    matches the oracle."""
+    import torch
+    rng = np.random.default_rng(560)
+    B, H, G = 3, 2, 4
+    ctx = np.array([128 + 5, 256, 3 * 128 - 1], np.int32)
+    bt, num_pages, slots, kq, vq, tail_ref = kvarn_problem(rng, B, H, ctx)
+    # every token of every sequence, sequence-major, as kvarn_problem drew them
+    T = int(ctx.sum())
+    rng2 = np.random.default_rng(561)
+    k_all = workloads.random_halves(rng2, (T, H, D))
+    v_all = workloads.random_halves(rng2, (T, H, D))
+    starts = np.concatenate([[0], np.cumsum(ctx)[:-1]])
+    full_slots, full_rows = [], []
+    tail_ref = np.zeros((B, 2, H, P, D), np.float16)
+    for b in range(B):
+        n_full = int(ctx[b]) // P
+        for t in range(n_full):
+            full_slots.append(bt[b, t].astype(np.int64) * P + np.arange(P))
+            full_rows.append(starts[b] + t * P + np.arange(P))
+        nt = int(ctx[b]) - n_full * P
+        tail_ref[b, 0, :, :nt] = k_all[starts[b] + n_full * P: starts[b] + ctx[b]].transpose(1, 0, 2)
+        tail_ref[b, 1, :, :nt] = v_all[starts[b] + n_full * P: starts[b] + ctx[b]].transpose(1, 0, 2)
+    full_slots = np.concatenate(full_slots)
+    full_rows = np.concatenate(full_rows)
+    lay = K.layout(5, H, D, P, num_pages)
+    ref_cache = O.quantize_write(olayout(lay), k_all[full_rows], v_all[full_rows], full_slots)
+
+    cache = torch.zeros(num_pages * K.kvq_page_bytes(lay), dtype=torch.uint8, device="cuda")
+    tail = torch.zeros((B, 2, H, P, D), dtype=torch.float16, device="cuda")
+    kd, vd, btd = dev(k_all), dev(v_all), dev(bt)
+
+    def append(pairs):
+        rows = np.array([starts[b] + p for b, p in pairs], np.int64)
+        K.kvq_kvarn_append(lay, kd[dev(rows)], vd[dev(rows)], dev(np.array([b for b, _ in pairs], np.int32)),
+                           dev(np.array([p for _, p in pairs], np.int32)), tail, btd, cache)
+
+    log("kvarn incremental append")
+    append([(b, p) for b in range(B) for p in range(50)])  # a chunk within the first tile
+    for p in range(50, int(ctx.max())):
+        append([(b, p) for b in range(B) if p < ctx[b]])
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    pb = K.kvq_page_bytes(lay)
+    for b in range(B):
+        for t in range(int(ctx[b]) // P):
+            pg = int(bt[b, t])
+            assert np.array_equal(got[pg * pb:(pg + 1) * pb], ref_cache[pg * pb:(pg + 1) * pb]), (b, t)
+    gt = tail.cpu().numpy()
+    for b in range(B):
+        nt = int(ctx[b]) % P
+        assert np.array_equal(gt[b, :, :, :nt].view(np.uint16), tail_ref[b, :, :, :nt].view(np.uint16)), b
+    q16 = workloads.random_halves(rng, (B, H * G, D))
+    ref = O.decode_attention(olayout(lay), ref_cache, q16, bt, ctx, 0.088, tail16=tail_ref)
+    out = torch.empty((B, H * G, D), dtype=torch.float16, device="cuda")
+    ws = K.DecodeWorkspace(lay, B, H * G, bt.shape[1])
+    K.kvq_decode_attention(lay, cache, dev(q16), btd, dev(ctx), 0.088, out, ws.buffer, tail)
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy().astype(np.float64), ref)
