@@ -487,8 +487,18 @@ __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
     const float e = t < n_tail ? exp2f(lg - mt) : 0.0f;
     e_tail[t] = e;
     const float lt = block_sum(e, red);  // its barriers also publish e_tail
+    // eight independent row loads per iteration (rows below 128 are in the
+    // buffer; rows at or past the tail length carry no weight)
     const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P) * D + t;
-    for (int j = 0; j < n_tail; ++j) ot += e_tail[j] * (float)__builtin_bit_cast(half_t, vt[(int64_t)j * D]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < n_tail; j0 += 8) {
+      half_t vv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) vv[u] = __builtin_bit_cast(half_t, vt[(int64_t)(j0 + u) * D]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += (j0 + u < n_tail) ? e_tail[j0 + u] * (float)vv[u] : 0.0f;
+    }
+    ot = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     const float mx = fmaxf(M, mt);
     const float sp = exp2f(M - mx), st = exp2f(mt - mx);
     L = L * sp + lt * st;
