@@ -224,3 +224,34 @@ def test_workspace_reuse_many_calls(K, O):
                                splits)
         torch.cuda.synchronize()
         assert_attn_close(out.cpu().numpy().astype(np.float64), ref[:nb], f"call {it}")
+
+
+@pytest.mark.parametrize("fmt,flags", [(2, 0), (4, 1), (6, 0)], ids=["int8pth", "nvfp4_4over6", "int4pth"])
+def test_decode_long_splits_and_limits(K, O, fmt, flags):
+    """One split walking more than 256 pages (several block-table chunks in
+    LDS), the largest page size, the maximum split count, and a batch whose
+    sequences mix empty, one-page and long contexts."""
+    rng = np.random.default_rng(4000 + fmt + flags)
+    H, G, D = 2, 8, 128
+    for P, ctx in ((16, [16 * 600 + 7, 0, 16, 5000]), (256, [256 * 3 + 1, 255, 256 * 9])):
+        ctx = np.array(ctx, np.int32)
+        B = ctx.size
+        bt, num_pages, slots = paged_problem(rng, B, H, G, D, P, ctx)
+        n = slots.shape[0]
+        k16 = workloads.random_halves(rng, (n, H, D))
+        v16 = workloads.random_halves(rng, (n, H, D))
+        lay = layout_for(K, fmt, flags, H, D, P, num_pages, k16, v16)
+        cache = O.quantize_write(olayout(lay), k16, v16, slots)
+        q16 = workloads.random_halves(rng, (B, H * G, D))
+        sm = 1.0 / math.sqrt(D)
+        pairs = np.array([(b, h) for b in range(B) for h in (0, 5, H * G - 1)], np.int32)
+        ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, sm, pairs=pairs)
+        cdev = dev(cache)
+        for splits in (1, 256):
+            log(f"long decode fmt={fmt} P={P} splits={splits} max_pages={bt.shape[1]}")
+            got, ws = gpu_decode(K, lay, cdev, q16, bt, ctx, sm, num_splits=splits)
+            mp = bt.shape[1]
+            pps = -(-mp // min(splits, mp))  # pages per split; empty trailing splits are dropped
+            assert ws.num_splits == -(-mp // pps)
+            for (b, h), r in zip(pairs, ref):
+                assert_attn_close(got[b, h], r, f"P={P} splits={splits} b={b} h={h}")
