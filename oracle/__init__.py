@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
 
-FP8_PER_TENSOR, INT8_PTH, FP8_PTH, NVFP4, KVARN_K4V2_G128, INT4_PTH = 1, 2, 3, 4, 5, 6
+FP8_PER_TENSOR, INT8_PTH, FP8_PTH, NVFP4, KVARN_K4V2_G128, INT4_PTH, MXFP4 = 1, 2, 3, 4, 5, 6, 7
 FLAG_NVFP4_4OVER6 = 1
 
 

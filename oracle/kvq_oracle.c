@@ -45,7 +45,8 @@ enum {
   O_FP8_PTH = 3,         /* [P1] §2.2 pseudo-code */
   O_NVFP4 = 4,           /* [P1] §2.3; [P5] §双层缩放怎样恢复动态范围 */
   O_KVARN_K4V2_G128 = 5, /* [P2] §技术原理, §配置与部署 */
-  O_INT4_PTH = 6         /* [P4] §scale 和数据放在一起 (int4_per_token_head) */
+  O_INT4_PTH = 6,        /* [P4] §scale 和数据放在一起 (int4_per_token_head) */
+  O_MXFP4 = 7            /* [P5] §双层缩放怎样恢复动态范围 (the MXFP4 comparison) */
 };
 enum { O_FLAG_NVFP4_4OVER6 = 1 }; /* [P5] §用一组数直观看缩放的作用 */
 
@@ -265,10 +266,38 @@ static void quant_row_nvfp4(const float* x, int D, float st, int four_over_six,
   }
 }
 
+/* MXFP4.  [P5] §双层缩放怎样恢复动态范围 contrasts NVFP4 with MXFP4: blocks
+ * of 32 values sharing one E8M0 scale, a pure power of two, and E2M1
+ * elements.  The page gives no rule for choosing the scale; reading: the
+ * format's published definition (OCP Microscaling Formats v1.0, conversion
+ * of a block), i.e. X = 2^(floor(log2(max|x|)) - 2), 2 being the exponent of
+ * E2M1's largest power of two (4), and q_i = E2M1(x_i / X) with values above
+ * 6 saturated (the top binade of the block, [6, 8) * X, clips).  The scale
+ * byte is the biased exponent floor(log2(max|x|)) - 2 + 127.  A block whose
+ * values are all zero has no exponent; it takes the smallest scale, byte 0
+ * (any scale reconstructs zeros).  x_i / X is exact (a power of two). */
+static void quant_row_mxfp4(const float* x, int D, uint8_t* codes, uint8_t* bscales) {
+  for (int b = 0; b < D / 32; b++) {
+    const float* xb = x + 32 * b;
+    float a = 0.0f;
+    for (int i = 0; i < 32; i++) a = fmaxf(a, fabsf(xb[i]));
+    if (a == 0.0f) {
+      bscales[b] = 0;
+      for (int i = 0; i < 32; i++) codes[32 * b + i] = kvqo_e2m1_encode(xb[i]);
+      continue;
+    }
+    int ex;
+    frexpf(a, &ex); /* a = m * 2^ex, m in [0.5, 1): floor(log2(a)) = ex - 1 */
+    int k = (ex - 1) - 2;
+    bscales[b] = (uint8_t)(k + 127);
+    for (int i = 0; i < 32; i++) codes[32 * b + i] = kvqo_e2m1_encode(ldexpf(xb[i], -k));
+  }
+}
+
 /* Exported row quantiser for pins: x is D binary16 values; codes gets one
  * unpacked code per element (INT8 as a signed byte, E4M3 byte, or E2M1
- * nibble); scales gets the fp32 per-token-head scale (as 4 bytes) or the D/16
- * NVFP4 block-scale bytes.  scale is the per-tensor / global scale. */
+ * nibble); scales gets the fp32 per-token-head scale (as 4 bytes), the D/16
+ * NVFP4 block-scale bytes or the D/32 MXFP4 E8M0 bytes.  scale is the per-tensor / global scale. */
 int kvqo_quantize_row(int format, int flags, float scale, const uint16_t* x16, int D,
                       uint8_t* codes, uint8_t* scales) {
   if (D <= 0 || D % 32 != 0 || D > 4096) return O_BAD_ARG;
@@ -283,6 +312,7 @@ int kvqo_quantize_row(int format, int flags, float scale, const uint16_t* x16, i
     case O_NVFP4:
       quant_row_nvfp4(x, D, scale, flags & O_FLAG_NVFP4_4OVER6, codes, scales);
       return O_OK;
+    case O_MXFP4: quant_row_mxfp4(x, D, codes, scales); return O_OK;
   }
   return O_BAD_ARG;
 }
@@ -454,6 +484,9 @@ void kvqo_kvarn_tile(const uint16_t* x16, int64_t stride, int side, float* y_rot
  *                                            nibble d%2
  *    K block scales [P][D/16]  at P*D:       byte t*D/16 + d/16
  *    V block scales [D/16][P]  after:        byte (d/16)*P + t
+ *  MXFP4: the NVFP4 code layout, with E8M0 bytes per 32 channels
+ *    K block scales [P][D/32]  at P*D:       byte t*D/32 + d/32
+ *    V block scales [D/32][P]  after:        byte (d/32)*P + t
  *  INT4 per-token-head (two's-complement nibbles, low nibble first):
  *    K codes  [P][D/2]      at 0:            byte t*D/2 + d/2, nibble d%2
  *    V codes  [P/4][D/2][4] at P*D/2:        byte 2*D*(t/4) + 4*(d/2) + t%4,
@@ -475,6 +508,7 @@ static int valid_layout(const kvqo_layout* L) {
     case O_FP8_PTH:
     case O_NVFP4:
     case O_INT4_PTH:
+    case O_MXFP4:
       return D > 0 && D % 32 == 0 && D <= 4096 && P > 0 && P % 16 == 0;
     case O_KVARN_K4V2_G128:
       return D == 128 && P == 128;
@@ -496,6 +530,7 @@ int64_t kvqo_chunk_bytes(const kvqo_layout* L) {
     case O_FP8_PTH: return 2 * P * D + 2 * 4 * P;
     case O_INT4_PTH: return 2 * (P * D / 2) + 2 * 4 * P;
     case O_NVFP4: return 2 * (P * D / 2) + 2 * (P * D / 16);
+    case O_MXFP4: return 2 * (P * D / 2) + 2 * (P * D / 32);
     case O_KVARN_K4V2_G128: return P * D / 2 + P * D / 4 + 4 * (3 * D + 3 * P);
   }
   return -1;
@@ -561,6 +596,10 @@ static void store_row(const kvqo_layout* L, uint8_t* ch, int t, const float* xk,
       quant_row_int4(xk, D, ck, &sk);
       quant_row_int4(xv, D, cv, &sv);
       break;
+    case O_MXFP4:
+      quant_row_mxfp4(xk, D, ck, bk);
+      quant_row_mxfp4(xv, D, cv, bv);
+      break;
   }
   if (L->format == O_INT4_PTH) {
     uint8_t* kc = ch;
@@ -572,17 +611,18 @@ static void store_row(const kvqo_layout* L, uint8_t* ch, int t, const float* xk,
     }
     ksc[t] = sk;
     ksc[P + t] = sv;
-  } else if (L->format == O_NVFP4) {
+  } else if (L->format == O_NVFP4 || L->format == O_MXFP4) {
+    const int BL = L->format == O_NVFP4 ? 16 : 32; /* values per block scale */
     uint8_t* kc = ch;
     uint8_t* vc = ch + (int64_t)P * D / 2;
     uint8_t* ks = ch + (int64_t)P * D;
-    uint8_t* vs = ks + (int64_t)P * D / 16;
+    uint8_t* vs = ks + (int64_t)P * D / BL;
     for (int d = 0; d < D; d++) {
       put_nibble(kc + (int64_t)t * D / 2 + d / 2, d % 2, ck[d]);
       put_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 4, d % 2, cv[d]);
     }
-    for (int b = 0; b < D / 16; b++) {
-      ks[(int64_t)t * (D / 16) + b] = bk[b];
+    for (int b = 0; b < D / BL; b++) {
+      ks[(int64_t)t * (D / BL) + b] = bk[b];
       vs[(int64_t)b * P + t] = bv[b];
     }
   } else {
@@ -651,6 +691,20 @@ static void load_row(const kvqo_layout* L, const uint8_t* ch, int t, double* k, 
         /* x_hat = s_t * s_b * q, [P5] §双层缩放怎样恢复动态范围 */
         k[d] = (double)L->k_scale * sbk * kvqo_e2m1_decode(a);
         v[d] = (double)L->v_scale * sbv * kvqo_e2m1_decode(b);
+      }
+      break;
+    }
+    case O_MXFP4: {
+      const uint8_t* kc = ch;
+      const uint8_t* vc = ch + (int64_t)P * D / 2;
+      const uint8_t* ks = ch + (int64_t)P * D;
+      const uint8_t* vs = ks + (int64_t)P * D / 32;
+      for (int d = 0; d < D; d++) {
+        uint8_t a = get_nibble(kc + (int64_t)t * D / 2 + d / 2, d % 2);
+        uint8_t b = get_nibble(vc + 2LL * D * (t / 4) + 4 * (d / 2) + t % 4, d % 2);
+        /* x_hat = 2^(E - 127) * q, E the block's E8M0 byte */
+        k[d] = ldexp(kvqo_e2m1_decode(a), (int)ks[(int64_t)t * (D / 32) + d / 32] - 127);
+        v[d] = ldexp(kvqo_e2m1_decode(b), (int)vs[(int64_t)(d / 32) * P + t] - 127);
       }
       break;
     }

@@ -318,6 +318,87 @@ def pin_nvfp4(O, rng=None):
         assert np.array_equal(rec, x.astype(np.float64))
 
 
+def _pow2_exponent_brute(a):
+    """The integer k with 4 * 2^k <= a < 8 * 2^k, by search (a > 0)."""
+    hits = [k for k in range(-160, 140) if 4.0 * 2.0 ** k <= a < 8.0 * 2.0 ** k]
+    assert len(hits) == 1
+    return hits[0]
+
+
+def pin_mxfp4(O, rng=None):
+    """MXFP4 (reading: the OCP MX block conversion): per 32-value block the
+    power of two 2^k with 4 * 2^k <= max|x| < 8 * 2^k, found by search, the
+    biased E8M0 byte k + 127, brute-force E2M1 of x / 2^k with saturation at
+    6; hand-worked blocks; exact round trip of values already on the grid;
+    the cache round trip."""
+    rng = rng or np.random.default_rng(13)
+    rows = []
+    for D in (32, 128):
+        rows += _rows(rng, D)
+        rows.append(rng.standard_t(4, D).astype(np.float16))
+    for x16 in rows:
+        D = x16.shape[0]
+        codes, sb = O.quantize_row(oracle.MXFP4, x16)
+        x = x16.astype(np.float64)
+        for b in range(D // 32):
+            xb, cb = x[32 * b:32 * (b + 1)], codes[32 * b:32 * (b + 1)]
+            a = float(np.abs(xb).max())
+            if a == 0.0:
+                assert sb[b] == 0 and not np.any(cb & 7)
+                continue
+            k = _pow2_exponent_brute(a)
+            assert int(sb[b]) == k + 127
+            assert np.array_equal(cb, _e2m1_brute(xb / 2.0 ** k))
+            # only the top binade [6, 8) * 2^k can clip; the max never rounds to zero
+            assert cb[np.argmax(np.abs(xb))] & 7 >= 6
+    # hand-worked blocks (32 values: the listed ones, then zeros)
+    cases = [
+        ([6.0, 5.0, 0.25, -0.75], 127, [7, 6, 0, 8 | 2]),       # max 6: 2^0; ties go to the even code
+        ([7.0, -7.0, 1.25], 127, [7, 8 | 7, 2]),                # max 7: 2^0, 7 saturates to 6
+        ([8.0, 7.0, 3.0], 128, [6, 6, 3]),                      # max 8: 2^1; 7/2 = 3.5 ties 3|4 -> 4
+        ([0.75, 0.09375, -0.0], 124, [7, 2, 8]),                # max 0.75: 2^-3; 0.09375 * 8 = 0.75 ties 0.5|1
+        ([65504.0, 1.0], 140, [7, 0]),                          # max 65504: 2^13; 1 / 8192 -> 0
+        ([2.0 ** -24], 101, [6]),                               # smallest subnormal half: 2^-26, value 4
+    ]
+    for vals, byte, want in cases:
+        x16 = np.zeros(32, np.float16)
+        x16[:len(vals)] = vals
+        codes, sb = O.quantize_row(oracle.MXFP4, x16)
+        assert int(sb[0]) == byte, (vals, int(sb[0]))
+        assert list(codes[:len(vals)]) == want, (vals, list(codes[:len(vals)]))
+        assert not np.any(codes[len(vals):])
+    # values already on 2^k * grid with a block max of 4 or 6 (times 2^k) reproduce exactly
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    D, P, H = 128, 16, 2
+    k16 = np.zeros((P, H, D), np.float16)
+    v16 = np.zeros((P, H, D), np.float16)
+    for t in range(P):
+        for h in range(H):
+            for dst in (k16, v16):
+                e = rng.integers(-20, 12, D // 32)
+                vals = rng.choice(grid, D) * rng.choice([-1, 1], D)
+                vals[::32] = rng.choice([4.0, 6.0], D // 32)
+                dst[t, h] = (vals * np.repeat(2.0 ** e, 32)).astype(np.float16)
+                assert np.array_equal(dst[t, h].astype(np.float64), vals * np.repeat(2.0 ** e, 32))
+    lay = oracle.layout(oracle.MXFP4, H, D, P, 2)
+    slots = (P + rng.permutation(P)).astype(np.int64)
+    cache = O.quantize_write(lay, k16, v16, slots)
+    kh, vh = O.dequantize(lay, cache, slots)
+    assert np.array_equal(kh, k16.astype(np.float64)) and np.array_equal(vh, v16.astype(np.float64))
+    # cache round trip of random rows: x_hat = 2^(byte - 127) * e2m1(code)
+    k = workloads.random_halves(rng, (20, H, D))
+    v = workloads.random_halves(rng, (20, H, D), 3.0)
+    slots = rng.choice(2 * P, 20, replace=False).astype(np.int64)
+    cache = O.quantize_write(lay, k, v, slots)
+    kh, vh = O.dequantize(lay, cache, slots)
+    for src, got in ((k, kh), (v, vh)):
+        for i in range(20):
+            for h in range(H):
+                codes, sb = O.quantize_row(oracle.MXFP4, src[i, h])
+                vals = np.array([O.e2m1_decode(int(c)) for c in codes])
+                assert np.array_equal(got[i, h], vals * np.repeat(2.0 ** (sb[:D // 32].astype(np.int64) - 127), 32))
+
+
 # --------------------------------------------------------------------------- #
 # page layout
 # --------------------------------------------------------------------------- #
@@ -340,11 +421,21 @@ def pin_page_bytes(O):
         div = int(g["int4_head_size_divisor"][0][0])
         lay = oracle.layout(oracle.INT4_PTH, 8, D, P, 4)
         assert O.chunk_bytes(lay) == P * ((D // div + D // div) * 1 + 2 * sb)
+        # MXFP4: the NVFP4 code bytes with one E8M0 byte per 32 values
+        mx = golden("mxfp4_block.txt")
+        blk = int(mx["block_values"][0][0])
+        lay = oracle.layout(oracle.MXFP4, 8, D, P, 4)
+        assert O.chunk_bytes(lay) == P * 2 * (D // 2 + (D // blk) * int(mx["block_scale_bits"][0][0]) // 8)
+    # MXFP4 metadata is sparser than NVFP4's: 4.25 against 4.5 bits per value
+    lay = oracle.layout(oracle.MXFP4, 1, 128, 16, 1)
+    mx_bits = O.chunk_bytes(lay) * 8 / (2 * 16 * 128)
+    assert mx_bits == (int(mx["block_code_bits"][0][0]) + int(mx["block_scale_bits"][0][0])) / blk
     # NVFP4: 4.5 bits per value from the 16-value micro-block
     nb = golden("nvfp4_bits.txt")
     lay = oracle.layout(oracle.NVFP4, 1, 128, 16, 1)
     bits = O.chunk_bytes(lay) * 8 / (2 * 16 * 128)
     assert bits == float(nb["bits_per_value"][0][0])
+    assert mx_bits < bits
     assert round(16 / bits, 2) == float(nb["ratio_vs_bf16"][0][0])
     assert round(8 / bits, 2) == float(nb["ratio_vs_fp8"][0][0])
     # 4-bit per-token KV bytes are about 0.28 of FP16 at head size 128
@@ -396,7 +487,7 @@ def pin_layout_bijective(O, rng=None):
     """Every token-head row owns its own nibbles; a full page covers the chunk
     exactly once."""
     rng = rng or np.random.default_rng(7)
-    for fmt in (oracle.INT8_PTH, oracle.FP8_PTH, oracle.FP8_PER_TENSOR, oracle.NVFP4, oracle.INT4_PTH):
+    for fmt in (oracle.INT8_PTH, oracle.FP8_PTH, oracle.FP8_PER_TENSOR, oracle.NVFP4, oracle.INT4_PTH, oracle.MXFP4):
         D, P, H = 64, 16, 2
         lay = oracle.layout(fmt, H, D, P, 2, 0.05, 0.05)
         k = workloads.random_halves(rng, (P, H, D))
@@ -596,6 +687,6 @@ def pin_attention_kvarn(O, rng=None):
 
 ALL_PINS = [
     pin_half_widening, pin_e4m3_decode, pin_e4m3_encode, pin_e2m1_encode, pin_int8_pth, pin_int4_pth, pin_fp8_pth,
-    pin_fp8_pt, pin_nvfp4, pin_page_bytes, pin_glossary_bytes, pin_layout_bijective, pin_kvarn_rotation,
+    pin_fp8_pt, pin_nvfp4, pin_mxfp4, pin_page_bytes, pin_glossary_bytes, pin_layout_bijective, pin_kvarn_rotation,
     pin_kvarn_tile, pin_attention, pin_attention_kvarn,
 ]

@@ -47,6 +47,14 @@ MUTANTS = [
      [pins.pin_int4_pth]),
     ("int4_unsigned_decode", "k[d] = (double)((a ^ 8) - 8) * (double)tmp[0];", "k[d] = (double)a * (double)tmp[0];", 0,
      [pins.pin_int4_pth]),
+    ("mxfp4_emax_1", "int k = (ex - 1) - 2;", "int k = (ex - 1) - 1;", 0, [pins.pin_mxfp4]),
+    ("mxfp4_ceil_exponent", "int k = (ex - 1) - 2;", "int k = ex - 2;", 0, [pins.pin_mxfp4]),
+    ("mxfp4_unbiased_byte", "bscales[b] = (uint8_t)(k + 127);", "bscales[b] = (uint8_t)(k + 128);", 0,
+     [pins.pin_mxfp4]),
+    ("mxfp4_v_scale_token_major", "vs[(int64_t)b * P + t] = bv[b];", "vs[(int64_t)t * (D / BL) + b] = bv[b];", 0,
+     [pins.pin_mxfp4, pins.pin_layout_bijective]),
+    ("mxfp4_decode_scale_block_16", "(int)ks[(int64_t)t * (D / 32) + d / 32] - 127",
+     "(int)ks[(int64_t)t * (D / 32) + d / 16 % (D / 32)] - 127", 0, [pins.pin_mxfp4]),
     ("chunk_head_major", "return (uint8_t*)cache + (page * L->num_kv_heads + h) * kvqo_chunk_bytes(L);",
      "return (uint8_t*)cache + ((int64_t)h * L->num_pages + page) * kvqo_chunk_bytes(L);", 0,
      [pins.pin_layout_bijective]),
