@@ -371,7 +371,8 @@ def main():
         fmts = {}
         others = [("fp8_sink_4k", K.KVQ_FP8_PER_TENSOR, 0), ("fp8_sink_4k", K.KVQ_FP8_PTH, 0),
                   ("nvfp4_16k", K.KVQ_NVFP4, 0), ("nvfp4_16k", K.KVQ_NVFP4, K.KVQ_FLAG_NVFP4_4OVER6),
-                  ("kvarn_16k", K.KVQ_KVARN_K4V2_G128, 0), ("int8_32k", K.KVQ_INT4_PTH, 0)]
+                  ("nvfp4_16k", K.KVQ_MXFP4, 0), ("kvarn_16k", K.KVQ_KVARN_K4V2_G128, 0),
+                  ("int8_32k", K.KVQ_INT4_PTH, 0)]
         for name, fmt, flags in others:
             if name == args.workload and fmt == main_fmt[0] and flags == main_fmt[1]:
                 continue

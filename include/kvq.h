@@ -39,6 +39,9 @@
  *     V codes  [P/4][D/2][4] at P*D/2    byte 2*D*(t/4) + 4*(d/2) + t%4
  *     K block scales E4M3 [P][D/16]  at P*D     byte t*D/16 + d/16
  *     V block scales E4M3 [D/16][P]  after them byte (d/16)*P + t
+ *   MXFP4: the NVFP4 code layout, with E8M0 block scales per 32 channels
+ *     K block scales E8M0 [P][D/32]  at P*D     byte t*D/32 + d/32
+ *     V block scales E8M0 [D/32][P]  after them byte (d/32)*P + t
  *   INT4 per-token-head (two's-complement nibbles, low nibble = even channel):
  *     K codes  [P][D/2]     at 0         byte t*D/2 + d/2
  *     V codes  [P/4][D/2][4] at P*D/2    byte 2*D*(t/4) + 4*(d/2) + t%4
@@ -50,7 +53,8 @@
  *     (rotated tile rebuilt as K = rho_t (alpha_d code + beta_d),
  *      V = gamma_d (alpha_t code + beta_t); see kvq_quantize_write)
  *   Codes: INT8 = two's-complement byte; FP8 = OCP E4M3 ("fn", max 448);
- *   NVFP4 = E2M1 nibble (sign bit 3) with E4M3 block scales; INT4 =
+ *   NVFP4 = E2M1 nibble (sign bit 3) with E4M3 block scales; MXFP4 = E2M1
+ *   nibble with E8M0 block scales (byte e is 2^(e-127)); INT4 =
  *   two's-complement nibble, -7..7.
  */
 #ifndef KVQ_H
@@ -66,14 +70,16 @@ extern "C" {
 /* Storage formats.  Values 1..4 follow the mode numbering of vLLM's
  * KVQuantMode listed in [P1] §二 (NONE = 0 is not a cache format here);
  * 5 is KVarN's k4v2 g128 preset ([P2] §配置与部署); 6 is vLLM's
- * int4_per_token_head mode ([P4] §scale 和数据放在一起). */
+ * int4_per_token_head mode ([P4] §scale 和数据放在一起); 7 is MXFP4, the
+ * comparison point of [P5] §双层缩放怎样恢复动态范围. */
 typedef enum {
   KVQ_FP8_PER_TENSOR = 1,  /* [P1] §2.1, [P4] §FP8 per-tensor */
   KVQ_INT8_PTH = 2,        /* per-token-head INT8, [P3] §它改变缓存表示 */
   KVQ_FP8_PTH = 3,         /* per-token-head FP8, [P1] §2.2 */
   KVQ_NVFP4 = 4,           /* [P5] §双层缩放怎样恢复动态范围 */
   KVQ_KVARN_K4V2_G128 = 5, /* [P2] §技术原理 */
-  KVQ_INT4_PTH = 6         /* per-token-head INT4, [P4] §scale 和数据放在一起 */
+  KVQ_INT4_PTH = 6,        /* per-token-head INT4, [P4] §scale 和数据放在一起 */
+  KVQ_MXFP4 = 7            /* 32-value E2M1 blocks, E8M0 scale, [P5] §双层缩放怎样恢复动态范围 */
 } kvq_format;
 
 /* NVFP4 only: per block, keep the max/4 block scale instead of max/6 when its
@@ -141,6 +147,12 @@ kvq_status kvq_check_device(int hip_device);
  *                     at 6); a block whose s_b decodes to 0 stores zero codes.
  *                     With KVQ_FLAG_NVFP4_4OVER6 the max/4 candidate is kept
  *                     when its binary32 squared error is strictly smaller.
+ *   MXFP4:            per 32 channels, X = 2^(floor(log2 max|x|) - 2),
+ *                     code = E2M1(x / X) (exact division; ties to even,
+ *                     saturating at 6), scale byte floor(log2 max|x|) + 125;
+ *                     an all-zero block stores byte 0.  The page names only
+ *                     the block size and the E8M0 scale; the rule is the OCP
+ *                     Microscaling block conversion.  No per-layer scale.
  *   KVarN k4v2 g128:  per 128-token tile and kv head ([P2] §技术原理):
  *                     normalised Sylvester Walsh-Hadamard rotation of every
  *                     token row, 4 sweeps of alternating token / channel
@@ -236,7 +248,7 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
 /* Expand cached tokens back to binary32 [n_tok][H][D] for inspection and tests
  * (x_hat = s q, [P3] §它改变缓存表示).  8-bit formats: code value times scale,
  * one rounding.  NVFP4: E2M1 value times the E4M3 block scale (exact), times
- * s_t (one rounding).  KVarN: rebuilt in the rotated basis, then rotated back
+ * s_t (one rounding).  MXFP4: E2M1 value times 2^(e-127) (exact).  KVarN: rebuilt in the rotated basis, then rotated back
  * (binary32, a few ulps).  Skipped slots (as in kvq_quantize_write) leave their
  * rows untouched. */
 kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int64_t* slot_mapping,

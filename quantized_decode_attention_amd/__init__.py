@@ -25,10 +25,11 @@ KVQ_FP8_PTH = 3
 KVQ_NVFP4 = 4
 KVQ_KVARN_K4V2_G128 = 5
 KVQ_INT4_PTH = 6
+KVQ_MXFP4 = 7
 KVQ_FLAG_NVFP4_4OVER6 = 1
 
 FORMAT_NAMES = {1: "fp8_per_tensor", 2: "int8_per_token_head", 3: "fp8_per_token_head", 4: "nvfp4",
-                5: "kvarn_k4v2_g128", 6: "int4_per_token_head"}
+                5: "kvarn_k4v2_g128", 6: "int4_per_token_head", 7: "mxfp4"}
 
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "KVQ_ERR_WORKSPACE_TOO_SMALL",
           4: "KVQ_ERR_DEVICE", 5: "KVQ_ERR_HIP"}

@@ -1,5 +1,6 @@
 // decode_attn.hip -- dequant-fused paged GQA decode attention for FP8
-// per-tensor, INT8 / FP8 / INT4 per-token-head and NVFP4 caches (gfx950).
+// per-tensor, INT8 / FP8 / INT4 per-token-head, NVFP4 and MXFP4 caches
+// (gfx950).
 //
 // Computes O = softmax(q K^T * sm_scale) V for every (sequence, q head) with
 // the cache read through block tables ([P5] "NVFP4 KV Cache：Blackwell 上的
@@ -37,9 +38,9 @@ namespace {
 
 constexpr int kDepth = 2;  // 16-token units per wave: 1 in compute, kDepth-1 in flight
 
-// Formats with 4-bit codes in the nibble layout (NVFP4, INT4 per-token-head)
-// and formats with per-token-head fp32 scales.
-template <int FMT> constexpr bool kNibble = FMT == 4 || FMT == 6;
+// Formats with 4-bit codes in the nibble layout (NVFP4, INT4 per-token-head,
+// MXFP4) and formats with per-token-head fp32 scales.
+template <int FMT> constexpr bool kNibble = FMT == 4 || FMT == 6 || FMT == 7;
 template <int FMT> constexpr bool kPth = FMT == 2 || FMT == 3 || FMT == 6;
 
 // INT4 keys enter the QK product with their channels in the order
@@ -54,7 +55,7 @@ struct Raw {
   static constexpr int VW = kNibble<FMT> ? D / 32 : D / 16;  // dwords of V codes
   uint32_t k[KW];
   uint32_t v[VW];
-  uint32_t ksc, vsc;  // NVFP4 block-scale bytes (K: this token's blocks; V: 4 tokens)
+  uint32_t ksc, vsc;  // block-scale bytes (K: this token's blocks; V: 4 tokens)
   float4 ks, vs;      // per-token-head scales of the lane's 4 score tokens
 };
 
@@ -101,6 +102,11 @@ __device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom&
       else
         r.ksc = __builtin_nontemporal_load(sp);
       r.vsc = ld_nt(chunk + g.v_scales + (int64_t)((NV * n) / 16) * P + 4 * quad);
+    } else if constexpr (FMT == 7) {
+      // the lane's D/4 key channels and D/16 value channels each lie in one
+      // 32-channel block: one E8M0 byte for the key, one per token for V
+      r.ksc = __builtin_nontemporal_load(chunk + g.k_scales + (int64_t)tk * (D / 32) + (DL * gq) / 32);
+      r.vsc = ld_nt(chunk + g.v_scales + (int64_t)((NV * n) / 32) * P + 4 * quad);
     } else {
       r.ks = ld_nt_f4(chunk + g.k_scales + 4 * (sub * 16 + 4 * gq));
       r.vs = ld_nt_f4(chunk + g.v_scales + 4 * (sub * 16 + 4 * gq));
@@ -110,8 +116,13 @@ __device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom&
 
 // K operand for QK MFMA kk: 8 channels (D/4)*gq + 8*kk .. +7 of token row n.
 template <int FMT, int D>
-__device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2_t ksc) {
-  if constexpr (FMT == 6) {
+__device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2_t ksc, float kmx) {
+  if constexpr (FMT == 7) {
+    // E2M1 * 2^k in binary16, the block scale applied by the conversion
+    uint32_t h[4];
+    e2m1x8_to_h_scaled(r.k[kk], kmx, h);
+    return cat(as_h2(h[0]), as_h2(h[1]), as_h2(h[2]), as_h2(h[3]));
+  } else if constexpr (FMT == 6) {
     // two's-complement nibble ^ 8 = code + 8; under the 0x64 exponent byte it
     // reads 1032 + code, and subtracting 1032 is exact
     const uint32_t w = r.k[kk] ^ 0x88888888u;
@@ -154,6 +165,10 @@ __device__ __forceinline__ half4_t v_operand(const Raw<FMT, D>& r, int nn, half2
     const uint32_t x = (nn & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
     const half2_t k1032 = {(half_t)1032.0f, (half_t)1032.0f};
     return cat4(as_h2(perm(0x64646464u, x, 0x04010400u)) - k1032, as_h2(perm(0x64646464u, x, 0x04030402u)) - k1032);
+  } else if constexpr (FMT == 7) {
+    // `pairs` already carry each token's block scale
+    const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+    return cat4(as_h2(perm(pairs[1], pairs[0], sel)), as_h2(perm(pairs[3], pairs[2], sel)));
   } else if constexpr (FMT != 4) {
     half2_t a, b;
     if constexpr (FMT == 2) {
@@ -187,10 +202,11 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
 
   half2_t ksc01 = {0, 0}, ksc23 = {0, 0};
   if constexpr (FMT == 4) e4m3x4_to_h(r.ksc, ksc01, ksc23);
+  const float kmx = FMT == 7 ? e8m0_scale(r.ksc) : 0.0f;
   float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<FMT, D>(r, kk, ksc01), qB[kk], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<FMT, D>(r, kk, ksc01, kmx), qB[kk], s, 0, 0, 0);
 
   // scores in log2 units; a unit wholly inside the context and on a valid
   // page (the common case, uniform across the wave) needs no token masks.
@@ -247,11 +263,17 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
       pA = half4_t{0, 0, 0, 0};
     half2_t vs01 = {0, 0}, vs23 = {0, 0};
     if constexpr (FMT == 4) e4m3x4_to_h(r.vsc, vs01, vs23);
+    float vmx[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == 7)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vmx[i] = e8m0_scale(r.vsc >> (8 * i));
     uint32_t pairs[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn) {
       if constexpr (FMT == 4)
         if ((nn & 1) == 0) e2m1x8_to_h(r.v[nn / 2], pairs);
+      if constexpr (FMT == 7)
+        if ((nn & 1) == 0) e2m1x8_to_h_scaled4(r.v[nn / 2], vmx, pairs);
       st.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand<FMT, D>(r, nn, vs01, vs23, pairs),
                                                          st.acc[nn], 0, 0, 0);
     }
@@ -517,6 +539,7 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s) {
     case 3: e = launch_fmt<3>(a, s); break;
     case 4: e = launch_fmt<4>(a, s); break;
     case 6: e = launch_fmt<6>(a, s); break;
+    case 7: e = launch_fmt<7>(a, s); break;
   }
   if (e != hipSuccess || a.num_splits == 1) return e;
   const float post = (fmt == 1 || fmt == 4) ? a.v_scale : 1.0f;

@@ -3,7 +3,8 @@
 // x_hat = s * q ([P3] "KV Cache 量化 · LLM Glossary", §它改变缓存表示; INT4
 // per-token-head codes are two's-complement nibbles), and for
 // NVFP4 x_hat = s_t * s_b * q ([P5] "NVFP4 KV Cache：Blackwell 上的 4-bit 缓存
-// 量化", §双层缩放怎样恢复动态范围).  KVarN ([P2] "KVarN：华为推出的原生 vLLM
+// 量化", §双层缩放怎样恢复动态范围); MXFP4 x_hat = 2^(e - 127) * q for the
+// block's E8M0 byte e (exact).  KVarN ([P2] "KVarN：华为推出的原生 vLLM
 // KV-cache 量化后端", §技术原理): the rotated tile is rebuilt from the folded
 // metadata, K_tj = rho_t (alpha_j code + beta_j) and
 // V_tj = gamma_j (alpha_t code + beta_t), and rotated back with the normalised
@@ -39,6 +40,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(WriteArgs a, float* k_out,
       const float* sc = reinterpret_cast<const float*>(chunk + a.geom.k_scales);
       kx = (float)((kc ^ 8) - 8) * sc[t];  // two's-complement nibble times scale
       vx = (float)((vc ^ 8) - 8) * sc[P + t];
+    } else if constexpr (FMT == 7) {
+      const uint32_t kb = chunk[(int64_t)t * (D / 2) + d / 2];
+      const uint32_t vb = chunk[a.geom.v_codes + 2 * D * (t / 4) + 4 * (d / 2) + (t % 4)];
+      const uint32_t kc = (d & 1) ? kb >> 4 : kb & 15u;
+      const uint32_t vc = (d & 1) ? vb >> 4 : vb & 15u;
+      const int ke = chunk[a.geom.k_scales + (int64_t)t * (D / 32) + d / 32];
+      const int ve = chunk[a.geom.v_scales + (int64_t)(d / 32) * P + t];
+      const float kq = (kc & 8u) ? -e2m1_val(kc & 7u) : e2m1_val(kc & 7u);
+      const float vq = (vc & 8u) ? -e2m1_val(vc & 7u) : e2m1_val(vc & 7u);
+      kx = ldexpf(kq, ke - 127);
+      vx = ldexpf(vq, ve - 127);
     } else if constexpr (FMT == 4) {
       const uint32_t kb = chunk[(int64_t)t * (D / 2) + d / 2];
       const uint32_t vb = chunk[a.geom.v_codes + 2 * D * (t / 4) + 4 * (d / 2) + (t % 4)];
@@ -127,6 +139,7 @@ hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_ou
     case 3: dequant_kernel<3><<<grid, threads, 0, s>>>(a, k_out, v_out); break;
     case 4: dequant_kernel<4><<<grid, threads, 0, s>>>(a, k_out, v_out); break;
     case 6: dequant_kernel<6><<<grid, threads, 0, s>>>(a, k_out, v_out); break;
+    case 7: dequant_kernel<7><<<grid, threads, 0, s>>>(a, k_out, v_out); break;
     case 5: dequant_kvarn_kernel<<<grid, 128, 0, s>>>(a, k_out, v_out, 1.0 / sqrt(128.0)); break;
     default: return hipErrorInvalidValue;
   }

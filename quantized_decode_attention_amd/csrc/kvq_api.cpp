@@ -26,6 +26,7 @@ kvq_status check_layout(const kvq_layout* L) {
     case KVQ_FP8_PTH:
     case KVQ_NVFP4:
     case KVQ_INT4_PTH:
+    case KVQ_MXFP4:
       if (L->head_dim != 32 && L->head_dim != 64 && L->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
       if (L->page_size < 16 || L->page_size > 256 || (L->page_size & (L->page_size - 1))) return KVQ_ERR_UNSUPPORTED;
       break;
@@ -70,6 +71,12 @@ ChunkGeom geometry(const kvq_layout* L) {
       g.k_scales = P * D;
       g.v_scales = P * D + P * D / 16;
       g.chunk_bytes = P * D + P * D / 8;
+      break;
+    case KVQ_MXFP4:
+      g.v_codes = P * D / 2;
+      g.k_scales = P * D;
+      g.v_scales = P * D + P * D / 32;
+      g.chunk_bytes = P * D + P * D / 16;
       break;
     case KVQ_KVARN_K4V2_G128:
       g.v_codes = P * D / 2;

@@ -196,6 +196,36 @@ __device__ __forceinline__ void e2m1x8_to_h(uint32_t w, uint32_t (&h)[4]) {
       : "v"(w));
 }
 
+// The same with a power-of-two scale: the conversion multiplies by the
+// scale's binary32 exponent, so E2M1 value * 2^k comes out exact while it is
+// a binary16 number (k in [-23, 13]).
+__device__ __forceinline__ void e2m1x8_to_h_scaled(uint32_t w, float scale, uint32_t (&h)[4]) {
+  asm("s_nop 1\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %0, %4, %5\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %1, %4, %5 op_sel:[1,0,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %2, %4, %5 op_sel:[0,1,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %3, %4, %5 op_sel:[1,1,0]\n\t"
+      "s_nop 1"
+      : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+      : "v"(w), "v"(scale));
+}
+
+// Byte i of w (two E2M1 codes) with its own power-of-two scale s[i].
+__device__ __forceinline__ void e2m1x8_to_h_scaled4(uint32_t w, const float (&s)[4], uint32_t (&h)[4]) {
+  asm("s_nop 1\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %0, %4, %5\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %1, %4, %6 op_sel:[1,0,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %2, %4, %7 op_sel:[0,1,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp4 %3, %4, %8 op_sel:[1,1,0]\n\t"
+      "s_nop 1"
+      : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+      : "v"(w), "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]));
+}
+
+// E8M0 byte e -> 2^(e - 127) as a binary32 scale operand (e = 0 gives +0,
+// used only by all-zero blocks).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) { return __uint_as_float((e & 0xFFu) << 23); }
+
 // Four E4M3 codes -> two binary16 pairs in code order.
 __device__ __forceinline__ void e4m3x4_to_h_hw(uint32_t w, uint32_t& lo, uint32_t& hi) {
   asm("s_nop 1\n\t"

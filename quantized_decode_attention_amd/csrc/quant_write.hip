@@ -10,8 +10,8 @@
 // head); a run of tokens that fills one aligned 16-token group of a page is
 // quantised by lanes of 16 values and written as contiguous 16-byte stores,
 // any other slot pattern row by row (D/8 lanes of 8 values).  The 4-bit
-// formats (NVFP4, INT4 per-token-head) use the same group / per-row split with
-// one lane per 16 values.
+// formats (NVFP4, MXFP4, INT4 per-token-head) use the same group / per-row
+// split with one lane per 16 values.
 // This file is built with -ffp-contract=off: every binary32 operation below
 // rounds exactly as written.
 #include "kvq_device.h"
@@ -306,13 +306,39 @@ __device__ __forceinline__ float int4_encode_block(const float* x, uint32_t* byt
   return s;
 }
 
+// MXFP4 codes of one lane's 16 values; lanes j and j ^ 1 hold the two halves
+// of a 32-value block and share its scale.  The block's E8M0 exponent is
+// floor(log2 max|x|) - 2 (OCP Microscaling conversion; [P5]
+// §双层缩放怎样恢复动态范围 gives the block size and the E8M0 scale), read off
+// the binary32 exponent field of the max: byte = field - 2 and x / 2^k is the
+// exact product x * 2^-k, with 2^-k's field 256 - field.  Values in the top
+// binade [6, 8) * 2^k saturate to 6.  An all-zero block stores byte 0.
+// byte[i] packs values 2i (low nibble) and 2i+1.  Returns the scale byte.
+__device__ __forceinline__ uint32_t mxfp4_encode_half(const float* x, uint32_t* byte) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = group_max<2>(amax);
+  const uint32_t field = __float_as_uint(amax) >> 23;
+  const float inv = amax > 0.0f ? __uint_as_float((256u - field) << 23) : 1.0f;
+  uint32_t code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) code[i] = e2m1_mag(fabsf(x[i] * inv)) | (sign_bit(x[i]) << 3);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) byte[i] = code[2 * i] | (code[2 * i + 1] << 4);
+  return amax > 0.0f ? field - 2u : 0u;
+}
+
 // One token-head row of a 4-bit format (FMT 4 = NVFP4, 6 = INT4
-// per-token-head) by D/16 lanes (lane j: values 16j .. 16j+15), any slot.
-// Both share the code layout; NVFP4 stores an E4M3 scale per block, INT4 one
-// fp32 scale per row.
+// per-token-head, 7 = MXFP4) by D/16 lanes (lane j: values 16j .. 16j+15),
+// any slot.  All share the code layout; NVFP4 stores an E4M3 scale per 16
+// values, MXFP4 an E8M0 scale per 32 values (lane pairs), INT4 one fp32 scale
+// per row.
 template <int FMT, int D>
 __device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, int j) {
   constexpr int NB = D / 16;
+  constexpr int NS = FMT == 7 ? D / 32 : D / 16;  // block-scale bytes per row
+  constexpr int SL = FMT == 7 ? 2 : 1;            // lanes per block scale
   RowCtx c;
   if (!row_ctx(a, row, c)) return;
   float x[16];
@@ -324,20 +350,23 @@ __device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, 
   float s = 0.0f;
   if constexpr (FMT == 4)
     sb = nvfp4_encode_block(x, c.side ? a.v_scale : a.k_scale, a.flags, byte);
+  else if constexpr (FMT == 7)
+    sb = mxfp4_encode_half(x, byte);
   else
     s = int4_encode_block<NB>(x, byte);
+  const bool scale_lane = (FMT == 4 || FMT == 7) && j % SL == 0;
   if (c.side == 0) {
     uint2 packed;
     packed.x = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
     packed.y = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
     *reinterpret_cast<uint2*>(c.chunk + (int64_t)c.t * (D / 2) + 8 * j) = packed;
-    if constexpr (FMT == 4) c.chunk[a.geom.k_scales + (int64_t)c.t * NB + j] = (uint8_t)sb;
+    if (scale_lane) c.chunk[a.geom.k_scales + (int64_t)c.t * NS + j / SL] = (uint8_t)sb;
   } else {
     // V: byte (quad, channel pair, token) so that each byte belongs to one token
     uint8_t* vp = c.chunk + a.geom.v_codes + 2 * D * (c.t / 4) + 32 * j + (c.t % 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) vp[4 * i] = (uint8_t)byte[i];
-    if constexpr (FMT == 4) c.chunk[a.geom.v_scales + (int64_t)j * a.P + c.t] = (uint8_t)sb;
+    if (scale_lane) c.chunk[a.geom.v_scales + (int64_t)(j / SL) * a.P + c.t] = (uint8_t)sb;
   }
   if constexpr (FMT == 6)
     if (j == 0) reinterpret_cast<float*>(c.chunk + a.geom.k_scales)[c.side * a.P + c.t] = s;
@@ -345,15 +374,17 @@ __device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, 
 
 // One workgroup per (16 consecutive tokens, kv head), as for the 8-bit
 // formats: an aligned run is assembled in LDS (K codes and V codes: one
-// contiguous run each; NVFP4 K block scales: one run, V block scales: D/16
-// runs of 16 bytes; INT4: 16 fp32 scales per side) and written with 16-byte
-// stores; other slot patterns go row by row.
+// contiguous run each; NVFP4 / MXFP4 K block scales: one run, V block scales:
+// one run of 16 bytes per block column; INT4: 16 fp32 scales per side) and
+// written with 16-byte stores; other slot patterns go row by row.
 template <int FMT, int D>
 __global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
-  constexpr int NB = D / 16;         // blocks per row
-  constexpr int CB = 16 * D / 2;     // code bytes of 16 tokens, one side
+  constexpr int NB = D / 16;                      // 16-value lanes per row
+  constexpr int NS = FMT == 7 ? D / 32 : D / 16;  // block-scale bytes per row
+  constexpr int SL = FMT == 7 ? 2 : 1;            // lanes per block scale
+  constexpr int CB = 16 * D / 2;                  // code bytes of 16 tokens, one side
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][CB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][16 * NB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][16 * NS];
   __shared__ float s_rs[2][16];
   __shared__ int s_ok;
   __shared__ int64_t s_slot0;
@@ -383,20 +414,23 @@ __global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
     uint32_t sb = 0;
     if constexpr (FMT == 4) {
       sb = nvfp4_encode_block(x, side ? a.v_scale : a.k_scale, a.flags, byte);
+    } else if constexpr (FMT == 7) {
+      sb = mxfp4_encode_half(x, byte);
     } else {
       const float s = int4_encode_block<NB>(x, byte);
       if (q == 0) s_rs[side][sidx] = s;
     }
+    const bool scale_lane = q % SL == 0;
     if (side == 0) {
       uint8_t* kp = s_codes[0] + sidx * (D / 2) + 8 * q;
 #pragma unroll
       for (int i = 0; i < 8; ++i) kp[i] = (uint8_t)byte[i];
-      s_sc[0][sidx * NB + q] = (uint8_t)sb;
+      if (scale_lane) s_sc[0][sidx * NS + q / SL] = (uint8_t)sb;
     } else {
       uint8_t* vp = s_codes[1] + 2 * D * (sidx / 4) + 32 * q + (sidx % 4);
 #pragma unroll
       for (int i = 0; i < 8; ++i) vp[4 * i] = (uint8_t)byte[i];
-      s_sc[1][q * 16 + sidx] = (uint8_t)sb;  // [block][token]
+      if (scale_lane) s_sc[1][(q / SL) * 16 + sidx] = (uint8_t)sb;  // [block][token]
     }
   }
   __syncthreads();
@@ -408,14 +442,14 @@ __global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
     uint8_t* base = chunk + (sd ? a.geom.v_codes : 0) + (int64_t)t0 * (D / 2);
     *reinterpret_cast<uint4*>(base + o) = *reinterpret_cast<const uint4*>(&s_codes[sd][o]);
   }
-  if constexpr (FMT == 4) {
-    // K block scales: 16 * NB contiguous bytes; V block scales: NB runs of 16
-    if (tid < NB)
-      *reinterpret_cast<uint4*>(chunk + a.geom.k_scales + (int64_t)t0 * NB + 16 * tid) =
+  if constexpr (FMT == 4 || FMT == 7) {
+    // K block scales: 16 * NS contiguous bytes; V block scales: NS runs of 16
+    if (tid < NS)
+      *reinterpret_cast<uint4*>(chunk + a.geom.k_scales + (int64_t)t0 * NS + 16 * tid) =
           *reinterpret_cast<const uint4*>(&s_sc[0][16 * tid]);
-    else if (tid < 2 * NB)
-      *reinterpret_cast<uint4*>(chunk + a.geom.v_scales + (int64_t)(tid - NB) * a.P + t0) =
-          *reinterpret_cast<const uint4*>(&s_sc[1][16 * (tid - NB)]);
+    else if (tid < 2 * NS)
+      *reinterpret_cast<uint4*>(chunk + a.geom.v_scales + (int64_t)(tid - NS) * a.P + t0) =
+          *reinterpret_cast<const uint4*>(&s_sc[1][16 * (tid - NS)]);
   } else {
     if (tid < 32)
       reinterpret_cast<float*>(chunk + a.geom.k_scales)[(tid / 16) * a.P + t0 + (tid % 16)] =
@@ -429,7 +463,7 @@ hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
   const int64_t groups = (a.n_tok + 15) / 16;
   if (groups > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
   const dim3 g2((unsigned)groups, (unsigned)a.H);
-  if constexpr (FMT == 4 || FMT == 6) {
+  if constexpr (FMT == 4 || FMT == 6 || FMT == 7) {
     switch (a.D) {
       case 32: quant_write_4bit<FMT, 32><<<g2, kBlock, 0, s>>>(a); break;
       case 64: quant_write_4bit<FMT, 64><<<g2, kBlock, 0, s>>>(a); break;
@@ -456,6 +490,7 @@ hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s) {
     case 3: return launch_fmt<3>(a, s);
     case 4: return launch_fmt<4>(a, s);
     case 6: return launch_fmt<6>(a, s);
+    case 7: return launch_fmt<7>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -22,7 +22,7 @@ import numpy as np
 
 # Largest code value of each format's scaled grid (used to express the row's
 # largest reconstructed magnitude as an effective scale).
-TOP_CODE = {1: 448.0, 2: 127.0, 3: 448.0, 4: 6.0, 6: 7.0}
+TOP_CODE = {1: 448.0, 2: 127.0, 3: 448.0, 4: 6.0, 6: 7.0, 7: 6.0}
 # Relative margin above the row's largest reconstruction beyond which an input
 # counts as clipped (above every format's half-step rounding error).
 CLIP_MARGIN = 0.25
@@ -163,11 +163,11 @@ def report_format(K, w, fmt, flags=0):
 
 
 FORMATS_OF = {
-    "glossary_int8": [(2, 0), (3, 0), (1, 0), (6, 0), (4, 0), (4, 1)],
-    "fp8_sink_4k": [(1, 0), (3, 0), (2, 0), (6, 0), (4, 0), (4, 1)],
-    "int8_32k": [(2, 0), (3, 0), (6, 0), (4, 0)],
-    "nvfp4_16k": [(4, 0), (4, 1), (3, 0), (2, 0), (6, 0)],
-    "kvarn_16k": [(5, 0), (2, 0), (4, 0), (6, 0)],
+    "glossary_int8": [(2, 0), (3, 0), (1, 0), (6, 0), (4, 0), (4, 1), (7, 0)],
+    "fp8_sink_4k": [(1, 0), (3, 0), (2, 0), (6, 0), (4, 0), (4, 1), (7, 0)],
+    "int8_32k": [(2, 0), (3, 0), (6, 0), (4, 0), (7, 0)],
+    "nvfp4_16k": [(4, 0), (4, 1), (7, 0), (3, 0), (2, 0), (6, 0)],
+    "kvarn_16k": [(5, 0), (2, 0), (4, 0), (7, 0), (6, 0)],
 }
 
 

@@ -64,7 +64,21 @@ __global__ void k_cvt_fp8_f16_asm(const uint32_t* src, int n, uint32_t* out) {
   out[2 * (int64_t)i + 1] = hi;
 }
 
+// One v_mfma_f32_16x16x32_f16 on operands given per lane: a and b hold 8
+// binary16 values per lane (64 lanes), out gets the 4 results of each lane.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+__global__ void k_mfma_f16(const half8_t* a, const half8_t* b, float4_t* out) {
+  const int l = threadIdx.x;
+  out[l] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[l], b[l], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
 extern "C" {
+int probe_mfma_f16(const void* a, const void* b, void* out) {
+  k_mfma_f16<<<1, 64>>>(reinterpret_cast<const half8_t*>(a), reinterpret_cast<const half8_t*>(b),
+                        reinterpret_cast<float4_t*>(out));
+  return (int)hipGetLastError();
+}
 int probe_cvt_fp8_f16_asm(const uint32_t* src, int n, uint32_t* out) {
   if (n <= 0) return 0;
   k_cvt_fp8_f16_asm<<<(n + 255) / 256, 256>>>(src, n, out);

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(K):
 
 
 def _layouts():
-    for fmt in (1, 2, 3, 4, 6):
+    for fmt in (1, 2, 3, 4, 6, 7):
         for D in (32, 64, 128):
             for P in (16, 32, 64, 128, 256):
                 yield fmt, 0, 3, D, P
@@ -44,7 +44,7 @@ def test_page_bytes_match_oracle(K, fmt, flags, H, D, P):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(fmt=0), dict(fmt=7), dict(D=96), dict(D=256), dict(P=8), dict(P=24), dict(P=48), dict(P=512), dict(H=0),
+    dict(fmt=0), dict(fmt=8), dict(fmt=7, flags=1), dict(D=96), dict(D=256), dict(P=8), dict(P=24), dict(P=48), dict(P=512), dict(H=0),
     dict(pages=0), dict(fmt=5, P=16), dict(fmt=5, D=64), dict(flags=1), dict(flags=2, fmt=4),
     dict(fmt=1, ks=0.0), dict(fmt=1, ks=float("inf")), dict(fmt=4, vs=-1.0), dict(fmt=4, vs=1e-30),
 ])

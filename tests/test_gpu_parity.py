@@ -13,8 +13,8 @@ from gpu_util import (assert_attn_close, dev, first_mismatch, gpu_decode, gpu_wr
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (6, 0)]
-FMT_IDS = ["fp8pt", "int8pth", "fp8pth", "nvfp4", "nvfp4_4over6", "int4pth"]
+FORMATS = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (6, 0), (7, 0)]
+FMT_IDS = ["fp8pt", "int8pth", "fp8pth", "nvfp4", "nvfp4_4over6", "int4pth", "mxfp4"]
 
 
 def edge_rows(rng, n, H, D):
@@ -226,7 +226,7 @@ def test_workspace_reuse_many_calls(K, O):
         assert_attn_close(out.cpu().numpy().astype(np.float64), ref[:nb], f"call {it}")
 
 
-@pytest.mark.parametrize("fmt,flags", [(2, 0), (4, 1), (6, 0)], ids=["int8pth", "nvfp4_4over6", "int4pth"])
+@pytest.mark.parametrize("fmt,flags", [(2, 0), (4, 1), (6, 0), (7, 0)], ids=["int8pth", "nvfp4_4over6", "int4pth", "mxfp4"])
 def test_decode_long_splits_and_limits(K, O, fmt, flags):
     """One split walking more than 256 pages (several block-table chunks in
     LDS), the largest page size, the maximum split count, and a batch whose
@@ -255,3 +255,31 @@ def test_decode_long_splits_and_limits(K, O, fmt, flags):
             assert ws.num_splits == -(-mp // pps)
             for (b, h), r in zip(pairs, ref):
                 assert_attn_close(got[b, h], r, f"P={P} splits={splits} b={b} h={h}")
+
+
+def test_mxfp4_decode_small_and_large_blocks(K, O):
+    """MXFP4 blocks across the whole binary16 range: block exponents from -26
+    (subnormal inputs, whose binary16 operands round) to 13 (values near
+    65504), mixed within one token row and across tokens."""
+    rng = np.random.default_rng(4242)
+    B, H, G, D, P = 3, 2, 8, 128, 16
+    ctx = np.array([40, 130, 77], np.int32)
+    bt, num_pages, slots = paged_problem(rng, B, H, G, D, P, ctx)
+    n = slots.shape[0]
+    mags = 2.0 ** rng.integers(-24, 15, (n, H, D // 32))  # per-block magnitude
+    k16 = (rng.uniform(-1, 1, (n, H, D)) * np.repeat(mags, 32, axis=-1)).astype(np.float16)
+    mags = 2.0 ** rng.integers(-24, 15, (n, H, D // 32))
+    v16 = (rng.uniform(-1, 1, (n, H, D)) * np.repeat(mags, 32, axis=-1)).astype(np.float16)
+    lay = K.layout(7, H, D, P, num_pages)
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    got_cache = gpu_write(K, lay, k16, v16, slots).cpu().numpy()
+    mm = first_mismatch(got_cache, cache)
+    assert mm is None, f"cache byte {mm[0]}: gpu {mm[1]:#x} oracle {mm[2]:#x}"
+    # queries small enough that the huge keys give finite, spread-out logits
+    q16 = (workloads.random_halves(rng, (B, H * G, D)) * np.float16(2.0 ** -14)).astype(np.float16)
+    sm = 1.0 / math.sqrt(D)
+    ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, sm)
+    for splits in (1, 4):
+        log(f"mxfp4 wide-range decode splits={splits}")
+        got, _ = gpu_decode(K, lay, dev(cache), q16, bt, ctx, sm, num_splits=splits)
+        assert_attn_close(got, ref, f"splits={splits}")

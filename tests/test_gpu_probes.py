@@ -123,3 +123,60 @@ def test_cvt_e2m1_to_f16_exact(PL, O):
             b = (int(w) >> (8 * k)) & 0xFF
             for e, c in enumerate((b & 15, b >> 4)):
                 assert got[i, k, e] == dec[c] and np.signbit(got[i, k, e]) == np.signbit(dec[c]), (hex(int(w)), k, e)
+
+
+def test_cvt_e2m1_to_f16_power_of_two_scales(PL, O):
+    """E2M1 pairs -> binary16 with scale 2^k, as the MXFP4 decode issues them
+    (the block's E8M0 byte placed in a binary32 exponent field): every code
+    gives E2M1 value * 2^k exactly for every k whose products are binary16
+    numbers, binary16 subnormals included (k in [-23, 13]); binary16 inputs
+    give MXFP4 block exponents in [-26, 13], and below -23 the conversion
+    stays within 2^-24 of the exact value.  Byte 0 (scale +0) turns the zero
+    codes into zeros."""
+    import torch
+    words = _all_byte_positions(np.random.default_rng(4))
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    dec = np.array([O.e2m1_decode(c) for c in range(16)])
+    codes = np.stack([(words[:, None] >> (8 * np.arange(4))) & 15, (words[:, None] >> (8 * np.arange(4) + 4)) & 15],
+                     axis=-1).astype(np.int64)  # [word, byte, nibble]
+    for k in list(range(-30, 14)):
+        scale = np.float32(2.0 ** k)
+        out = torch.zeros(words.size * 4, dtype=torch.int32, device="cuda")
+        assert PL.probe_cvt_fp4_f16_asm(_ptr(src), words.size, ctypes.c_float(float(scale)), _ptr(out)) == 0
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.float16).astype(np.float64).reshape(words.size, 4, 2)
+        exact = dec[codes] * 2.0 ** k
+        if k >= -23:
+            assert np.array_equal(got, exact), f"k={k}"
+            assert np.array_equal(np.signbit(got), np.signbit(exact)), f"k={k}"
+        else:
+            assert np.all(np.abs(got - exact) <= 2.0 ** -24), f"k={k}"
+    log("probe cvt e2m1->f16 with 2^k scales: exact for k >= -23")
+    zero = torch.from_numpy(np.array([0x80808080 - 2 ** 32, 0], np.int64).astype(np.int32)).cuda()
+    out = torch.ones(8, dtype=torch.int32, device="cuda")
+    assert PL.probe_cvt_fp4_f16_asm(_ptr(zero), 2, ctypes.c_float(0.0), _ptr(out)) == 0
+    torch.cuda.synchronize()
+    assert not np.any(out.cpu().numpy().view(np.float16).astype(np.float64))
+
+
+def test_mfma_f16_subnormal_operands(PL):
+    """The QK product takes binary16 subnormal operands (MXFP4 keys of small
+    blocks) without flushing: 16x16x32 products of m * 2^-24 values with small
+    integers come out exactly."""
+    import torch
+    rng = np.random.default_rng(5)
+    A = (rng.integers(-7, 8, (16, 32)) * 2.0 ** -24).astype(np.float16)  # subnormals
+    A[3] = (rng.integers(-7, 8, 32) * 2.0 ** -14).astype(np.float16)     # normal row for contrast
+    B = rng.integers(-4, 5, (32, 16)).astype(np.float16)
+    assert np.array_equal(A.astype(np.float64), np.round(A.astype(np.float64) * 2.0 ** 24) * 2.0 ** -24)
+    # lane l: A row l % 16 and B column l % 16, k = 8 * (l // 16) + 0..7
+    la = np.stack([A[l % 16, 8 * (l // 16):8 * (l // 16) + 8] for l in range(64)])
+    lb = np.stack([B[8 * (l // 16):8 * (l // 16) + 8, l % 16] for l in range(64)])
+    out = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    assert PL.probe_mfma_f16(_ptr(torch.from_numpy(la).cuda()), _ptr(torch.from_numpy(lb).cuda()), _ptr(out)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = A.astype(np.float64) @ B.astype(np.float64)  # exact: small integers times 2^-24
+    # lane l: column l % 16, rows 4 * (l // 16) + 0..3
+    want = np.stack([ref[4 * (l // 16):4 * (l // 16) + 4, l % 16] for l in range(64)])
+    assert np.array_equal(got, want), np.abs(got - want).max()
