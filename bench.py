@@ -382,7 +382,7 @@ def main():
             key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "")
             fmts[key] = {"workload": name, "decode_gbs": round(p.kv_bytes / (ms_d * 1e-3) / 1e9, 1),
                          "decode_frac_of_peak": round(p.kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "decode_us": round(ms_d * 1e3, 2), "step_us": round(ms_s * 1e3, 2),
+                         "decode_us": round(ms_d * 1e3, 2), **p.dec_percentiles_us(), "step_us": round(ms_s * 1e3, 2),
                          "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits,
                          "step": ("append to the binary16 tail (tile quantised when complete) + decode over "
                                   "tiles and tail" if fmt == K.KVQ_KVARN_K4V2_G128 else "append + decode")}

@@ -196,18 +196,26 @@ kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void*
                             const int32_t* block_tables, int32_t max_pages_per_seq, void* cache,
                             void* stream);
 
-/* Bytes of workspace kvq_decode_attention needs for this problem (host-only;
- * -1 if invalid): one partial record of binary32 (max, sum, output row) per
- * (sequence, kv head, context split), 0 when a single split is used.
+/* Bytes of workspace kvq_decode_attention needs for this problem (-1 if
+ * invalid, including num_q_heads not a multiple of H): one partial record of
+ * binary32 (max, sum, output row) per (sequence, kv head, context split), 0
+ * when a single split is used (KVarN: always at least one record).
  * num_splits: 0 = let the library choose, else the number of context splits
- * per (sequence, kv head) to use (clamped to [1, min(256, max_pages_per_seq)]). */
+ * per (sequence, kv head) to use (clamped to [1, min(256, max_pages_per_seq)]).
+ * The library's choice fills one resident round of the split kernel on the
+ * current HIP device (its compute units times the kernel's resident
+ * workgroups per unit for this format, D and GQA group), with at least 8 pages
+ * per split; it is fixed per device and process, so a workspace sized here
+ * fits every later call with the same arguments.  Without a usable device the
+ * plan assumes 256 compute units and 2 workgroups per unit.  Host-only (no
+ * kernel launched). */
 int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,
                                    int32_t max_pages_per_seq, int32_t num_splits);
 
-/* Number of context splits kvq_decode_attention will use (host-only; -1 if
- * invalid).  Same arguments as kvq_decode_workspace_bytes. */
-int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t max_pages_per_seq,
-                              int32_t num_splits);
+/* Number of context splits kvq_decode_attention will use (-1 if invalid).
+ * Same arguments and rules as kvq_decode_workspace_bytes. */
+int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,
+                              int32_t max_pages_per_seq, int32_t num_splits);
 
 /* Dequant-fused paged GQA decode attention ([P5] §K 与 V 的量化误差进入 attention
  * 的位置不同: O = softmax(Q K^T / sqrt(d) + M) V with M = 0 for decode; the

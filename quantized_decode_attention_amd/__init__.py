@@ -66,7 +66,7 @@ def _load():
         "kvq_check_device": (ctypes.c_int, [ctypes.c_int]),
         "kvq_quantize_write": (ctypes.c_int, [LP, P, P, P, I64, P, P]),
         "kvq_decode_workspace_bytes": (I64, [LP, I32, I32, I32, I32]),
-        "kvq_decode_num_splits": (I32, [LP, I32, I32, I32]),
+        "kvq_decode_num_splits": (I32, [LP, I32, I32, I32, I32]),
         "kvq_decode_attention": (ctypes.c_int, [LP, P, P, I32, P, I32, P, I32, F32, P, P, P, I64, I32, P]),
         "kvq_dequantize": (ctypes.c_int, [LP, P, P, I64, P, P, P]),
         "kvq_kvarn_append": (ctypes.c_int, [LP, P, P, P, P, I64, P, I32, P, I32, P, P]),
@@ -142,8 +142,9 @@ def kvq_decode_workspace_bytes(lay: KvqLayout, batch: int, num_q_heads: int, max
     return int(_lib.kvq_decode_workspace_bytes(ctypes.byref(lay), batch, num_q_heads, max_pages_per_seq, num_splits))
 
 
-def kvq_decode_num_splits(lay: KvqLayout, batch: int, max_pages_per_seq: int, num_splits: int = 0) -> int:
-    return int(_lib.kvq_decode_num_splits(ctypes.byref(lay), batch, max_pages_per_seq, num_splits))
+def kvq_decode_num_splits(lay: KvqLayout, batch: int, num_q_heads: int, max_pages_per_seq: int,
+                          num_splits: int = 0) -> int:
+    return int(_lib.kvq_decode_num_splits(ctypes.byref(lay), batch, num_q_heads, max_pages_per_seq, num_splits))
 
 
 def kvq_decode_attention(lay: KvqLayout, cache, q, block_tables, context_lens, sm_scale, out, workspace,
@@ -193,5 +194,5 @@ class DecodeWorkspace:
         nbytes = kvq_decode_workspace_bytes(lay, batch, num_q_heads, max_pages_per_seq, num_splits)
         if nbytes < 0:
             raise KvqError(1, "kvq_decode_workspace_bytes")
-        self.num_splits = kvq_decode_num_splits(lay, batch, max_pages_per_seq, num_splits)
+        self.num_splits = kvq_decode_num_splits(lay, batch, num_q_heads, max_pages_per_seq, num_splits)
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)

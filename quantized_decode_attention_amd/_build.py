@@ -29,7 +29,7 @@ SOURCES = {
     "kvarn_write.hip": ["-ffp-contract=off"],
     "dequant.hip": ["-ffp-contract=off"],
     "decode_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "kvarn_decode.hip": [],
+    "kvarn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 COMMON = [

@@ -528,7 +528,49 @@ hipError_t launch_fmt(const DecodeArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int FMT, int D, int G>
+int occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&decode_kernel<FMT, D, G>), 256,
+                                                   0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+template <int FMT, int D>
+int occupancy_g(int G) {
+  switch (G) {
+    case 1: return occupancy<FMT, D, 1>();
+    case 2: return occupancy<FMT, D, 2>();
+    case 4: return occupancy<FMT, D, 4>();
+    case 8: return occupancy<FMT, D, 8>();
+  }
+  return 0;
+}
+
+template <int FMT>
+int occupancy_dg(int D, int G) {
+  switch (D) {
+    case 32: return occupancy_g<FMT, 32>(G);
+    case 64: return occupancy_g<FMT, 64>(G);
+    case 128: return occupancy_g<FMT, 128>(G);
+  }
+  return 0;
+}
+
 }  // namespace
+
+int decode_blocks_per_cu(int fmt, int D, int G) {
+  switch (fmt) {
+    case 1: return occupancy_dg<1>(D, G);
+    case 2: return occupancy_dg<2>(D, G);
+    case 3: return occupancy_dg<3>(D, G);
+    case 4: return occupancy_dg<4>(D, G);
+    case 6: return occupancy_dg<6>(D, G);
+    case 7: return occupancy_dg<7>(D, G);
+  }
+  return 0;
+}
 
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;

@@ -527,6 +527,27 @@ __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
 
 }  // namespace
 
+namespace {
+template <int G>
+int kvarn_occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&kvarn_decode_kernel<G>), 256,
+                                                   0) != hipSuccess)
+    return 0;
+  return n;
+}
+}  // namespace
+
+int kvarn_decode_blocks_per_cu(int G) {
+  switch (G) {
+    case 1: return kvarn_occupancy<1>();
+    case 2: return kvarn_occupancy<2>();
+    case 4: return kvarn_occupancy<4>();
+    case 8: return kvarn_occupancy<8>();
+  }
+  return 0;
+}
+
 hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   const dim3 grid((unsigned)a.num_splits, (unsigned)a.H, (unsigned)a.B);

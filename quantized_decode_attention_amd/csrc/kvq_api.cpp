@@ -115,16 +115,53 @@ kvq_status current_device_ok() {
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
 // Context splits per (sequence, kv head): enough workgroups for one resident
-// round on MI355X (256 compute units x 2 decode workgroups), while keeping at
-// least 8 pages (two per wavefront) in a split.  Empty trailing splits are
-// dropped.
-constexpr int64_t kTargetWorkgroups = 512;
+// round of the split kernel, i.e. compute units x the kernel's resident
+// workgroups per compute unit, while keeping at least 8 pages (two per
+// wavefront) in a split.  Empty trailing splits are dropped.  The 4-bit
+// formats' kernels are bound by instruction issue and latency, and a third
+// resident workgroup per CU (their registers allow it) hides more of it
+// (~10% on MI355X); the 8-bit formats are bound by HBM, where a third
+// workgroup only adds contention, so they stay at 2.  Both figures come from
+// the current device and are cached per device; without a usable device the
+// plan assumes MI355X's 256 compute units and 2 workgroups per CU.
+constexpr int kMaxDevices = 64;
+constexpr int kFallbackCUs = 256;
+constexpr int kFallbackBlocksPerCU = 2;
+std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<int> g_blocks_per_cu[kMaxDevices][8][3][4];  // [dev][format][D 32/64/128][G 1/2/4/8]
 
-void plan_splits(int batch, int H, int max_pages, int hint, int* splits, int* pages_per_split) {
+int index_of_d(int D) { return D == 32 ? 0 : (D == 64 ? 1 : 2); }
+int index_of_g(int G) { return G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3)); }
+
+int64_t target_workgroups(const kvq_layout* L, int G) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices || device_ok(dev) != KVQ_OK ||
+      L->format < 1 || L->format > 7 || (G != 1 && G != 2 && G != 4 && G != 8))
+    return (int64_t)kFallbackCUs * kFallbackBlocksPerCU;
+  int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = kFallbackCUs;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  }
+  std::atomic<int>& slot = g_blocks_per_cu[dev][L->format][index_of_d(L->head_dim)][index_of_g(G)];
+  int per_cu = slot.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    per_cu = L->format == KVQ_KVARN_K4V2_G128 ? kvarn_decode_blocks_per_cu(G)
+                                              : decode_blocks_per_cu(L->format, L->head_dim, G);
+    if (per_cu < 1) per_cu = kFallbackBlocksPerCU;
+    const bool eight_bit = L->format == KVQ_FP8_PER_TENSOR || L->format == KVQ_INT8_PTH || L->format == KVQ_FP8_PTH;
+    if (eight_bit && per_cu > 2) per_cu = 2;
+    slot.store(per_cu, std::memory_order_relaxed);
+  }
+  return (int64_t)cus * per_cu;
+}
+
+void plan_splits(int batch, int H, int max_pages, int hint, int64_t target, int* splits, int* pages_per_split) {
   const int64_t units = (int64_t)batch * H;
   int s = hint;
   if (s <= 0) {
-    const int64_t want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
+    const int64_t want = units > 0 ? (target + units - 1) / units : 1;
     const int64_t cap = (max_pages + 7) / 8;
     s = (int)(want < cap ? want : cap);
   }
@@ -209,21 +246,25 @@ kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void*
   return from_hip(launch_kvarn_append(a, static_cast<hipStream_t>(stream)));
 }
 
-int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t max_pages_per_seq,
-                              int32_t num_splits) {
-  if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0) return -1;
+int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,
+                              int32_t max_pages_per_seq, int32_t num_splits) {
+  if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0 ||
+      num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
+    return -1;
   int s, pps;
-  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits, &s, &pps);
+  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits,
+              target_workgroups(layout, num_q_heads / layout->num_kv_heads), &s, &pps);
   return s;
 }
 
 int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,
                                    int32_t max_pages_per_seq, int32_t num_splits) {
   if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0 ||
-      num_q_heads < 1)
+      num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return -1;
   int s, pps;
-  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits, &s, &pps);
+  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits,
+              target_workgroups(layout, num_q_heads / layout->num_kv_heads), &s, &pps);
   return workspace_bytes_for(layout, batch, s);
 }
 
@@ -243,7 +284,7 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
   if (kvarn_tail && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
   if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
   int splits, pps;
-  plan_splits(batch, H, max_pages_per_seq, num_splits, &splits, &pps);
+  plan_splits(batch, H, max_pages_per_seq, num_splits, target_workgroups(layout, G), &splits, &pps);
   const int64_t need = workspace_bytes_for(layout, batch, splits);
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;

@@ -77,4 +77,9 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s);
 
+// Resident workgroups per compute unit of the decode split kernel for a
+// format, head size and GQA group on the current device (0 if unknown).
+int decode_blocks_per_cu(int fmt, int D, int G);
+int kvarn_decode_blocks_per_cu(int G);
+
 }  // namespace kvq

@@ -78,13 +78,18 @@ def test_argument_errors_before_launch(K):
 
 
 def test_split_plan_and_workspace(K):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("the automatic plan follows the device; covered by the GPU tests")
     lay = K.layout(2, 8, 128, 16, 16384)
-    # one MI355X: one resident round of 512 workgroups
-    assert K.kvq_decode_num_splits(lay, 8, 2048) == 8
-    assert K.kvq_decode_num_splits(lay, 32, 256) == 2
-    assert K.kvq_decode_num_splits(lay, 2, 1) == 1
-    assert K.kvq_decode_num_splits(lay, 2, 10, 3) == 3
-    assert K.kvq_decode_num_splits(lay, 2, 9, 4) == 3  # empty trailing split dropped
+    # no device: 256 compute units x 2 workgroups, one resident round of 512
+    assert K.kvq_decode_num_splits(lay, 8, 64, 2048) == 8
+    assert K.kvq_decode_num_splits(lay, 32, 64, 256) == 2
+    assert K.kvq_decode_num_splits(lay, 2, 64, 1) == 1
+    assert K.kvq_decode_num_splits(lay, 2, 64, 10, 3) == 3
+    assert K.kvq_decode_num_splits(lay, 2, 64, 9, 4) == 3  # empty trailing split dropped
+    assert K.kvq_decode_num_splits(lay, 2, 60, 9, 4) == -1  # q heads not a multiple of kv heads
+    assert K.kvq_decode_workspace_bytes(lay, 2, 60, 9, 4) == -1
     assert K.kvq_decode_workspace_bytes(lay, 8, 64, 2048, 1) == 0
     for splits in (3, 16):
         b = K.kvq_decode_workspace_bytes(lay, 8, 64, 2048, splits)
@@ -93,7 +98,7 @@ def test_split_plan_and_workspace(K):
     # KVarN always merges (binary16 tail, rotation back): a record even for one split
     klay = K.layout(5, 8, 128, 128, 2048)
     assert K.kvq_decode_workspace_bytes(klay, 16, 64, 128, 1) == 16 * 8 * 1 * (2 * 8 + 8 * 128) * 4
-    assert K.kvq_decode_num_splits(klay, 16, 128) == 4
+    assert K.kvq_decode_num_splits(klay, 16, 64, 128) == 4
 
 
 def test_status_strings(K):

@@ -283,3 +283,26 @@ def test_mxfp4_decode_small_and_large_blocks(K, O):
         log(f"mxfp4 wide-range decode splits={splits}")
         got, _ = gpu_decode(K, lay, dev(cache), q16, bt, ctx, sm, num_splits=splits)
         assert_attn_close(got, ref, f"splits={splits}")
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5, 6, 7])
+def test_auto_split_plan_fills_the_device(K, O, fmt):
+    """The automatic plan gives one resident round of the split kernel (2 to
+    4 workgroups per compute unit on MI355X's 256), and a workspace of exactly
+    the queried size is accepted while one byte less is refused."""
+    import ctypes
+    import torch
+    B, H, G, D = 16, 8, 8, 128
+    P = 128 if fmt == 5 else 16
+    mp = 16384 // P
+    lay = K.layout(fmt, H, D, P, B * mp, 0.05, 0.05)
+    s = K.kvq_decode_num_splits(lay, B, H * G, mp)
+    log(f"auto plan fmt={fmt}: {s} splits, {s * B * H} workgroups")
+    assert 2 * 256 <= s * B * H <= 4 * 256 or s == -(-mp // 8)
+    need = K.kvq_decode_workspace_bytes(lay, B, H * G, mp)
+    assert need == B * H * s * (2 * 8 + 8 * D) * 4
+    # the call validates the workspace size before touching any buffer
+    cache = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    p = ctypes.c_void_p(cache.data_ptr())
+    st = K.lib.kvq_decode_attention(ctypes.byref(lay), p, p, H * G, p, mp, p, B, 0.1, None, p, p, need - 1, 0, None)
+    assert st == 3
