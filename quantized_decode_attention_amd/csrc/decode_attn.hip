@@ -69,47 +69,85 @@ __device__ __forceinline__ void zero_raw(Raw<FMT, D>& r) {
   r.ks = r.vs = float4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Per-lane byte offsets of a unit's loads, fixed for the whole kernel: the
+// unit's position (page, 16-token group) enters through a wave-uniform base
+// pointer, so every load is a global load with a scalar base and a 32-bit
+// vector offset, and no 64-bit address arithmetic runs per unit.
+struct LaneOffs {
+  uint32_t k, v, ks, vs;
+};
+
+template <int FMT, int D>
+__device__ __forceinline__ LaneOffs lane_offsets(int gq, int n, int P) {
+  constexpr int DL = D / 4;
+  constexpr int NV = D / 16;
+  LaneOffs o;
+  if constexpr (!kNibble<FMT>) {
+    constexpr int B = DL < 16 ? DL : 16;
+    o.k = 16 * B * gq + B * n;
+    o.v = o.k;
+    o.ks = o.vs = 16 * gq;  // per-token-head scales of tokens 4gq .. 4gq+3
+  } else {
+    o.k = n * (D / 2) + (DL / 2) * gq;
+    o.v = 2 * D * gq + 4 * ((NV * n) / 2);
+    if constexpr (FMT == 4) {
+      o.ks = n * (D / 16) + (DL * gq) / 16;
+      o.vs = ((NV * n) / 16) * P + 4 * gq;
+    } else if constexpr (FMT == 7) {
+      o.ks = n * (D / 32) + (DL * gq) / 32;
+      o.vs = ((NV * n) / 32) * P + 4 * gq;
+    } else {
+      o.ks = o.vs = 16 * gq;
+    }
+  }
+  return o;
+}
+
+template <int N>
+__device__ __forceinline__ void load_dwords_at(const uint8_t* base, uint32_t off, uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = ld_nt(base + off + 4 * i);
+}
+
 // Issue the loads of unit `sub` (16 tokens) of a chunk.  K: D/4 channels of
 // token row n starting at channel (D/4)*gq; V: channels (D/16)*n .. +D/16 of
 // tokens 4*gq .. 4*gq+3.
 template <int FMT, int D>
-__device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom& g, int P, int sub, int gq, int n,
+__device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom& g, int sub, const LaneOffs& lo,
                                           Raw<FMT, D>& r) {
   constexpr int DL = D / 4;
   constexpr int NV = D / 16;
-  const int tk = sub * 16 + n;
-  const int quad = sub * 4 + gq;
   if constexpr (!kNibble<FMT>) {
     // coalesced 8-bit layout: piece h of all 64 lanes is one contiguous run
     constexpr int B = DL < 16 ? DL : 16;
-    const uint8_t* kp = chunk + (int64_t)16 * D * sub + 16 * B * gq + B * n;
-    const uint8_t* vp = chunk + g.v_codes + (int64_t)16 * D * sub + 16 * B * gq + B * n;
+    const uint8_t* kb = chunk + (int64_t)16 * D * sub;
+    const uint8_t* vb = chunk + g.v_codes + (int64_t)16 * D * sub;
 #pragma unroll
-    for (int h = 0; h < DL / B; ++h) load_dwords<B / 4>(kp + 64 * B * h, r.k + (B / 4) * h);
+    for (int h = 0; h < DL / B; ++h) load_dwords_at<B / 4>(kb + 64 * B * h, lo.k, r.k + (B / 4) * h);
 #pragma unroll
-    for (int h = 0; h < (4 * NV) / B; ++h) load_dwords<B / 4>(vp + 64 * B * h, r.v + (B / 4) * h);
+    for (int h = 0; h < (4 * NV) / B; ++h) load_dwords_at<B / 4>(vb + 64 * B * h, lo.v, r.v + (B / 4) * h);
     if constexpr (FMT == 2 || FMT == 3) {
-      r.ks = ld_nt_f4(chunk + g.k_scales + 4 * (sub * 16 + 4 * gq));
-      r.vs = ld_nt_f4(chunk + g.v_scales + 4 * (sub * 16 + 4 * gq));
+      r.ks = ld_nt_f4(chunk + g.k_scales + 64 * sub + lo.ks);
+      r.vs = ld_nt_f4(chunk + g.v_scales + 64 * sub + lo.vs);
     }
   } else {
-    load_dwords<Raw<FMT, D>::KW>(chunk + (int64_t)tk * (D / 2) + (DL / 2) * gq, r.k);
-    load_dwords<Raw<FMT, D>::VW>(chunk + g.v_codes + (int64_t)2 * D * quad + 4 * ((NV * n) / 2), r.v);
+    load_dwords_at<Raw<FMT, D>::KW>(chunk + (int64_t)sub * 16 * (D / 2), lo.k, r.k);
+    load_dwords_at<Raw<FMT, D>::VW>(chunk + g.v_codes + (int64_t)sub * 8 * D, lo.v, r.v);
     if constexpr (FMT == 4) {
-      const uint8_t* sp = chunk + g.k_scales + (int64_t)tk * (D / 16) + (DL * gq) / 16;
+      const uint8_t* sp = chunk + g.k_scales + sub * 16 * (D / 16) + lo.ks;
       if constexpr (DL >= 32)
         r.ksc = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp));
       else
         r.ksc = __builtin_nontemporal_load(sp);
-      r.vsc = ld_nt(chunk + g.v_scales + (int64_t)((NV * n) / 16) * P + 4 * quad);
+      r.vsc = ld_nt(chunk + g.v_scales + 16 * sub + lo.vs);
     } else if constexpr (FMT == 7) {
       // the lane's D/4 key channels and D/16 value channels each lie in one
       // 32-channel block: one E8M0 byte for the key, one per token for V
-      r.ksc = __builtin_nontemporal_load(chunk + g.k_scales + (int64_t)tk * (D / 32) + (DL * gq) / 32);
-      r.vsc = ld_nt(chunk + g.v_scales + (int64_t)((NV * n) / 32) * P + 4 * quad);
+      r.ksc = __builtin_nontemporal_load(chunk + g.k_scales + sub * 16 * (D / 32) + lo.ks);
+      r.vsc = ld_nt(chunk + g.v_scales + 16 * sub + lo.vs);
     } else {
-      r.ks = ld_nt_f4(chunk + g.k_scales + 4 * (sub * 16 + 4 * gq));
-      r.vs = ld_nt_f4(chunk + g.v_scales + 4 * (sub * 16 + 4 * gq));
+      r.ks = ld_nt_f4(chunk + g.k_scales + 64 * sub + lo.ks);
+      r.vs = ld_nt_f4(chunk + g.v_scales + 64 * sub + lo.vs);
     }
   }
 }
@@ -124,7 +162,9 @@ __device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2
     return cat(as_h2(h[0]), as_h2(h[1]), as_h2(h[2]), as_h2(h[3]));
   } else if constexpr (FMT == 6) {
     // two's-complement nibble ^ 8 = code + 8; under the 0x64 exponent byte it
-    // reads 1032 + code, and subtracting 1032 is exact
+    // reads 1032 + code, and subtracting 1032 is exact.  (Leaving the bias in
+    // the scores, as for INT8, costs too much accuracy here: INT4 scales are
+    // 18x coarser, so the binary32 rounding of the biased sum weighs 18x more.)
     const uint32_t w = r.k[kk] ^ 0x88888888u;
     const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
     const half2_t k1032 = {(half_t)1032.0f, (half_t)1032.0f};
@@ -220,18 +260,24 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     vsc[i] = PTH ? r.vs[i] : 1.0f;
   }
   if (!full) {
+    // a masked token's score becomes -inf and, with per-token value scales,
+    // its scale 0 (its scale slot may hold anything, including a NaN that a
+    // zero weight would not cancel)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (!(valid && tok0 + 4 * gq + i < ctx)) lg[i] = kNegInf;
+      if (!(valid && tok0 + 4 * gq + i < ctx)) {
+        lg[i] = kNegInf;
+        if constexpr (PTH) vsc[i] = 0.0f;
+      }
   }
+  // The reference m_run is always finite (it starts at kRefStart), so a
+  // masked score (-inf) gives exactly 0 without a select.
   float p[4], pv[4];
   bool over = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool live = lg[i] != kNegInf;
-    p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
-    // select, not multiply: a masked token's scale slot may hold anything
-    pv[i] = live ? p[i] * vsc[i] : 0.0f;
+    p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
+    pv[i] = p[i] * vsc[i];
     over |= !(pv[i] <= kTauPow);
   }
   over = over && (n < G);
@@ -241,14 +287,16 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
   // never merged between the branches (which costs a register copy of every
   // accumulator on the common path).
   auto accumulate = [&]() {
-    half4_t ph, plo;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st.l_run += p[i];
-      const half_t hh = (half_t)pv[i];
-      ph[i] = hh;
-      plo[i] = (half_t)(pv[i] - (float)hh);
-    }
+    for (int i = 0; i < 4; ++i) st.l_run += p[i];
+    // P = hi + lo: hi = binary16(P) two at a time, lo = binary16 of the exact
+    // binary32 remainder P - hi (one fused multiply-add from the binary16 hi)
+    const half2_t h01 = __builtin_convertvector(float2_t{pv[0], pv[1]}, half2_t);
+    const half2_t h23 = __builtin_convertvector(float2_t{pv[2], pv[3]}, half2_t);
+    const float2_t r01 = {__builtin_fmaf(-(float)h01[0], 1.0f, pv[0]), __builtin_fmaf(-(float)h01[1], 1.0f, pv[1])};
+    const float2_t r23 = {__builtin_fmaf(-(float)h23[0], 1.0f, pv[2]), __builtin_fmaf(-(float)h23[1], 1.0f, pv[3])};
+    const half4_t ph = cat4(h01, h23);
+    const half4_t plo = cat4(__builtin_convertvector(r01, half2_t), __builtin_convertvector(r23, half2_t));
     // rows G..2G-1 carry the binary16 remainder of rows 0..G-1
     const uint2 lob = __builtin_bit_cast(uint2, plo);
     uint2 shifted;
@@ -303,9 +351,8 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     st.m_run = m_new;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool live = lg[i] != kNegInf;
-      p[i] = live ? __builtin_amdgcn_exp2f(lg[i] - st.m_run) : 0.0f;
-      pv[i] = live ? p[i] * vsc[i] : 0.0f;
+      p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
+      pv[i] = p[i] * vsc[i];
     }
     accumulate();
   } else {
@@ -325,7 +372,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ int s_pages[kPageChunk];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, n = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int P = a.P;
   const int S = a.num_splits;
 
@@ -374,7 +422,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   WaveState<D> st;
 #pragma unroll
   for (int nn = 0; nn < NV; ++nn) st.acc[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
-  st.m_run = kNegInf;
+  st.m_run = kRefStart;
   st.l_run = 0.0f;
 
   // This wave's pages: p_begin + w + 4*j, j < n_it.  Their block-table
@@ -382,6 +430,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // read with readlane, so no load sits between consecutive pages.  Units of
   // 16 tokens are double-buffered: the next unit's bytes are in flight while
   // the current one is computed.
+  const LaneOffs lofs = lane_offsets<FMT, D>(gq, n, P);
   const int sp_shift = a.sp_shift;  // P / 16 == 1 << sp_shift
   const int sp_mask = (1 << sp_shift) - 1;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_pages;
@@ -431,7 +480,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const int up = u + k - (kDepth - 1);    // unit processed now
         const int ls = k;                        // its ring slots
         const int ps = (k + 1) % kDepth;
-        load_unit<FMT, D>(unit_page(ul, vv[ls]), a.geom, P, ul & sp_mask, gq, n, rr[ls]);
+        load_unit<FMT, D>(unit_page(ul, vv[ls]), a.geom, ul & sp_mask, lofs, rr[ls]);
         const bool live = vv[ps] && up >= 0 && up < nu;
         process_unit<FMT, D, G>(rr[ps], live, unit_tok0(up < 0 ? 0 : up), ctx, n, gq, l, qB, kconst, kbias, st);
       }

@@ -22,6 +22,12 @@ constexpr float kNegInf = -INFINITY;
 constexpr float kTau = 8.0f;
 constexpr float kTauPow = 256.0f;
 
+// Starting reference of the running maximum: finite and far below any score
+// (log2 units; scores of binary16 data stay below 2^40 in magnitude), so the
+// first live score always triggers a rescale (its weight overflows to +inf,
+// alpha = 2^(kRefStart - m) = 0) while masked scores (-inf) give weight 0.
+constexpr float kRefStart = -0x1p100f;
+
 __device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d) {
   half8_t r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];

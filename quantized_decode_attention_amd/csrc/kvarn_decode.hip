@@ -448,11 +448,17 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // binary16 tail tokens (original basis), and the rotation back:
 //   M = max(m_s, tail scores), L = sum 2^(m_s-M) l_s + sum_t 2^(s_t-M),
 //   o = ( H sum 2^(m_s-M) o_s + sum_t 2^(s_t-M) v_t ) / L.
-// 128 threads; thread d owns channel d (and tail token d for the scores).
-// The partials are read in one round trip per 8 splits; the inverse rotation
-// runs as six in-wave butterfly stages and one exchange between the waves.
+// 128 threads; for the partials and the output thread d owns channel d.  The
+// partials are read in one round trip per 8 splits; the inverse rotation runs
+// as six in-wave butterfly stages and one exchange between the waves.
+// Tail: thread (row group r = t/16, channel group c = t%16) loads 8 channels
+// (16 bytes) of tail rows r, r+8, ..., r+120 of both K and V, all requests in
+// flight at once; a row's score is the sum over the 16 lanes of its group
+// (in-wave butterflies, which leave it in every lane), and the value sum is
+// reduced over the 8 row groups in LDS.
 __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
-  __shared__ float e_tail[P];
+  constexpr int NR = P / 8;  // tail rows per thread
+  __shared__ float part[8][D];
   __shared__ float xch[D];
   __shared__ float red[2];
   const int kvh = blockIdx.x, b = blockIdx.y, g = blockIdx.z, t = threadIdx.x;
@@ -469,36 +475,46 @@ __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
 
   float ot = 0.0f;
   if (n_tail > 0) {  // uniform across the block
-    // tail scores (log2 units), thread t = tail token t
-    float lg = kNegInf;
-    if (t < n_tail) {
-      const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + t) * D;
-      const uint16_t* qp = a.q + ((int64_t)b * a.Hq + hq) * D;
+    const int r = t >> 4, c = t & 15;
+    const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + r) * D + 8 * c;
+    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P + r) * D + 8 * c;
+    // every row below 128 is inside the tail buffer; rows at or past the
+    // tail length are loaded but carry no weight
+    half8_t kv[NR], vv[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) kv[i] = *reinterpret_cast<const half8_t*>(kt + (int64_t)8 * i * D);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) vv[i] = *reinterpret_cast<const half8_t*>(vt + (int64_t)8 * i * D);
+    const half8_t qv = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)b * a.Hq + hq) * D + 8 * c);
+    float lg[NR];
+    float mloc = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
       float acc = 0.0f;
-      for (int c8 = 0; c8 < D / 8; ++c8) {
-        const half8_t kv = *reinterpret_cast<const half8_t*>(kt + 8 * c8);
-        const half8_t qv = *reinterpret_cast<const half8_t*>(qp + 8 * c8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)kv[e] * (float)qv[e];
-      }
-      lg = acc * a.qk_scale;
+      for (int e = 0; e < 8; ++e) acc += (float)kv[i][e] * (float)qv[e];
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+      lg[i] = r + 8 * i < n_tail ? acc * a.qk_scale : kNegInf;
+      mloc = fmaxf(mloc, lg[i]);
     }
-    const float mt = block_max(lg, red);
-    const float e = t < n_tail ? exp2f(lg - mt) : 0.0f;
-    e_tail[t] = e;
-    const float lt = block_sum(e, red);  // its barriers also publish e_tail
-    // eight independent row loads per iteration (rows below 128 are in the
-    // buffer; rows at or past the tail length carry no weight)
-    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P) * D + t;
+    const float mt = block_max(mloc, red);
+    float lsum = 0.0f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < n_tail; j0 += 8) {
-      half_t vv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) vv[u] = __builtin_bit_cast(half_t, vt[(int64_t)(j0 + u) * D]);
+    for (int i = 0; i < NR; ++i) {
+      const bool live = lg[i] != kNegInf;
+      const float e = live ? exp2f(lg[i] - mt) : 0.0f;
+      lsum += e;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += (j0 + u < n_tail) ? e_tail[j0 + u] * (float)vv[u] : 0.0f;
+      for (int j = 0; j < 8; ++j) acc[j] += live ? e * (float)vv[i][j] : 0.0f;
     }
-    ot = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[r][8 * c + j] = acc[j];
+    // each row's weight is held by all 16 lanes of its group: count it once
+    const float lt = block_sum(c == 0 ? lsum : 0.0f, red);  // its barriers also publish part
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) ot += part[rr][t];
     const float mx = fmaxf(M, mt);
     const float sp = exp2f(M - mx), st = exp2f(mt - mx);
     L = L * sp + lt * st;

@@ -19,6 +19,7 @@ typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
@@ -178,16 +179,18 @@ __device__ __forceinline__ uint32_t e2m1x4_hibytes(uint32_t n) {
 // gfx950 hardware conversions, issued directly: the compiler's lowering of the
 // matching builtins repacks the two binary16 results when they are used one by
 // one (the high half is replaced by a copy of the low half).  With scale 1.0
-// both conversions are exact for every finite code.  The surrounding s_nop
-// covers the one-wait-state forwarding hazard of the scaled conversions on
-// either side, which the compiler cannot see inside an asm statement.
+// both conversions are exact for every finite code.  Each block ends with two
+// wait states: the compiler does not see these instructions' latency inside
+// an asm statement and may otherwise place an MFMA that reads their results
+// too close behind (observed as wrong FP8 products).  Reading their source
+// right after a VALU write needs no wait state (the compiler's own code for
+// the builtins does it back to back).
 // ---------------------------------------------------------------------------
 
 // Eight E2M1 codes (two per byte, low nibble first) -> four binary16 pairs in
 // code order.
 __device__ __forceinline__ void e2m1x8_to_h(uint32_t w, uint32_t (&h)[4]) {
-  asm("s_nop 1\n\t"
-      "v_cvt_scalef32_pk_f16_fp4 %0, %4, 1.0\n\t"
+  asm("v_cvt_scalef32_pk_f16_fp4 %0, %4, 1.0\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %1, %4, 1.0 op_sel:[1,0,0]\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %2, %4, 1.0 op_sel:[0,1,0]\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %3, %4, 1.0 op_sel:[1,1,0]\n\t"
@@ -200,8 +203,7 @@ __device__ __forceinline__ void e2m1x8_to_h(uint32_t w, uint32_t (&h)[4]) {
 // scale's binary32 exponent, so E2M1 value * 2^k comes out exact while it is
 // a binary16 number (k in [-23, 13]).
 __device__ __forceinline__ void e2m1x8_to_h_scaled(uint32_t w, float scale, uint32_t (&h)[4]) {
-  asm("s_nop 1\n\t"
-      "v_cvt_scalef32_pk_f16_fp4 %0, %4, %5\n\t"
+  asm("v_cvt_scalef32_pk_f16_fp4 %0, %4, %5\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %1, %4, %5 op_sel:[1,0,0]\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %2, %4, %5 op_sel:[0,1,0]\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %3, %4, %5 op_sel:[1,1,0]\n\t"
@@ -212,8 +214,7 @@ __device__ __forceinline__ void e2m1x8_to_h_scaled(uint32_t w, float scale, uint
 
 // Byte i of w (two E2M1 codes) with its own power-of-two scale s[i].
 __device__ __forceinline__ void e2m1x8_to_h_scaled4(uint32_t w, const float (&s)[4], uint32_t (&h)[4]) {
-  asm("s_nop 1\n\t"
-      "v_cvt_scalef32_pk_f16_fp4 %0, %4, %5\n\t"
+  asm("v_cvt_scalef32_pk_f16_fp4 %0, %4, %5\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %1, %4, %6 op_sel:[1,0,0]\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %2, %4, %7 op_sel:[0,1,0]\n\t"
       "v_cvt_scalef32_pk_f16_fp4 %3, %4, %8 op_sel:[1,1,0]\n\t"
@@ -228,8 +229,7 @@ __device__ __forceinline__ float e8m0_scale(uint32_t e) { return __uint_as_float
 
 // Four E4M3 codes -> two binary16 pairs in code order.
 __device__ __forceinline__ void e4m3x4_to_h_hw(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  asm("s_nop 1\n\t"
-      "v_cvt_scalef32_pk_f16_fp8 %0, %2, 1.0\n\t"
+  asm("v_cvt_scalef32_pk_f16_fp8 %0, %2, 1.0\n\t"
       "v_cvt_scalef32_pk_f16_fp8 %1, %2, 1.0 op_sel:[1,0,0]\n\t"
       "s_nop 1"
       : "=&v"(lo), "=&v"(hi)
