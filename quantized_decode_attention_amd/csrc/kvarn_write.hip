@@ -24,11 +24,16 @@
 // correctly rounded division and square root), so the codes and metadata are
 // a deterministic function of the binary16 input.
 //
-// Mapping.  One workgroup of 128 threads per (tile, kv head, side).  The tile
-// lives in LDS as binary32 with rows padded to 129 words; in a token pass
-// thread t holds token row t in registers, in a channel pass thread t holds
-// channel column t, so every sum and every division is in-thread and in the
-// canonical order, and both access patterns are free of bank conflicts.
+// Mapping.  One workgroup of 256 threads (4 wavefronts) per (tile, kv head,
+// side).  The tile lives in LDS as binary32 with rows padded to 129 words.
+// Thread (i, half) -- i = 64 * (wave & 1) + lane, half = wave >> 1 -- holds
+// the half [64 half, 64 half + 64) of token row i in a token pass and of
+// channel column i in a channel pass.  A 128-value sum is the canonical tree
+// of its two 64-value halves, S = S(left) + S(right): each thread sums its
+// half in registers and the two halves meet through LDS, so every sum keeps
+// the canonical order.  Within a wavefront the lanes hold 64 consecutive rows
+// (or columns) of one half, so both access patterns are free of bank
+// conflicts.  Two workgroups fit the LDS of a compute unit: 8 wavefronts.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -45,28 +50,46 @@ constexpr float kInvSqrt128 = (float)0.088388347648318440550;  // RN(1/sqrt(128)
 constexpr int kVCodes = 128 * 64;
 constexpr int kMeta = kVCodes + 128 * 32;
 
-// Balanced pairwise sum of 128 values in index order.
-__device__ __forceinline__ float tree_sum(const float (&v)[N]) {
-  float t[N / 2];
+constexpr int H = N / 2;  // values per thread and pass
+
+// Balanced pairwise sum of 64 values in index order (one half of the
+// canonical 128-value tree).
+__device__ __forceinline__ float tree_sum64(const float (&v)[H]) {
+  float t[H / 2];
 #pragma unroll
-  for (int i = 0; i < N / 2; ++i) t[i] = v[2 * i] + v[2 * i + 1];
+  for (int i = 0; i < H / 2; ++i) t[i] = v[2 * i] + v[2 * i + 1];
 #pragma unroll
-  for (int w = N / 4; w >= 1; w >>= 1)
+  for (int w = H / 4; w >= 1; w >>= 1)
 #pragma unroll
     for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
   return t[0];
 }
 
-// Population standard deviation; a zero or non-finite result becomes 1.
-__device__ __forceinline__ float deviation(const float (&v)[N]) {
-  const float mean = tree_sum(v) * 0.0078125f;
-  float sq[N];
+// Workgroup exchange of the two halves' partial results for index i:
+// slot[half][i]; returns the left half's and the right half's values.
+struct Halves {
+  float left, right;
+};
+__device__ __forceinline__ Halves exchange(float* slot, int i, int half, float v) {
+  slot[half * N + i] = v;
+  __syncthreads();
+  const Halves r{slot[i], slot[N + i]};
+  return r;
+}
+
+// Population standard deviation of 128 values (this thread's half v and the
+// partner's); a zero or non-finite result becomes 1.
+__device__ __forceinline__ float deviation(const float (&v)[H], float* xa, float* xb, int i, int half) {
+  const Halves s = exchange(xa, i, half, tree_sum64(v));
+  const float mean = (s.left + s.right) * 0.0078125f;
+  float sq[H];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float d = v[i] - mean;
-    sq[i] = d * d;
+  for (int k = 0; k < H; ++k) {
+    const float d = v[k] - mean;
+    sq[k] = d * d;
   }
-  float sd = __builtin_sqrtf(tree_sum(sq) * 0.0078125f);
+  const Halves q = exchange(xb, i, half, tree_sum64(sq));
+  float sd = __builtin_sqrtf((q.left + q.right) * 0.0078125f);
   if (!(sd > 0.0f) || !__builtin_isfinite(sd)) sd = 1.0f;
   return sd;
 }
@@ -78,88 +101,115 @@ __device__ __forceinline__ float div_rn_z(float x, float s, Recip r) {
 }
 
 // Divide the 128 values by their deviation; returns the deviation.
-__device__ __forceinline__ float normalise(float (&v)[N]) {
-  const float sd = deviation(v);
+__device__ __forceinline__ float normalise(float (&v)[H], float* xa, float* xb, int i, int half) {
+  const float sd = deviation(v, xa, xb, i, half);
   const Recip rc = make_recip(sd);
 #pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = div_rn_z(v[i], sd, rc);
+  for (int k = 0; k < H; ++k) v[k] = div_rn_z(v[k], sd, rc);
   return sd;
 }
 
-__device__ __forceinline__ void rotate(float (&y)[N]) {
+// Butterfly stages h = 1 .. 32 of the rotation, all inside one half.
+__device__ __forceinline__ void rotate_half(float (&y)[H]) {
 #pragma unroll
-  for (int h = 1; h < N; h <<= 1)
+  for (int h = 1; h < H; h <<= 1)
 #pragma unroll
-    for (int j = 0; j < N; ++j)
+    for (int j = 0; j < H; ++j)
       if ((j & h) == 0) {
         const float p = y[j], q = y[j + h];
         y[j] = p + q;
         y[j + h] = p - q;
       }
-#pragma unroll
-  for (int j = 0; j < N; ++j) y[j] = y[j] * kInvSqrt128;
 }
 
-// Asymmetric round-to-nearest of one group of 128 values into `levels` + 1
-// codes (one byte each, written to LDS at codes[stride * i]).  Returns the
-// step; *mn receives the zero point.
+// Asymmetric round-to-nearest of one group of 128 values (this thread's half
+// and the partner's) into LEVELS + 1 codes; this half's codes go to LDS bytes
+// codes[stride * k].  Returns the step; *mn_out receives the zero point.
 template <int LEVELS>
-__device__ __forceinline__ float quantise_group(const float (&y)[N], uint8_t* codes, int stride, float* mn_out) {
+__device__ __forceinline__ float quantise_group(const float (&y)[H], uint8_t* codes, int stride, float* xa,
+                                                float* xb, int i, int half, float* mn_out) {
   float mn = y[0], mx = y[0];
 #pragma unroll
-  for (int i = 1; i < N; ++i) {
-    mn = fminf(mn, y[i]);
-    mx = fmaxf(mx, y[i]);
+  for (int k = 1; k < H; ++k) {
+    mn = fminf(mn, y[k]);
+    mx = fmaxf(mx, y[k]);
   }
+  const Halves a = exchange(xa, i, half, mn);
+  const Halves b = exchange(xb, i, half, mx);
+  mn = fminf(a.left, a.right);
+  mx = fmaxf(b.left, b.right);
   const float s = (mx - mn) / (float)LEVELS;
   const Recip rc = make_recip(s);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    float q = __builtin_rintf(div_rn(y[i] - mn, s, rc));
+  for (int k = 0; k < H; ++k) {
+    float q = __builtin_rintf(div_rn(y[k] - mn, s, rc));
     q = fminf(fmaxf(q, 0.0f), (float)LEVELS);
-    codes[stride * i] = s != 0.0f ? (uint8_t)q : (uint8_t)0;
+    codes[stride * k] = s != 0.0f ? (uint8_t)q : (uint8_t)0;
   }
   *mn_out = mn;
   return s;
 }
 
-// One tile-head side, by the 128 threads of a workgroup: token rows at
-// src + t * row_stride (binary16), codes and metadata into chunk.  `tile` is
-// the workgroup's LDS.
+// One tile-head side, by the 256 threads of a workgroup: token rows at
+// src + t * row_stride (binary16), codes and metadata into chunk.  `lds`
+// holds the tile (N * LDP floats) followed by two exchange arrays (2 * N
+// floats each).
 __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stride, uint8_t* chunk, int side,
-                                           float* tile) {
+                                           float* lds) {
+  float* tile = lds;
+  float* xa = lds + N * LDP;
+  float* xb = xa + 2 * N;
   uint8_t* cb = reinterpret_cast<uint8_t*>(tile);  // codes [token][channel], after the last pass
   const int t = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int i = 64 * (wv & 1) + (t & 63);  // token row / channel column
+  const int half = wv >> 1;
+  const int o = H * half;                  // first value of this half
 
   // stage 1: the tile, binary16 -> binary32 (exact), coalesced 16-byte loads
 #pragma unroll 4
-  for (int k = 0; k < 16; ++k) {
-    const int p = t + 128 * k, row = p >> 4, c8 = (p & 15) * 8;
+  for (int k = 0; k < 8; ++k) {
+    const int p = t + 256 * k, row = p >> 4, c8 = (p & 15) * 8;
     const half8_t x = *reinterpret_cast<const half8_t*>(src + row * row_stride + c8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) tile[row * LDP + c8 + e] = (float)x[e];
   }
   __syncthreads();
 
-  float y[N];
-  float r = 1.0f, c = 1.0f;  // running token factor r_t, channel factor c_t
+  float y[H];
+  float r = 1.0f, c = 1.0f;  // running token factor r_i, channel factor c_i
 #pragma unroll 1
   for (int it = 0; it < kSweeps; ++it) {
-    // token pass (thread t: token row t); stage 2 on the first visit
+    // token pass (token row i, this half); stage 2 on the first visit
 #pragma unroll
-    for (int j = 0; j < N; ++j) y[j] = tile[t * LDP + j];
-    if (it == 0) rotate(y);
-    r = r * normalise(y);
+    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + o + j];
+    if (it == 0) {
+      // stages h = 1 .. 32 in registers, stage 64 across the halves:
+      // (a, b) -> (a + b, a - b) with a in the left half, b in the right
+      rotate_half(y);
 #pragma unroll
-    for (int j = 0; j < N; ++j) tile[t * LDP + j] = y[j];
+      for (int j = 0; j < H; ++j) tile[i * LDP + o + j] = y[j];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const float z = tile[i * LDP + (H - o) + j];
+        y[j] = half == 0 ? y[j] + z : z - y[j];
+      }
+#pragma unroll
+      for (int j = 0; j < H; ++j) y[j] = y[j] * kInvSqrt128;
+      __syncthreads();  // both halves have read their partner's values
+    }
+    r = r * normalise(y, xa, xb, i, half);
+#pragma unroll
+    for (int j = 0; j < H; ++j) tile[i * LDP + o + j] = y[j];
     __syncthreads();
-    // channel pass (thread t: channel column t)
+    // channel pass (channel column i, this half)
 #pragma unroll
-    for (int i = 0; i < N; ++i) y[i] = tile[i * LDP + t];
-    c = c * normalise(y);
+    for (int k = 0; k < H; ++k) y[k] = tile[(o + k) * LDP + i];
+    c = c * normalise(y, xa, xb, i, half);
     if (it + 1 < kSweeps) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) tile[i * LDP + t] = y[i];
+      for (int k = 0; k < H; ++k) tile[(o + k) * LDP + i] = y[k];
       __syncthreads();
     }
   }
@@ -169,15 +219,17 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
     // keys: 4-bit codes per channel over the tile's tokens
     __syncthreads();  // every column has been read: the tile memory is free
     float mn;
-    const float s = quantise_group<15>(y, cb + t, N, &mn);
-    meta[t] = c * s;
-    meta[N + t] = c * mn;
-    meta[2 * N + t] = r;
+    const float s = quantise_group<15>(y, cb + o * N + i, N, xa, xb, i, half, &mn);
+    if (half == 0) {
+      meta[i] = c * s;
+      meta[N + i] = c * mn;
+      meta[2 * N + i] = r;
+    }
     __syncthreads();
     // pack: output byte t*64 + j/2 holds channel j (low nibble) and j+1
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int o0 = 16 * (t + 128 * k);
+    for (int k = 0; k < 2; ++k) {
+      const int o0 = 16 * (t + 256 * k);
       const uint32_t* w = reinterpret_cast<const uint32_t*>(cb + (o0 >> 6) * N + 2 * (o0 & 63));
       uint32_t out[4];
 #pragma unroll
@@ -191,21 +243,22 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
   } else {
     // values: back to token rows, 2-bit codes per token over the channels
 #pragma unroll
-    for (int i = 0; i < N; ++i) tile[i * LDP + t] = y[i];
+    for (int k = 0; k < H; ++k) tile[(o + k) * LDP + i] = y[k];
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < N; ++j) y[j] = tile[t * LDP + j];
+    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + o + j];
     __syncthreads();  // every row has been read: the tile memory is free
     float mn;
-    const float s = quantise_group<3>(y, cb + t * N, 1, &mn);
-    meta[t] = r * s;
-    meta[N + t] = r * mn;
-    meta[2 * N + t] = c;
+    const float s = quantise_group<3>(y, cb + i * N + o, 1, xa, xb, i, half, &mn);
+    if (half == 0) {
+      meta[i] = r * s;
+      meta[N + i] = r * mn;
+      meta[2 * N + i] = c;
+    }
     __syncthreads();
     // pack: output byte 128*(t/4) + j holds token 4*(t/4) + k in bits 2k..2k+1
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int o0 = 16 * (t + 128 * k);
+    {
+      const int o0 = 16 * t;
       const int quad = o0 >> 7, j0 = o0 & 127;
       uint32_t out[4];
 #pragma unroll
@@ -221,15 +274,17 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
   }
 }
 
-__global__ __launch_bounds__(128) void kvarn_write_kernel(WriteArgs a) {
-  __shared__ float tile[N * LDP];
+constexpr int kLdsFloats = N * LDP + 4 * N;
+
+__global__ __launch_bounds__(256) void kvarn_write_kernel(WriteArgs a) {
+  __shared__ float lds[kLdsFloats];
   const int ti = blockIdx.x, h = blockIdx.y, side = blockIdx.z;
   // only the first slot of a tile is read: the tile fills that page in order
   const int64_t s0 = a.slots[(int64_t)ti * N];
   if (s0 < 0 || s0 >= (int64_t)a.num_pages * N) return;
   uint8_t* chunk = a.cache + ((s0 / N) * a.H + h) * a.geom.chunk_bytes;
   const uint16_t* src = (side ? a.v : a.k) + ((int64_t)ti * N * a.H + h) * N;
-  kvarn_tile(src, (int64_t)a.H * N, chunk, side, tile);
+  kvarn_tile(src, (int64_t)a.H * N, chunk, side, lds);
 }
 
 // Incremental path ([P2] §配置与部署: the decode keeps the not yet quantised
@@ -249,8 +304,8 @@ __global__ __launch_bounds__(64) void kvarn_append_kernel(KvarnAppendArgs a) {
 
 // Tile completion: a token at position 127 mod 128 completes its sequence's
 // tile, which is quantised from the tail into the page of that tile.
-__global__ __launch_bounds__(128) void kvarn_complete_kernel(KvarnAppendArgs a) {
-  __shared__ float tile[N * LDP];
+__global__ __launch_bounds__(256) void kvarn_complete_kernel(KvarnAppendArgs a) {
+  __shared__ float lds[kLdsFloats];
   const int64_t i = blockIdx.x;
   const int h = blockIdx.y, side = blockIdx.z;
   const int b = a.seq[i], pos = a.pos[i];
@@ -261,7 +316,7 @@ __global__ __launch_bounds__(128) void kvarn_complete_kernel(KvarnAppendArgs a) 
   if (page < 0 || page >= a.num_pages) return;
   uint8_t* chunk = a.cache + ((int64_t)page * a.H + h) * a.chunk_bytes;
   const uint16_t* src = a.tail + (((int64_t)b * 2 + side) * a.H + h) * N * N;
-  kvarn_tile(src, N, chunk, side, tile);
+  kvarn_tile(src, N, chunk, side, lds);
 }
 
 }  // namespace
@@ -270,7 +325,7 @@ hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s) {
   const int64_t tiles = a.n_tok / N;
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
-  kvarn_write_kernel<<<dim3((unsigned)tiles, (unsigned)a.H, 2u), 128, 0, s>>>(a);
+  kvarn_write_kernel<<<dim3((unsigned)tiles, (unsigned)a.H, 2u), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -280,7 +335,7 @@ hipError_t launch_kvarn_append(const KvarnAppendArgs& a, hipStream_t s) {
   kvarn_append_kernel<<<dim3((unsigned)a.n_tok, (unsigned)(2 * a.H)), 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  kvarn_complete_kernel<<<dim3((unsigned)a.n_tok, (unsigned)a.H, 2u), 128, 0, s>>>(a);
+  kvarn_complete_kernel<<<dim3((unsigned)a.n_tok, (unsigned)a.H, 2u), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
