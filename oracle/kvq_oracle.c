@@ -64,6 +64,9 @@ enum { O_OK = 0, O_BAD_ARG = 1 };
 /* Normalisation sweeps of the KVarN preset (one sweep = token pass, then
  * channel pass). */
 #define KVARN_ITERS 4
+/* One KVarN tile (128 tokens x 128 channels): 4-bit K codes, 2-bit V codes,
+ * 6 x 128 fp32 metadata. */
+#define KVARN_TILE_BYTES (128 * 64 + 128 * 32 + 4 * 6 * 128)
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */
@@ -492,7 +495,9 @@ void kvqo_kvarn_tile(const uint16_t* x16, int64_t stride, int side, float* y_rot
  *    V codes  [P/4][D/2][4] at P*D/2:        byte 2*D*(t/4) + 4*(d/2) + t%4,
  *                                            nibble d%2
  *    K scales fp32 [P] at P*D, V scales fp32 [P] after
- *  KVarN k4v2 (P = D = 128):
+ *  KVarN k4v2 (D = 128, P = 128 or 256): a page holds P/128 tiles of 128
+ *  tokens back to back, KVARN_TILE_BYTES each; tile k holds tokens
+ *  128k .. 128k+127 of the page, t below is the token's offset in its tile:
  *    K codes  [P][D/2] 4-bit at 0:           byte t*D/2 + d/2, nibble d%2
  *    V codes  [P/4][D] 2-bit at P*D/2:       byte D*(t/4) + d, bits 2(t%4)+1..2(t%4)
  *    fp32 K alpha[D], K beta[D], K rho[P], V alpha[P], V beta[P], V gamma[D]
@@ -511,7 +516,7 @@ static int valid_layout(const kvqo_layout* L) {
     case O_MXFP4:
       return D > 0 && D % 32 == 0 && D <= 4096 && P > 0 && P % 16 == 0;
     case O_KVARN_K4V2_G128:
-      return D == 128 && P == 128;
+      return D == 128 && (P == 128 || P == 256);
     default:
       return 0;
   }
@@ -531,7 +536,7 @@ int64_t kvqo_chunk_bytes(const kvqo_layout* L) {
     case O_INT4_PTH: return 2 * (P * D / 2) + 2 * 4 * P;
     case O_NVFP4: return 2 * (P * D / 2) + 2 * (P * D / 16);
     case O_MXFP4: return 2 * (P * D / 2) + 2 * (P * D / 32);
-    case O_KVARN_K4V2_G128: return P * D / 2 + P * D / 4 + 4 * (3 * D + 3 * P);
+    case O_KVARN_K4V2_G128: return (P / 128) * KVARN_TILE_BYTES;
   }
   return -1;
 }
@@ -724,6 +729,8 @@ static void load_row(const kvqo_layout* L, const uint8_t* ch, int t, double* k, 
       break;
     }
     case O_KVARN_K4V2_G128: {
+      ch += (int64_t)(t / 128) * KVARN_TILE_BYTES; /* the token's tile in the page */
+      t %= 128;
       const uint8_t* kc = ch;
       const uint8_t* vc = ch + 128 * 64;
       const float* meta = (const float*)(ch + 128 * 64 + 128 * 32);
@@ -749,7 +756,8 @@ static void load_row(const kvqo_layout* L, const uint8_t* ch, int t, double* k, 
 /* Quantise-on-write: k16, v16 are [n_tok][H][D] binary16; token i goes to
  * slot slots[i] = page * P + offset.  Negative slots and slots past the pool
  * are skipped.  KVarN: n_tok % 128 == 0 and each run of 128 tokens must
- * fill one page in order (slot page*128 + 0..127). */
+ * fill one tile of a page in order (slots s0 + 0..127, s0 a multiple of
+ * 128). */
 int kvqo_quantize_write(const kvqo_layout* L, const uint16_t* k16, const uint16_t* v16,
                         const int64_t* slots, int64_t n_tok, uint8_t* cache) {
   if (!valid_layout(L) || n_tok < 0) return O_BAD_ARG;
@@ -768,9 +776,9 @@ int kvqo_quantize_write(const kvqo_layout* L, const uint16_t* k16, const uint16_
       if (s0 % 128) { free(codes); return O_BAD_ARG; }
       for (int t = 1; t < 128; t++)
         if (slots[tile * 128 + t] != s0 + t) { free(codes); return O_BAD_ARG; }
-      int64_t page = s0 / 128;
+      int64_t page = s0 / P;
       for (int h = 0; h < H; h++) {
-        uint8_t* ch = chunk_at(L, cache, page, h);
+        uint8_t* ch = chunk_at(L, cache, page, h) + (s0 % P) / 128 * KVARN_TILE_BYTES;
         const int64_t row0 = (tile * 128 * H + h) * (int64_t)D;
         float* mbase = (float*)(ch + 128 * 64 + 128 * 32);
         /* keys */

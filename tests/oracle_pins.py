@@ -508,6 +508,13 @@ def pin_layout_bijective(O, rng=None):
     w = _written_nibbles(O, lay, k, v, 128 + np.arange(128))
     half = w.size // 2
     assert not np.any(w[:half]) and np.all(w[half:])
+    # two tiles per page: each owns its own bytes, together they cover page 1
+    lay = oracle.layout(oracle.KVARN_K4V2_G128, 2, 128, 256, 2)
+    w0 = _written_nibbles(O, lay, k, v, 256 + np.arange(128))
+    w1 = _written_nibbles(O, lay, k, v, 384 + np.arange(128))
+    half = w0.size // 2
+    assert not np.any(w0 & w1)
+    assert not np.any(w0[:half] | w1[:half]) and np.all((w0 | w1)[half:])
 
 
 # --------------------------------------------------------------------------- #
@@ -651,11 +658,50 @@ def pin_attention(O, rng=None):
         assert np.allclose(out[0, h], h // (Hq // H) + 1, rtol=1e-6)
 
 
+def pin_kvarn_pages(O, rng=None):
+    """Pages of 256 tokens hold two independent 128-token tiles: their bytes
+    are exactly the bytes of the same tokens written as two 128-token pages,
+    placed back to back in each (page, head) chunk."""
+    rng = rng or np.random.default_rng(14)
+    H, D = 2, 128
+    k = workloads.random_halves(rng, (256, H, D))
+    v = workloads.random_halves(rng, (256, H, D), 2.0)
+    l256 = oracle.layout(oracle.KVARN_K4V2_G128, H, D, 256, 2)
+    l128 = oracle.layout(oracle.KVARN_K4V2_G128, H, D, 128, 2)
+    tb = O.chunk_bytes(l128)
+    assert O.chunk_bytes(l256) == 2 * tb
+    c256 = O.quantize_write(l256, k, v, 256 + np.arange(256))  # page 1
+    c128 = O.quantize_write(l128, k, v, np.arange(256))        # pages 0 and 1
+    pb = O.page_bytes(l256)
+    assert not np.any(c256[:pb])
+    for h in range(H):
+        for tile in range(2):
+            got = c256[pb + h * 2 * tb + tile * tb:pb + h * 2 * tb + (tile + 1) * tb]
+            want = c128[tile * H * tb + h * tb:tile * H * tb + (h + 1) * tb]
+            assert np.array_equal(got, want), (h, tile)
+    # and read back as the same values
+    k2, v2 = O.dequantize(l256, c256, 256 + np.arange(256))
+    k1, v1 = O.dequantize(l128, c128, np.arange(256))
+    assert np.array_equal(k2, k1) and np.array_equal(v2, v1)
+    # a tile must start on a multiple of 128 inside the page
+    try:
+        O.quantize_write(l256, k[:128], v[:128], 256 + 64 + np.arange(128))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a tile starting mid-page must be refused")
+
+
 def pin_attention_kvarn(O, rng=None):
     rng = rng or np.random.default_rng(11)
-    B, H, Hq, D, P = 2, 2, 4, 128, 128
-    ctx = np.array([256 + 37, 128], np.int32)
-    maxp = 3
+    for P in (128, 256):
+        _attention_kvarn_case(O, rng, P)
+
+
+def _attention_kvarn_case(O, rng, P):
+    B, H, Hq, D = 2, 2, 4, 128
+    ctx = np.array([256 + 37, 128], np.int32) if P == 128 else np.array([512 + 128 + 37, 384], np.int32)
+    maxp = int(-(-ctx.max() // P))
     bt = rng.permutation(B * maxp).astype(np.int32).reshape(B, maxp)
     lay = oracle.layout(oracle.KVARN_K4V2_G128, H, D, P, B * maxp)
     cache = np.zeros(lay.num_pages * O.page_bytes(lay), np.uint8)
@@ -688,5 +734,5 @@ def pin_attention_kvarn(O, rng=None):
 ALL_PINS = [
     pin_half_widening, pin_e4m3_decode, pin_e4m3_encode, pin_e2m1_encode, pin_int8_pth, pin_int4_pth, pin_fp8_pth,
     pin_fp8_pt, pin_nvfp4, pin_mxfp4, pin_page_bytes, pin_glossary_bytes, pin_layout_bijective, pin_kvarn_rotation,
-    pin_kvarn_tile, pin_attention, pin_attention_kvarn,
+    pin_kvarn_tile, pin_kvarn_pages, pin_attention, pin_attention_kvarn,
 ]

@@ -55,6 +55,9 @@ MUTANTS = [
      [pins.pin_mxfp4, pins.pin_layout_bijective]),
     ("mxfp4_decode_scale_block_16", "(int)ks[(int64_t)t * (D / 32) + d / 32] - 127",
      "(int)ks[(int64_t)t * (D / 32) + d / 16 % (D / 32)] - 127", 0, [pins.pin_mxfp4]),
+    ("kvarn_second_tile_over_first", "uint8_t* ch = chunk_at(L, cache, page, h) + (s0 % P) / 128 * KVARN_TILE_BYTES;",
+     "uint8_t* ch = chunk_at(L, cache, page, h);", 0, [pins.pin_kvarn_pages, pins.pin_layout_bijective]),
+    ("kvarn_read_first_tile", "ch += (int64_t)(t / 128) * KVARN_TILE_BYTES;", "(void)0;", 0, [pins.pin_kvarn_pages]),
     ("chunk_head_major", "return (uint8_t*)cache + (page * L->num_kv_heads + h) * kvqo_chunk_bytes(L);",
      "return (uint8_t*)cache + ((int64_t)h * L->num_pages + page) * kvqo_chunk_bytes(L);", 0,
      [pins.pin_layout_bijective]),
