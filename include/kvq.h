@@ -46,10 +46,13 @@
  *     K codes  [P][D/2]     at 0         byte t*D/2 + d/2
  *     V codes  [P/4][D/2][4] at P*D/2    byte 2*D*(t/4) + 4*(d/2) + t%4
  *     K scales fp32 [P] at P*D, then V scales fp32 [P]
- *   KVarN k4v2 g128 (P = D = 128):
- *     K codes 4-bit [P][D/2] at 0        byte t*D/2 + d/2, low nibble = even d
- *     V codes 2-bit [P/4][D] at P*D/2    byte D*(t/4) + d, bits 2(t%4)+1..2(t%4)
- *     fp32 K alpha[D], K beta[D], K rho[P], V alpha[P], V beta[P], V gamma[D]
+ *   KVarN k4v2 g128 (D = 128, P = 128 or 256): the chunk holds P/128 tiles
+ *   of 128 tokens back to back, 15360 bytes each; tile k holds the page's
+ *   tokens 128k .. 128k+127 and t below is a token's offset in its tile
+ *   (T = 128):
+ *     K codes 4-bit [T][D/2] at 0        byte t*D/2 + d/2, low nibble = even d
+ *     V codes 2-bit [T/4][D] at T*D/2    byte D*(t/4) + d, bits 2(t%4)+1..2(t%4)
+ *     fp32 K alpha[D], K beta[D], K rho[T], V alpha[T], V beta[T], V gamma[D]
  *     (rotated tile rebuilt as K = rho_t (alpha_d code + beta_d),
  *      V = gamma_d (alpha_t code + beta_t); see kvq_quantize_write)
  *   Codes: INT8 = two's-complement byte; FP8 = OCP E4M3 ("fn", max 448);
@@ -100,7 +103,8 @@ typedef enum {
  *   flags        KVQ_FLAG_* (only KVQ_FLAG_NVFP4_4OVER6, NVFP4 only)
  *   num_kv_heads H, >= 1
  *   head_dim     D: 32, 64 or 128 (KVarN: 128)
- *   page_size    P tokens per page: 16, 32, 64, 128 or 256 (KVarN: 128, one tile)
+ *   page_size    P tokens per page: 16, 32, 64, 128 or 256 (KVarN: 128 or 256,
+ *                i.e. one or two 128-token tiles)
  *   num_pages    pages in the pool, >= 1
  *   k_scale, v_scale  FP8 per-tensor: the layer's K and V scales (divide on
  *                write, multiply on read; [P4] §写和读).  NVFP4: the per-layer
@@ -160,8 +164,10 @@ kvq_status kvq_check_device(int hip_device);
  *                     channel over the tile's tokens; V: 2-bit per token over
  *                     channels), scales folded into the metadata above.
  *                     Requires n_tok % 128 == 0; tokens 128i..128i+127 must
- *                     map to slots page*128 + 0..127 of one page (only the
- *                     first slot of each tile is read).
+ *                     map to slots s0 + 0..127 of one tile of a page, s0 a
+ *                     multiple of 128 (only the first slot of each tile is
+ *                     read; a first slot off a multiple of 128 skips the
+ *                     tile).
  * Errors: KVQ_ERR_INVALID_ARG for NULL pointers, n_tok < 0, bad scales or a
  * KVarN n_tok not a multiple of 128; KVQ_ERR_UNSUPPORTED for layouts outside
  * the list above; KVQ_ERR_DEVICE off gfx950. */
@@ -182,8 +188,8 @@ kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const voi
  *   block_tables  int32 [batch][max_pages_per_seq] as for decode.
  *   cache         the paged cache.
  * A token at position 127 mod 128 completes its tile: rows 0..127 of the
- * sequence's tail are then quantised into page
- * block_tables[seq][pos / 128], with exactly the bytes kvq_quantize_write
+ * sequence's tail are then quantised into tile (pos / 128) % (P / 128) of
+ * page block_tables[seq][pos / P], with exactly the bytes kvq_quantize_write
  * gives for those 128 tokens.  Within one call, the tokens of a sequence must
  * lie in one tile and have distinct positions (a token of the next tile would
  * overwrite a tail row before the tile is quantised); entries with a sequence

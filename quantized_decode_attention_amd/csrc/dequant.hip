@@ -102,10 +102,11 @@ __global__ __launch_bounds__(128) void dequant_kvarn_kernel(WriteArgs a, float* 
   const int h = (int)(row - tok * a.H);
   const int j = threadIdx.x;
   const int64_t slot = a.slots[tok];
-  if (slot < 0 || slot >= (int64_t)a.num_pages * 128) return;
-  const int64_t page = slot / 128;
-  const int t = (int)(slot - page * 128);
-  const uint8_t* chunk = a.cache + (page * a.H + h) * a.geom.chunk_bytes;
+  if (slot < 0 || slot >= (int64_t)a.num_pages * a.P) return;
+  const int64_t page = slot / a.P;
+  const int tp = (int)(slot - page * a.P);  // token in the page: tile tp / 128, row t
+  const int t = tp & 127;
+  const uint8_t* chunk = a.cache + (page * a.H + h) * a.geom.chunk_bytes + (int64_t)(tp >> 7) * (a.geom.chunk_bytes / (a.P / 128));
   const float* meta = reinterpret_cast<const float*>(chunk + a.geom.k_scales);
   const uint32_t kb = chunk[t * 64 + j / 2];
   const uint32_t kc = (j & 1) ? kb >> 4 : kb & 15u;

@@ -37,6 +37,8 @@ constexpr int kRing = 4;  // sub-page buffers per wave (kRing - 1 in flight)
 constexpr int kVCodes = P * D / 2;          // V codes [32][128] 2-bit
 constexpr int kMeta = kVCodes + P * D / 4;  // binary32 metadata
 constexpr int kMetaFloats = 3 * D + 3 * P;
+constexpr int kTileBytes = kMeta + 4 * kMetaFloats;  // 15360; a page of a.P tokens holds a.P / 128 tiles
+static_assert(kTileBytes == 15360, "KVarN tile size");
 // metadata vectors (float offsets)
 constexpr int kKa = 0, kKb = 128, kKr = 256, kVa = 384, kVb = 512, kVg = 640;
 constexpr float kInvSqrt128 = (float)0.088388347648318440550;  // RN(1/sqrt(128))
@@ -212,7 +214,9 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   const int64_t rec_floats = ws_record_floats(D);
 
   int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
-  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
+  // the walk is over 128-token tiles; a page of a.P tokens holds a.P / 128
+  const int tshift = a.P == 256 ? 1 : 0;
   const int n_pages = ctx / P;  // complete tiles; the rest is the caller's tail
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(p_begin + a.pages_per_split, n_pages);
@@ -260,14 +264,15 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   for (int c0 = p_begin; c0 < p_end; c0 += kPageChunk) {
     const int nc = min(kPageChunk, p_end - c0);
     __syncthreads();
-    for (int i = tid; i < nc; i += 256) s_pages[i] = bt[c0 + i];
+    for (int i = tid; i < nc; i += 256) s_pages[i] = bt[(c0 + i) >> tshift];
     __syncthreads();
     const int nj = w < nc ? (nc - w + kWaves - 1) / kWaves : 0;
     if (nj == 0) continue;
     auto page_ptr = [&](int j, bool& valid) {
       const int page = __builtin_amdgcn_readfirstlane(s_pages[w + kWaves * j]);
+      const int sub = (c0 + w + kWaves * j) & ((1 << tshift) - 1);  // tile within the page
       valid = page >= 0 && page < a.num_pages;
-      return head_base + (valid ? page : 0) * page_stride;
+      return head_base + (valid ? page : 0) * page_stride + (valid ? sub : 0) * kTileBytes;
     };
     // the current page's metadata travels with its first sub-page: both are
     // requested while the previous page's last sub-page is computed
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
   const int64_t rf = ws_record_floats(D);
   const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
   int ctx = a.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
   const int n_tail = a.tail ? ctx % P : 0;
   const int hq = kvh * a.G + g;
 

@@ -49,6 +49,8 @@ constexpr float kInvSqrt128 = (float)0.088388347648318440550;  // RN(1/sqrt(128)
 // then binary32 metadata K alpha, K beta, K rho, V alpha, V beta, V gamma.
 constexpr int kVCodes = 128 * 64;
 constexpr int kMeta = kVCodes + 128 * 32;
+constexpr int kTileBytes = kMeta + 4 * 6 * 128;  // 15360; a page of P tokens holds P / 128 tiles
+static_assert(kTileBytes == 15360, "KVarN tile size");
 
 constexpr int H = N / 2;  // values per thread and pass
 
@@ -279,10 +281,12 @@ constexpr int kLdsFloats = N * LDP + 4 * N;
 __global__ __launch_bounds__(256) void kvarn_write_kernel(WriteArgs a) {
   __shared__ float lds[kLdsFloats];
   const int ti = blockIdx.x, h = blockIdx.y, side = blockIdx.z;
-  // only the first slot of a tile is read: the tile fills that page in order
+  // only the first slot of a tile is read: the tile fills one tile of its
+  // page in order (a first slot off a multiple of 128 is skipped)
   const int64_t s0 = a.slots[(int64_t)ti * N];
-  if (s0 < 0 || s0 >= (int64_t)a.num_pages * N) return;
-  uint8_t* chunk = a.cache + ((s0 / N) * a.H + h) * a.geom.chunk_bytes;
+  if (s0 < 0 || s0 >= (int64_t)a.num_pages * a.P || s0 % N != 0) return;
+  const int64_t page = s0 / a.P;
+  uint8_t* chunk = a.cache + (page * a.H + h) * a.geom.chunk_bytes + (s0 - page * a.P) / N * kTileBytes;
   const uint16_t* src = (side ? a.v : a.k) + ((int64_t)ti * N * a.H + h) * N;
   kvarn_tile(src, (int64_t)a.H * N, chunk, side, lds);
 }
@@ -310,11 +314,12 @@ __global__ __launch_bounds__(256) void kvarn_complete_kernel(KvarnAppendArgs a) 
   const int h = blockIdx.y, side = blockIdx.z;
   const int b = a.seq[i], pos = a.pos[i];
   if (b < 0 || b >= a.batch || pos < 0 || (pos & (N - 1)) != N - 1) return;
-  const int pi = pos / N;
-  if (pi >= a.max_pages) return;
-  const int page = a.block_tables[(int64_t)b * a.max_pages + pi];
+  const int ti = pos / N;  // tile index in the sequence
+  const int tpp = a.P / N;  // tiles per page
+  if (ti / tpp >= a.max_pages) return;
+  const int page = a.block_tables[(int64_t)b * a.max_pages + ti / tpp];
   if (page < 0 || page >= a.num_pages) return;
-  uint8_t* chunk = a.cache + ((int64_t)page * a.H + h) * a.chunk_bytes;
+  uint8_t* chunk = a.cache + ((int64_t)page * a.H + h) * a.chunk_bytes + (ti % tpp) * kTileBytes;
   const uint16_t* src = a.tail + (((int64_t)b * 2 + side) * a.H + h) * N * N;
   kvarn_tile(src, N, chunk, side, lds);
 }

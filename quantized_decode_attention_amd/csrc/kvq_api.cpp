@@ -31,7 +31,7 @@ kvq_status check_layout(const kvq_layout* L) {
       if (L->page_size < 16 || L->page_size > 256 || (L->page_size & (L->page_size - 1))) return KVQ_ERR_UNSUPPORTED;
       break;
     case KVQ_KVARN_K4V2_G128:
-      if (L->head_dim != 128 || L->page_size != 128) return KVQ_ERR_UNSUPPORTED;
+      if (L->head_dim != 128 || (L->page_size != 128 && L->page_size != 256)) return KVQ_ERR_UNSUPPORTED;
       break;
     default:
       return KVQ_ERR_UNSUPPORTED;
@@ -78,12 +78,15 @@ ChunkGeom geometry(const kvq_layout* L) {
       g.v_scales = P * D + P * D / 32;
       g.chunk_bytes = P * D + P * D / 16;
       break;
-    case KVQ_KVARN_K4V2_G128:
-      g.v_codes = P * D / 2;
-      g.k_scales = P * D / 2 + P * D / 4;  // start of the fp32 metadata
-      g.v_scales = g.k_scales + 4 * (2 * D + P);
-      g.chunk_bytes = P * D / 2 + P * D / 4 + 4 * (3 * D + 3 * P);
+    case KVQ_KVARN_K4V2_G128: {
+      // P / 128 tiles back to back; offsets inside one tile
+      constexpr int64_t T = 128;
+      g.v_codes = T * D / 2;
+      g.k_scales = T * D / 2 + T * D / 4;  // start of the fp32 metadata
+      g.v_scales = g.k_scales + 4 * (2 * D + T);
+      g.chunk_bytes = (P / T) * (T * D / 2 + T * D / 4 + 4 * (3 * D + 3 * T));
       break;
+    }
   }
   return g;
 }
@@ -175,6 +178,12 @@ void plan_splits(int batch, int H, int max_pages, int hint, int64_t target, int*
   if (*splits < 1) *splits = 1;
 }
 
+// The split kernel's unit of work along the context: a page, or for KVarN a
+// 128-token tile (a page holds page_size / 128 of them).
+int plan_units(const kvq_layout* L, int max_pages) {
+  return L->format == KVQ_KVARN_K4V2_G128 ? max_pages * (L->page_size / 128) : max_pages;
+}
+
 int64_t workspace_bytes_for(const kvq_layout* L, int batch, int splits) {
   if (splits <= 1 && L->format != KVQ_KVARN_K4V2_G128) return 0;
   return (int64_t)batch * L->num_kv_heads * splits * ws_record_floats(L->head_dim) * 4;
@@ -241,6 +250,7 @@ kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void*
   a.max_pages = max_pages_per_seq;
   a.cache = static_cast<uint8_t*>(cache);
   a.chunk_bytes = geometry(layout).chunk_bytes;
+  a.P = layout->page_size;
   a.H = layout->num_kv_heads;
   a.num_pages = layout->num_pages;
   return from_hip(launch_kvarn_append(a, static_cast<hipStream_t>(stream)));
@@ -252,7 +262,7 @@ int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t n
       num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return -1;
   int s, pps;
-  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits,
+  plan_splits(batch, layout->num_kv_heads, plan_units(layout, max_pages_per_seq), num_splits,
               target_workgroups(layout, num_q_heads / layout->num_kv_heads), &s, &pps);
   return s;
 }
@@ -263,7 +273,7 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int3
       num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return -1;
   int s, pps;
-  plan_splits(batch, layout->num_kv_heads, max_pages_per_seq, num_splits,
+  plan_splits(batch, layout->num_kv_heads, plan_units(layout, max_pages_per_seq), num_splits,
               target_workgroups(layout, num_q_heads / layout->num_kv_heads), &s, &pps);
   return workspace_bytes_for(layout, batch, s);
 }
@@ -284,7 +294,8 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
   if (kvarn_tail && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
   if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
   int splits, pps;
-  plan_splits(batch, H, max_pages_per_seq, num_splits, target_workgroups(layout, G), &splits, &pps);
+  plan_splits(batch, H, plan_units(layout, max_pages_per_seq), num_splits, target_workgroups(layout, G), &splits,
+              &pps);
   const int64_t need = workspace_bytes_for(layout, batch, splits);
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;

@@ -68,6 +68,7 @@ struct KvarnAppendArgs {
   uint8_t* cache;
   int64_t chunk_bytes;
   int H, num_pages;
+  int P;  // page size: 128 or 256 tokens, i.e. 1 or 2 tiles
 };
 
 hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s);

@@ -34,6 +34,7 @@ def _layouts():
                 yield fmt, 0, 3, D, P
     yield 4, 1, 8, 128, 16
     yield 5, 0, 8, 128, 128
+    yield 5, 0, 8, 128, 256
 
 
 @pytest.mark.parametrize("fmt,flags,H,D,P", list(_layouts()))
@@ -45,7 +46,7 @@ def test_page_bytes_match_oracle(K, fmt, flags, H, D, P):
 
 @pytest.mark.parametrize("bad", [
     dict(fmt=0), dict(fmt=8), dict(fmt=7, flags=1), dict(D=96), dict(D=256), dict(P=8), dict(P=24), dict(P=48), dict(P=512), dict(H=0),
-    dict(pages=0), dict(fmt=5, P=16), dict(fmt=5, D=64), dict(flags=1), dict(flags=2, fmt=4),
+    dict(pages=0), dict(fmt=5, P=16), dict(fmt=5, P=64), dict(fmt=5, D=64), dict(flags=1), dict(flags=2, fmt=4),
     dict(fmt=1, ks=0.0), dict(fmt=1, ks=float("inf")), dict(fmt=4, vs=-1.0), dict(fmt=4, vs=1e-30),
 ])
 def test_invalid_layouts_rejected(K, bad):
