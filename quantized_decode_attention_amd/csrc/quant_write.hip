@@ -76,14 +76,30 @@ __device__ __forceinline__ float row_scale(float amax) {
   return fmaxf(amax, 1e-8f) / (FMT == 2 ? 127.0f : 448.0f);
 }
 
+// Four codes of x[0..3] packed into a dword (code i in byte i).  INT8:
+// clip(rne(x / s)).  E4M3: x / s, its sign forced to x's (a zero quotient of
+// -0 keeps its sign), clamped to +-448 (saturation), then gfx950's packed
+// binary32 -> E4M3 conversion, which rounds to nearest even like the
+// encoder's definition for every |y| <= 448 (checked code by code in
+// tests/test_gpu_probes.py).
 template <int FMT>
-__device__ __forceinline__ uint32_t encode8(float x, float s, Recip rc) {
-  const float y = div_rn(x, s, rc);
+__device__ __forceinline__ uint32_t encode8x4(const float* x, float s, Recip rc) {
   if constexpr (FMT == 2) {
-    const float q = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
-    return (uint32_t)(int32_t)q & 0xFFu;
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q = fminf(fmaxf(__builtin_rintf(div_rn(x[i], s, rc)), -127.0f), 127.0f);
+      w |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * i);
+    }
+    return w;
   } else {
-    return e4m3_mag(fabsf(y)) | (sign_bit(x) << 7);
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      y[i] = __builtin_amdgcn_fmed3f(__builtin_copysignf(div_rn(x[i], s, rc), x[i]), -448.0f, 448.0f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+    return (uint32_t)r;
   }
 }
 
@@ -107,21 +123,19 @@ __device__ __forceinline__ void write_row_8bit(const WriteArgs& a, int64_t row, 
     s = row_scale<FMT>(group_max<LPR>(amax));
   }
   const Recip rc = make_recip(s);
-  uint32_t code[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) code[i] = encode8<FMT>(x[i], s, rc);
+  uint2 packed;
+  packed.x = encode8x4<FMT>(x, s, rc);
+  packed.y = encode8x4<FMT>(x + 4, s, rc);
 
   // 16-token groups of K and V are laid out in the decode's operand order
   // (see k8_offset / v8_offset)
   if (c.side == 0) {
-    uint2 packed;
-    packed.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-    packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
     *reinterpret_cast<uint2*>(c.chunk + k8_offset<D>(c.t, 8 * j)) = packed;
   } else {
     uint8_t* vp = c.chunk + a.geom.v_codes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vp[v8_offset<D>(c.t, 8 * j + i)] = (uint8_t)code[i];
+    for (int i = 0; i < 8; ++i)
+      vp[v8_offset<D>(c.t, 8 * j + i)] = (uint8_t)((i < 4 ? packed.x : packed.y) >> (8 * (i & 3)));
   }
   if (FMT != 1 && j == 0) {
     float* sp = reinterpret_cast<float*>(c.chunk + a.geom.k_scales) + c.side * a.P + c.t;
@@ -200,11 +214,19 @@ __global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
     }
     const Recip rc = make_recip(s);
     uint8_t* dst = s_codes[side];
+    uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 16 * q + i;
-      const int off = side == 0 ? (int)k8_offset<D>(sidx, d) : (int)v8_offset<D>(sidx, d);
-      dst[off] = (uint8_t)encode8<FMT>(x[i], s, rc);
+    for (int k = 0; k < 4; ++k) w[k] = encode8x4<FMT>(x + 4 * k, s, rc);
+    if (side == 0 && D >= 64) {
+      // channels 16q .. 16q+15 of a key row are 16 consecutive bytes
+      *reinterpret_cast<uint4*>(dst + k8_offset<D>(sidx, 16 * q)) = uint4{w[0], w[1], w[2], w[3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 16 * q + i;
+        const int off = side == 0 ? (int)k8_offset<D>(sidx, d) : (int)v8_offset<D>(sidx, d);
+        dst[off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+      }
     }
   }
   __syncthreads();
@@ -226,35 +248,60 @@ __global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
 // NVFP4 ([P5] §双层缩放怎样恢复动态范围): one lane per 16-value block.
 // ---------------------------------------------------------------------------
 
+// Sixteen E2M1 codes of y[0..15] (already divided by the block divisor)
+// with gfx950's scaled packed conversion at scale 1, which rounds to the
+// nearest value with ties to the even code and saturates at 6 like the
+// encoder's definition (checked nibble by nibble in tests/test_gpu_probes.py):
+// byte i of the result holds values 2i (low nibble) and 2i+1.
+__device__ __forceinline__ void e2m1_encode16(const float* y, uint32_t (&w)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float* p = y + 8 * h;
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[0], p[1], 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[2], p[3], 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[4], p[5], 1.0f, 2);
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[6], p[7], 1.0f, 3);
+  }
+}
+
 // Codes of one block for block-scale code sb, with the squared reconstruction
-// error summed by the balanced tree over the block's index order.
-__device__ __forceinline__ float nvfp4_block(const float* x, float st, uint32_t sb, uint32_t* code) {
+// error summed by the balanced tree over the block's index order.  The
+// quotients keep x's sign on zero; the reconstructions come back exactly
+// through the hardware E2M1 -> binary16 conversion.
+__device__ __forceinline__ float nvfp4_block(const float* x, float st, uint32_t sb, uint32_t (&w)[2]) {
   const float sbv = e4m3_val(sb);
   float e2[16];
   if (sbv == 0.0f) {
+    w[0] = w[1] = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      code[i] = 0;
-      e2[i] = x[i] * x[i];
-    }
+    for (int i = 0; i < 16; ++i) e2[i] = x[i] * x[i];
   } else {
     const float d = st * sbv;
     const Recip rc = make_recip(d);
+    float y[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float y = div_rn(x[i], d, rc);
-      const uint32_t m = e2m1_mag(fabsf(y));
-      const uint32_t sgn = sign_bit(x[i]);
-      code[i] = m | (sgn << 3);
-      const float v = sgn ? -e2m1_val(m) : e2m1_val(m);
-      const float e = x[i] - d * v;
-      e2[i] = e * e;
+    for (int i = 0; i < 16; ++i) y[i] = __builtin_copysignf(div_rn(x[i], d, rc), x[i]);
+    e2m1_encode16(y, w);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t v[4];
+      e2m1x8_to_h(w[h], v);  // values 8h .. 8h+7 in order
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const half2_t pr = as_h2(v[k]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 8 * h + 2 * k + e;
+          const float err = x[i] - d * (float)pr[e];
+          e2[i] = err * err;
+        }
+      }
     }
   }
 #pragma unroll
-  for (int w = 1; w < 16; w <<= 1)
+  for (int wd = 1; wd < 16; wd <<= 1)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2 * w) e2[i] = e2[i] + e2[i + w];
+    for (int i = 0; i < 16; i += 2 * wd) e2[i] = e2[i] + e2[i + wd];
   return e2[0];
 }
 
@@ -267,20 +314,20 @@ __device__ __forceinline__ uint32_t nvfp4_encode_block(const float* x, float st,
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
   uint32_t sb = e4m3_mag((amax / 6.0f) / st);
-  uint32_t code[16];
-  const float err6 = nvfp4_block(x, st, sb, code);
+  uint32_t w[2];
+  const float err6 = nvfp4_block(x, st, sb, w);
   if (flags & 1) {
     const uint32_t sb4 = e4m3_mag((amax / 4.0f) / st);
-    uint32_t code4[16];
-    const float err4 = nvfp4_block(x, st, sb4, code4);
+    uint32_t w4[2];
+    const float err4 = nvfp4_block(x, st, sb4, w4);
     if (err4 < err6) {
       sb = sb4;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = code4[i];
+      w[0] = w4[0];
+      w[1] = w4[1];
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) byte[i] = code[2 * i] | (code[2 * i + 1] << 4);
+  for (int i = 0; i < 8; ++i) byte[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
   return sb;
 }
 
@@ -321,11 +368,13 @@ __device__ __forceinline__ uint32_t mxfp4_encode_half(const float* x, uint32_t* 
   amax = group_max<2>(amax);
   const uint32_t field = __float_as_uint(amax) >> 23;
   const float inv = amax > 0.0f ? __uint_as_float((256u - field) << 23) : 1.0f;
-  uint32_t code[16];
+  float y[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) code[i] = e2m1_mag(fabsf(x[i] * inv)) | (sign_bit(x[i]) << 3);
+  for (int i = 0; i < 16; ++i) y[i] = x[i] * inv;  // exact, sign kept on zero
+  uint32_t w[2];
+  e2m1_encode16(y, w);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) byte[i] = code[2 * i] | (code[2 * i + 1] << 4);
+  for (int i = 0; i < 8; ++i) byte[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
   return amax > 0.0f ? field - 2u : 0u;
 }
 

@@ -24,6 +24,30 @@ __global__ void k_cvt_f32_fp4(const float* x, int64_t n, uint8_t* out) {
   out[i] = (uint8_t)(r & 0xF);
 }
 
+// Pairs (x[2i], x[2i+1]) -> E4M3 with the packed conversion into both words
+// of one dword, as an encoder would pack four values: out[i] holds pair 2i
+// in bytes 0-1 and pair 2i+1 in bytes 2-3.
+__global__ void k_cvt_f32_fp8_pairs(const float* x, int64_t n4, uint32_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i], x[4 * i + 1], 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i + 2], x[4 * i + 3], r, true);
+  out[i] = (uint32_t)r;
+}
+
+// Eight values -> E2M1 nibbles with the scaled packed conversion (scale 1),
+// value 2k in the low nibble of byte k, as an encoder would pack them.
+__global__ void k_cvt_f32_fp4_x8(const float* x, int64_t n8, uint32_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const float* p = x + 8 * i;
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[0], p[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[2], p[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[4], p[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[6], p[7], 1.0f, 3);
+  out[i] = r;
+}
+
 // E2M1 pairs -> binary16, issued directly as the library does (the
 // compiler's lowering of the builtin repacks the two results when they are
 // used one by one), byte selector k = 0..3.
@@ -92,6 +116,16 @@ int probe_cvt_fp4_f16_asm(const uint32_t* src, int n, float scale, uint32_t* out
 int probe_cvt_f32_fp8(const float* x, int64_t n, uint8_t* out) {
   if (n <= 0) return 0;
   k_cvt_f32_fp8<<<(unsigned)((n + 255) / 256), 256>>>(x, n, out);
+  return (int)hipGetLastError();
+}
+int probe_cvt_f32_fp8_pairs(const float* x, int64_t n4, uint32_t* out) {
+  if (n4 <= 0) return 0;
+  k_cvt_f32_fp8_pairs<<<(unsigned)((n4 + 255) / 256), 256>>>(x, n4, out);
+  return (int)hipGetLastError();
+}
+int probe_cvt_f32_fp4_x8(const float* x, int64_t n8, uint32_t* out) {
+  if (n8 <= 0) return 0;
+  k_cvt_f32_fp4_x8<<<(unsigned)((n8 + 255) / 256), 256>>>(x, n8, out);
   return (int)hipGetLastError();
 }
 int probe_cvt_f32_fp4(const float* x, int64_t n, uint8_t* out) {

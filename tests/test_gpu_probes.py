@@ -180,3 +180,53 @@ def test_mfma_f16_subnormal_operands(PL):
     # lane l: column l % 16, rows 4 * (l // 16) + 0..3
     want = np.stack([ref[4 * (l // 16):4 * (l // 16) + 4, l % 16] for l in range(64)])
     assert np.array_equal(got, want), np.abs(got - want).max()
+
+
+def _e4m3_inputs(O, rng):
+    grid = e4m3_grid(O)
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
+    x = np.concatenate([mids, -mids, np.nextafter(mids, np.float32(1e9)), np.nextafter(mids, np.float32(-1e9)),
+                        rng.uniform(-448, 448, 40000).astype(np.float32),
+                        (rng.standard_normal(20000) * 1e-3).astype(np.float32),
+                        np.float32([0.0, -0.0, 448.0, -448.0, 2.0 ** -10, -2.0 ** -10, 1e-30, -1e-30])])
+    x = x[:x.size // 4 * 4]
+    return rng.permutation(x).astype(np.float32)
+
+
+def test_cvt_f32_to_e4m3_pairs_in_both_words(PL, O):
+    """The packed binary32 -> E4M3 conversion used by the FP8 writes: both
+    values of a pair and both words of a dword match the oracle's encoder
+    for every |y| <= 448 (the writes clamp to +-448 first)."""
+    import torch
+    x = _e4m3_inputs(O, np.random.default_rng(6))
+    out = torch.zeros(x.size // 4, dtype=torch.int32, device="cuda")
+    log("probe cvt f32->e4m3 pairs")
+    assert PL.probe_cvt_f32_fp8_pairs(_ptr(torch.from_numpy(x).cuda()), ctypes.c_int64(x.size // 4), _ptr(out)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint8)
+    ref = np.array([O.e4m3_encode(float(v)) for v in x], np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:8]]
+
+
+def test_cvt_f32_to_e2m1_x8_packing(PL, O):
+    """The scaled binary32 -> E2M1 conversion used by the 4-bit writes, eight
+    values into one dword (byte selects 0..3): every nibble matches the
+    oracle's encoder, ties and saturation included."""
+    import torch
+    rng = np.random.default_rng(7)
+    g = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    mids = ((g[:-1] + g[1:]) / 2).astype(np.float32)
+    x = np.concatenate([mids, -mids, np.nextafter(mids, np.float32(9)), np.nextafter(mids, np.float32(-9)),
+                        rng.uniform(-8, 8, 40000).astype(np.float32),
+                        np.float32([0.0, -0.0, 6.0, -6.0, 6.5, -7.9, 1e-30, 5.0, -5.0, 0.25, -0.25, 7.0])])
+    x = rng.permutation(x[:x.size // 8 * 8]).astype(np.float32)
+    out = torch.zeros(x.size // 8, dtype=torch.int32, device="cuda")
+    log("probe cvt f32->e2m1 x8")
+    assert PL.probe_cvt_f32_fp4_x8(_ptr(torch.from_numpy(x).cuda()), ctypes.c_int64(x.size // 8), _ptr(out)) == 0
+    torch.cuda.synchronize()
+    b = out.cpu().numpy().view(np.uint8)
+    got = np.stack([b & 15, b >> 4], axis=1).ravel()
+    ref = np.array([O.e2m1_encode(float(v)) for v in x], np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:8]]
