@@ -96,10 +96,10 @@ __device__ __forceinline__ float deviation(const float (&v)[H], float* xa, float
   return sd;
 }
 
-// x / s correctly rounded, zero kept with its sign.
+// x / s correctly rounded (s > 0), zero kept with its sign: the quotient of
+// a non-zero x already has x's sign, so copying the sign only matters for -0.
 __device__ __forceinline__ float div_rn_z(float x, float s, Recip r) {
-  const float q = div_rn(x, s, r);
-  return x == 0.0f ? x : q;
+  return __builtin_copysignf(div_rn(x, s, r), x);
 }
 
 // Divide the 128 values by their deviation; returns the deviation.
