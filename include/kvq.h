@@ -211,8 +211,11 @@ kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void*
  * The library's choice fills one resident round of the split kernel on the
  * current HIP device (its compute units times the kernel's resident
  * workgroups per unit for this format, D and GQA group), with at least 8 pages
- * per split; it is fixed per device and process, so a workspace sized here
- * fits every later call with the same arguments.  Without a usable device the
+ * per split; where that asks for two splits of a kernel with two resident
+ * workgroups per unit and batch * H reaches the number of compute units, it
+ * runs one split of eight-wave workgroups instead (no workspace, no merge).
+ * The choice is fixed per device and process, so a workspace sized here fits
+ * every later call with the same arguments.  Without a usable device the
  * plan assumes 256 compute units and 2 workgroups per unit.  Host-only (no
  * kernel launched). */
 int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,

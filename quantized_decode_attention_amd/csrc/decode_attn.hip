@@ -360,15 +360,16 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
   }
 }
 
-template <int FMT, int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+template <int FMT, int D, int G, int W>
+__global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   constexpr int NK = D / 32;
   constexpr int NV = D / 16;
   constexpr int DL = D / 4;
 
-  __shared__ float lds_o[kWaves][2 * G][D];
-  __shared__ float lds_m[kWaves][16];
-  __shared__ float lds_l[kWaves][16];
+  constexpr int NT = 64 * W;  // threads
+  __shared__ float lds_o[W][2 * G][D];
+  __shared__ float lds_m[W][16];
+  __shared__ float lds_l[W][16];
   __shared__ int s_pages[kPageChunk];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -444,20 +445,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   for (int c0 = p_begin; c0 < p_end; c0 += kPageChunk) {
     const int nc = min(kPageChunk, p_end - c0);
     __syncthreads();
-    for (int i = tid; i < nc; i += 256) s_pages[i] = bt[c0 + i];
+    for (int i = tid; i < nc; i += NT) s_pages[i] = bt[c0 + i];
     __syncthreads();
-    const int nj = w < nc ? (nc - w + kWaves - 1) / kWaves : 0;  // this wave's pages
+    const int nj = w < nc ? (nc - w + W - 1) / W : 0;  // this wave's pages
     const int nu = nj << sp_shift;
     if (nu == 0) continue;
     // the unit count is padded to a whole number of ring turns; padded units
     // are masked out, so the loop body has no data-dependent branches
     const int nu_pad = (nu + kDepth - 1) / kDepth * kDepth;
     auto unit_page = [&](int u, bool& valid) {
-      const int page = __builtin_amdgcn_readfirstlane(s_pages[w + kWaves * (u >> sp_shift)]);
+      const int page = __builtin_amdgcn_readfirstlane(s_pages[w + W * (u >> sp_shift)]);
       valid = page >= 0 && page < a.num_pages;
       return head_base + (valid ? page : 0) * page_stride;
     };
-    auto unit_tok0 = [&](int u) { return (c0 + w + kWaves * (u >> sp_shift)) * P + (u & sp_mask) * 16; };
+    auto unit_tok0 = [&](int u) { return (c0 + w + W * (u >> sp_shift)) * P + (u & sp_mask) * 16; };
 
     // Units are prefetched kDepth-1 ahead into a ring of register buffers;
     // the loop is unrolled by kDepth so every ring slot is a fixed set of
@@ -505,15 +506,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   const float post = (FMT == 1 || FMT == 4) ? a.v_scale : 1.0f;
   float* rec = partials + (((int64_t)b * a.H + kvh) * S + split) * rec_floats;
-  for (int i = tid; i < G * D; i += 256) {
+  for (int i = tid; i < G * D; i += NT) {
     const int g = i / D, d = i % D;
     float M = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, lds_m[ww][g]);
+    for (int ww = 0; ww < W; ++ww) M = fmaxf(M, lds_m[ww][g]);
     float L = 0.0f, O = 0.0f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
+      for (int ww = 0; ww < W; ++ww) {
         const float f = exp2f(lds_m[ww][g] - M);
         L += f * lds_l[ww][g];
         O += f * (lds_o[ww][g][d] + lds_o[ww][g + G][d]);
@@ -554,14 +555,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int D, 
   a.out[idx] = __builtin_bit_cast(uint16_t, (half_t)o);
 }
 
+// Four-wave workgroups normally; eight waves when each (sequence, kv head)
+// runs as a single workgroup that fills a compute unit by itself.
+template <int FMT, int D, int G>
+hipError_t launch_w(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.waves == 8)
+    decode_kernel<FMT, D, G, 8><<<grid, 512, 0, s>>>(a);
+  else
+    decode_kernel<FMT, D, G, 4><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int FMT, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.num_splits, (unsigned)a.H, (unsigned)a.B);
   switch (a.G) {
-    case 1: decode_kernel<FMT, D, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: decode_kernel<FMT, D, 2><<<grid, 256, 0, s>>>(a); break;
-    case 4: decode_kernel<FMT, D, 4><<<grid, 256, 0, s>>>(a); break;
-    case 8: decode_kernel<FMT, D, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: return launch_w<FMT, D, 1>(a, grid, s);
+    case 2: return launch_w<FMT, D, 2>(a, grid, s);
+    case 4: return launch_w<FMT, D, 4>(a, grid, s);
+    case 8: return launch_w<FMT, D, 8>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -580,7 +592,7 @@ hipError_t launch_fmt(const DecodeArgs& a, hipStream_t s) {
 template <int FMT, int D, int G>
 int occupancy() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&decode_kernel<FMT, D, G>), 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&decode_kernel<FMT, D, G, 4>), 256,
                                                    0) != hipSuccess)
     return 0;
   return n;

@@ -117,6 +117,12 @@ kvq_status current_device_ok() {
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
+// The split kernel's unit of work along the context: a page, or for KVarN a
+// 128-token tile (a page holds page_size / 128 of them).
+int plan_units(const kvq_layout* L, int max_pages) {
+  return L->format == KVQ_KVARN_K4V2_G128 ? max_pages * (L->page_size / 128) : max_pages;
+}
+
 // Context splits per (sequence, kv head): enough workgroups for one resident
 // round of the split kernel, i.e. compute units x the kernel's resident
 // workgroups per compute unit, while keeping at least 8 pages (two per
@@ -136,11 +142,15 @@ std::atomic<int> g_blocks_per_cu[kMaxDevices][8][3][4];  // [dev][format][D 32/6
 int index_of_d(int D) { return D == 32 ? 0 : (D == 64 ? 1 : 2); }
 int index_of_g(int G) { return G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3)); }
 
-int64_t target_workgroups(const kvq_layout* L, int G) {
+struct Residency {
+  int cus, per_cu;  // compute units; resident split workgroups (4 waves) per unit
+};
+
+Residency residency(const kvq_layout* L, int G) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices || device_ok(dev) != KVQ_OK ||
       L->format < 1 || L->format > 7 || (G != 1 && G != 2 && G != 4 && G != 8))
-    return (int64_t)kFallbackCUs * kFallbackBlocksPerCU;
+    return Residency{kFallbackCUs, kFallbackBlocksPerCU};
   int cus = g_cu_count[dev].load(std::memory_order_relaxed);
   if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
@@ -157,10 +167,11 @@ int64_t target_workgroups(const kvq_layout* L, int G) {
     if (eight_bit && per_cu > 2) per_cu = 2;
     slot.store(per_cu, std::memory_order_relaxed);
   }
-  return (int64_t)cus * per_cu;
+  return Residency{cus, per_cu};
 }
 
-void plan_splits(int batch, int H, int max_pages, int hint, int64_t target, int* splits, int* pages_per_split) {
+void plan_splits(int batch, int H, int max_pages, int hint, int64_t target, int* splits, int* pages_per_split,
+                 int* waves) {
   const int64_t units = (int64_t)batch * H;
   int s = hint;
   if (s <= 0) {
@@ -176,12 +187,24 @@ void plan_splits(int batch, int H, int max_pages, int hint, int64_t target, int*
   *pages_per_split = pps;
   *splits = (max_pages + pps - 1) / pps;
   if (*splits < 1) *splits = 1;
+  *waves = 4;
 }
 
-// The split kernel's unit of work along the context: a page, or for KVarN a
-// 128-token tile (a page holds page_size / 128 of them).
-int plan_units(const kvq_layout* L, int max_pages) {
-  return L->format == KVQ_KVARN_K4V2_G128 ? max_pages * (L->page_size / 128) : max_pages;
+// The library's plan for a decode problem.  When the automatic plan asks for
+// two splits of four-wave workgroups, two resident per compute unit, and
+// every compute unit already gets a (sequence, kv head) of its own, one
+// eight-wave workgroup per pair keeps the same waves resident with no split
+// partials and no merge launch.
+void plan(const kvq_layout* L, int batch, int G, int max_pages, int hint, int* splits, int* pps, int* waves) {
+  const Residency r = residency(L, G);
+  plan_splits(batch, L->num_kv_heads, plan_units(L, max_pages), hint, (int64_t)r.cus * r.per_cu, splits, pps,
+              waves);
+  if (hint == 0 && L->format != KVQ_KVARN_K4V2_G128 && r.per_cu == 2 && *splits == 2 &&
+      (int64_t)batch * L->num_kv_heads >= r.cus) {
+    *splits = 1;
+    *pps = max_pages;
+    *waves = 8;
+  }
 }
 
 int64_t workspace_bytes_for(const kvq_layout* L, int batch, int splits) {
@@ -261,9 +284,8 @@ int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t n
   if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0 ||
       num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return -1;
-  int s, pps;
-  plan_splits(batch, layout->num_kv_heads, plan_units(layout, max_pages_per_seq), num_splits,
-              target_workgroups(layout, num_q_heads / layout->num_kv_heads), &s, &pps);
+  int s, pps, waves;
+  plan(layout, batch, num_q_heads / layout->num_kv_heads, max_pages_per_seq, num_splits, &s, &pps, &waves);
   return s;
 }
 
@@ -272,9 +294,8 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int3
   if (check_layout(layout) != KVQ_OK || batch < 0 || max_pages_per_seq < 1 || num_splits < 0 ||
       num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return -1;
-  int s, pps;
-  plan_splits(batch, layout->num_kv_heads, plan_units(layout, max_pages_per_seq), num_splits,
-              target_workgroups(layout, num_q_heads / layout->num_kv_heads), &s, &pps);
+  int s, pps, waves;
+  plan(layout, batch, num_q_heads / layout->num_kv_heads, max_pages_per_seq, num_splits, &s, &pps, &waves);
   return workspace_bytes_for(layout, batch, s);
 }
 
@@ -293,9 +314,8 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
   if (kvarn_tail && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
   if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
-  int splits, pps;
-  plan_splits(batch, H, plan_units(layout, max_pages_per_seq), num_splits, target_workgroups(layout, G), &splits,
-              &pps);
+  int splits, pps, waves;
+  plan(layout, batch, G, max_pages_per_seq, num_splits, &splits, &pps, &waves);
   const int64_t need = workspace_bytes_for(layout, batch, splits);
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;
@@ -323,6 +343,7 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
   a.workspace = static_cast<uint8_t*>(workspace);
   a.num_splits = splits;
   a.pages_per_split = pps;
+  a.waves = waves;
   a.sp_shift = __builtin_ctz(layout->page_size / 16);
   if (layout->format == KVQ_KVARN_K4V2_G128)
     return from_hip(launch_kvarn_decode(a, static_cast<hipStream_t>(stream)));

@@ -44,6 +44,7 @@ struct DecodeArgs {
   int num_splits;
   int pages_per_split;
   int sp_shift;  // log2(P / 16)
+  int waves;     // wavefronts per split workgroup: 4, or 8 for single-split plans
 };
 
 // Workspace: one partial record (m[8], l[8], o[8][D]) per (sequence, kv head,

@@ -85,7 +85,11 @@ def test_split_plan_and_workspace(K):
     lay = K.layout(2, 8, 128, 16, 16384)
     # no device: 256 compute units x 2 workgroups, one resident round of 512
     assert K.kvq_decode_num_splits(lay, 8, 64, 2048) == 8
-    assert K.kvq_decode_num_splits(lay, 32, 64, 256) == 2
+    assert K.kvq_decode_num_splits(lay, 16, 64, 256) == 4
+    # a (sequence, kv head) per compute unit: one split of eight-wave workgroups
+    assert K.kvq_decode_num_splits(lay, 32, 64, 256) == 1
+    assert K.kvq_decode_workspace_bytes(lay, 32, 64, 256) == 0
+    assert K.kvq_decode_num_splits(lay, 32, 64, 256, 2) == 2  # an explicit count is kept
     assert K.kvq_decode_num_splits(lay, 2, 64, 1) == 1
     assert K.kvq_decode_num_splits(lay, 2, 64, 10, 3) == 3
     assert K.kvq_decode_num_splits(lay, 2, 64, 9, 4) == 3  # empty trailing split dropped

@@ -306,3 +306,35 @@ def test_auto_split_plan_fills_the_device(K, O, fmt):
     p = ctypes.c_void_p(cache.data_ptr())
     st = K.lib.kvq_decode_attention(ctypes.byref(lay), p, p, H * G, p, mp, p, B, 0.1, None, p, p, need - 1, 0, None)
     assert st == 3
+    if fmt in (1, 2, 3):
+        # a (sequence, kv head) per compute unit or more: one split of
+        # eight-wave workgroups, no workspace
+        assert K.kvq_decode_num_splits(lay, 32, H * 4, mp) == 1
+        assert K.kvq_decode_workspace_bytes(lay, 32, H * 4, mp) == 0
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_decode_single_split_eight_waves(K, O, fmt):
+    """Enough (sequence, kv head) pairs to give every compute unit one: the
+    automatic plan runs one eight-wave workgroup per pair (no split
+    partials); every output matches the oracle, empty and ragged contexts
+    included."""
+    rng = np.random.default_rng(8100 + fmt)
+    B, H, G, D, P = 64, 4, 4, 128, 16
+    ctx = rng.integers(0, 300, B).astype(np.int32)
+    ctx[0], ctx[1], ctx[2] = 0, 1, 16 * 18
+    bt, num_pages, slots = paged_problem(rng, B, H, G, D, P, ctx)
+    n = slots.shape[0]
+    k16 = workloads.random_halves(rng, (n, H, D))
+    v16 = workloads.random_halves(rng, (n, H, D))
+    lay = layout_for(K, fmt, 0, H, D, P, num_pages, k16, v16)
+    assert K.kvq_decode_num_splits(lay, B, H * G, bt.shape[1]) == 1
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    q16 = workloads.random_halves(rng, (B, H * G, D))
+    sm = 1.0 / math.sqrt(D)
+    ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, sm)
+    log(f"decode eight-wave single split fmt={fmt}")
+    got, ws = gpu_decode(K, lay, dev(cache), q16, bt, ctx, sm)
+    assert ws.num_splits == 1 and ws.buffer.numel() == 0
+    assert_attn_close(got, ref)
+    assert not np.any(got[0])
