@@ -57,15 +57,18 @@ __device__ __forceinline__ void load_kv(const uint8_t* chunk, int u, int n, int 
 
 // K operand of QK MFMA kk: the 8 codes of dword kk as binary16.  The low
 // nibbles (even channels) and high nibbles (odd channels) are separated into
-// bytes, each byte is placed under the 0x64 exponent byte by a byte permute
-// (binary16 1024 + code) and 1024 is subtracted exactly.  Slot i holds
+// bytes.  A byte holding a code c in 0..15 is the E4M3 encoding of c * 2^-9
+// (codes 0..7 are the subnormals m * 2^-9, codes 8..15 the first normal
+// binade (8 + m) * 2^-9), so gfx950's scaled E4M3 -> binary16 conversion at
+// scale 2^9 returns c exactly, two codes per instruction.  Slot i holds
 // channel 8*kk + slot_channel(i): slots 0..3 = channels 0, 2, 4, 6 and slots
 // 4..7 = channels 1, 3, 5, 7.
-__device__ __forceinline__ half8_t k_operand(uint32_t w) {
+__device__ __forceinline__ half8_t k_operand(uint32_t w, float s512) {
   const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-  const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
-  return cat(as_h2(perm(0x64646464u, x, 0x04010400u)) - k1024, as_h2(perm(0x64646464u, x, 0x04030402u)) - k1024,
-             as_h2(perm(0x64646464u, y, 0x04010400u)) - k1024, as_h2(perm(0x64646464u, y, 0x04030402u)) - k1024);
+  uint32_t a, b, c, d;
+  e4m3x4_to_h_scaled(x, s512, a, b);
+  e4m3x4_to_h_scaled(y, s512, c, d);
+  return cat(as_h2(a), as_h2(b), as_h2(c), as_h2(d));
 }
 __host__ __device__ constexpr int slot_channel(int i) { return i < 4 ? 2 * i : 2 * (i - 4) + 1; }
 
@@ -103,7 +106,8 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
                                              const half8_t (&qB)[4], float qb, float qk, KvState& st) {
   float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(r.k[kk]), qB[kk], s, 0, 0, 0);
+  for (int kk = 0; kk < 4; ++kk)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(r.k[kk], 512.0f), qB[kk], s, 0, 0, 0);
 
   const float4 rho = *reinterpret_cast<const float4*>(mt + kKr + 16 * u + 4 * gq);
   const float4 va = *reinterpret_cast<const float4*>(mt + kVa + 16 * u + 4 * gq);

@@ -236,4 +236,13 @@ __device__ __forceinline__ void e4m3x4_to_h_hw(uint32_t w, uint32_t& lo, uint32_
       : "v"(w));
 }
 
+// The same with a power-of-two scale.
+__device__ __forceinline__ void e4m3x4_to_h_scaled(uint32_t w, float scale, uint32_t& lo, uint32_t& hi) {
+  asm("v_cvt_scalef32_pk_f16_fp8 %0, %2, %3\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %1, %2, %3 op_sel:[1,0,0]\n\t"
+      "s_nop 1"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(w), "v"(scale));
+}
+
 }  // namespace kvq

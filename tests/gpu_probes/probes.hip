@@ -97,7 +97,25 @@ __global__ void k_mfma_f16(const half8_t* a, const half8_t* b, float4_t* out) {
   out[l] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[l], b[l], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
 
+// E4M3 pairs -> binary16 with a scale operand, issued as the KVarN decode does:
+// word i -> out[2i] (bytes 0, 1), out[2i + 1] (bytes 2, 3).
+__global__ void k_cvt_fp8_f16_scaled(const uint32_t* src, int n, float scale, uint32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t lo, hi;
+  asm("s_nop 1\n\tv_cvt_scalef32_pk_f16_fp8 %0, %2, %3\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %1, %2, %3 op_sel:[1,0,0]\n\ts_nop 1"
+      : "=&v"(lo), "=&v"(hi) : "v"(src[i]), "v"(scale));
+  out[2 * (int64_t)i] = lo;
+  out[2 * (int64_t)i + 1] = hi;
+}
+
 extern "C" {
+int probe_cvt_fp8_f16_scaled(const uint32_t* src, int n, float scale, uint32_t* out) {
+  if (n <= 0) return 0;
+  k_cvt_fp8_f16_scaled<<<(n + 255) / 256, 256>>>(src, n, scale, out);
+  return (int)hipGetLastError();
+}
 int probe_mfma_f16(const void* a, const void* b, void* out) {
   k_mfma_f16<<<1, 64>>>(reinterpret_cast<const half8_t*>(a), reinterpret_cast<const half8_t*>(b),
                         reinterpret_cast<float4_t*>(out));

@@ -230,3 +230,21 @@ def test_cvt_f32_to_e2m1_x8_packing(PL, O):
     ref = np.array([O.e2m1_encode(float(v)) for v in x], np.uint8)
     bad = np.nonzero(got != ref)[0]
     assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:8]]
+
+
+def test_cvt_e4m3_nibbles_to_f16_integers(PL):
+    """KVarN key codes: a byte holding c in 0..15, read as E4M3 (c * 2^-9)
+    and converted with scale 2^9, gives exactly the integer c, in both
+    bytes of both words."""
+    import torch
+    rng = np.random.default_rng(8)
+    words = rng.integers(0, 2 ** 32, 4096, dtype=np.uint64).astype(np.uint32) & np.uint32(0x0F0F0F0F)
+    words[:16] = np.arange(16, dtype=np.uint32) * np.uint32(0x01010101)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    out = torch.zeros(words.size * 2, dtype=torch.int32, device="cuda")
+    log("probe cvt e4m3 nibbles -> integers")
+    assert PL.probe_cvt_fp8_f16_scaled(_ptr(src), words.size, ctypes.c_float(512.0), _ptr(out)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.float16).astype(np.float64).reshape(words.size, 4)
+    want = np.stack([(words >> (8 * k)) & 0xFF for k in range(4)], axis=1).astype(np.float64)
+    assert np.array_equal(got, want)
