@@ -354,7 +354,10 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
-            "kernel": f"decode_kernel<{pb.fmt}, {sp.D}, {sp.Hq // sp.Hkv}>"
+            # eight-wave workgroups when the plan runs a single split over
+            # at least one (sequence, kv head) per compute unit (kvq.h)
+            "kernel": f"decode_kernel<{pb.fmt}, {sp.D}, {sp.Hq // sp.Hkv}, "
+                      f"{8 if pb.ws.num_splits == 1 and pb.fmt in (1, 2, 3) and w.B * sp.Hkv >= 256 else 4}>"
                       + (" + decode_merge_kernel" if pb.ws.num_splits > 1 else ""),
             "algorithmic_bytes": pb.kv_bytes, "traffic_unit": "HBM bytes per decode call (rocprofv3 "
             "FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB copy)",
