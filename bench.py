@@ -300,7 +300,7 @@ def main():
     ap.add_argument("--workload", default="int8_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-formats", action="store_true", help="skip the other formats' workloads")
-    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences of the CPU baseline (0 = the whole batch)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -397,7 +397,9 @@ def main():
     if not args.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         log(f"[bench] CPU oracle baseline on {threads} threads ...")
-        result["cpu_baseline"] = cpu_baseline(args.workload, *main_fmt, args.cpu_seqs, threads)
+        import workloads
+        n_seq = args.cpu_seqs or workloads.SPECS[args.workload].B
+        result["cpu_baseline"] = cpu_baseline(args.workload, *main_fmt, n_seq, threads)
     print(json.dumps(result), flush=True)
 
 
