@@ -8,8 +8,9 @@
 // 读取路径: unpack, apply scales, feed the attention math inside the tile
 // load, never materialise a full-precision copy).
 //
-// Decomposition.  A workgroup of 4 wavefronts owns one (sequence, kv head,
-// context split); wave w walks pages w, w+4, ... of the split.  Per 16-token
+// Decomposition.  A workgroup of W wavefronts (4, or 8 when one workgroup
+// per (sequence, kv head) fills the GPU) owns one (sequence, kv head,
+// context split); wave w walks pages w, w+W, ... of the split.  Per 16-token
 // sub-page a wave computes
 //   S^T[16 tok][16 cols] = K[16 tok][D] * Q^T[D][16 cols]   (D/32 MFMA 16x16x32 f16)
 //   O[16 rows][D]       += P[16 rows][16 tok] * V[16 tok][D] (D/16 MFMA 16x16x16 f16)
@@ -29,8 +30,9 @@
 // are 16-byte vectors that together cover whole 128-byte lines and need no
 // LDS staging.
 //
-// Splits: each workgroup writes its partial (m, l, O) to the workspace and a
-// second, small kernel merges the partials of every (sequence, kv head).
+// Splits: with more than one, each workgroup writes its partial (m, l, O) to
+// the workspace and a second, small kernel merges the partials of every
+// (sequence, kv head); a single split writes the output directly.
 #include "decode_common.h"
 
 namespace kvq {
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- combine the four waves (and the hi/lo rows) in LDS
+  // ---- combine the W waves (and the hi/lo rows) in LDS
   float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (gq == 0) {

@@ -9,7 +9,7 @@
 
 namespace kvq {
 
-constexpr int kWaves = 4;          // wavefronts per decode workgroup
+constexpr int kWaves = 4;          // wavefronts per KVarN decode workgroup
 constexpr int kPageChunk = 256;    // block-table entries staged in LDS at a time
 constexpr float kNegInf = -INFINITY;
 
