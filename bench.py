@@ -208,9 +208,19 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
 
 # HBM traffic of one decode call, measured with rocprofv3 counters and kept in
 # a profile summary together with a digest of the decode kernel's sources: the
-# figure is reported only while those sources are unchanged.
+# figure is reported only while those sources are unchanged (comments and
+# blank lines aside).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int8_32k_traffic.md")
 DECODE_SOURCES = ("decode_attn.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
+
+
+def _code_only(text):
+    """Source text without // and /* */ comments, blank lines or trailing
+    blanks (string literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
 def decode_sources_digest():
@@ -219,8 +229,8 @@ def decode_sources_digest():
     from quantized_decode_attention_amd import _build
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
-        with open(os.path.join(_build.CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(_build.CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     h.update(" ".join(_build.SOURCES["decode_attn.hip"] + _build.COMMON[:4]).encode())
     return h.hexdigest()
 
