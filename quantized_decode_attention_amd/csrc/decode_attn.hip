@@ -163,15 +163,18 @@ __device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2
     e2m1x8_to_h_scaled(r.k[kk], kmx, h);
     return cat(as_h2(h[0]), as_h2(h[1]), as_h2(h[2]), as_h2(h[3]));
   } else if constexpr (FMT == 6) {
-    // two's-complement nibble ^ 8 = code + 8; under the 0x64 exponent byte it
-    // reads 1032 + code, and subtracting 1032 is exact.  (Leaving the bias in
-    // the scores, as for INT8, costs too much accuracy here: INT4 scales are
-    // 18x coarser, so the binary32 rounding of the biased sum weighs 18x more.)
+    // two's-complement nibble ^ 8 = code + 8 in 0..15.  A byte holding it is
+    // the E4M3 encoding of (code + 8) * 2^-9, so the scaled conversion at 2^9
+    // returns code + 8 exactly, two per instruction; the offset 8 * sum(q) is
+    // removed from the scores once per head.  (An offset of 1032, as a byte
+    // permute under the 0x64 exponent byte gives, would cost accuracy: the
+    // biased sums would be ~100x larger than the scores.)
     const uint32_t w = r.k[kk] ^ 0x88888888u;
     const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-    const half2_t k1032 = {(half_t)1032.0f, (half_t)1032.0f};
-    return cat(as_h2(perm(0x64646464u, x, 0x04010400u)) - k1032, as_h2(perm(0x64646464u, x, 0x04030402u)) - k1032,
-               as_h2(perm(0x64646464u, y, 0x04010400u)) - k1032, as_h2(perm(0x64646464u, y, 0x04030402u)) - k1032);
+    uint32_t a, b, c, d;
+    e4m3x4_to_h_scaled(x, 512.0f, a, b);
+    e4m3x4_to_h_scaled(y, 512.0f, c, d);
+    return cat(as_h2(a), as_h2(b), as_h2(c), as_h2(d));
   } else if constexpr (FMT != 4) {
     half2_t a, b, c, d;
     if constexpr (FMT == 2) {
@@ -410,9 +413,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   }
 
   const float kconst = (FMT == 1 || FMT == 4) ? a.k_scale * a.qk_scale : a.qk_scale;
-  // INT8 keys enter the MFMA as binary16 1152 + code: remove 1152 * sum(q)
+  // INT8 keys enter the MFMA as binary16 1152 + code, INT4 keys as code + 8:
+  // remove the offset times sum(q)
   float kbias = 0.0f;
-  if constexpr (FMT == 2) {
+  if constexpr (FMT == 2 || FMT == 6) {
     float qs = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
       for (int e = 0; e < 8; ++e) qs += (float)qB[kk][e];
     qs += __shfl_xor(qs, 16);
     qs += __shfl_xor(qs, 32);
-    kbias = 1152.0f * qs;
+    kbias = (FMT == 2 ? 1152.0f : 8.0f) * qs;
   }
   WaveState<D> st;
 #pragma unroll
