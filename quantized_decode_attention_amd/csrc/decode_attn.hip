@@ -246,7 +246,12 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
   constexpr bool PTH = kPth<FMT>;
 
   half2_t ksc01 = {0, 0}, ksc23 = {0, 0};
-  if constexpr (FMT == 4) e4m3x4_to_h(r.ksc, ksc01, ksc23);
+  if constexpr (FMT == 4) {
+    uint32_t lo, hi;
+    e4m3x4_to_h_hw(r.ksc, lo, hi);  // E4M3 block scales -> binary16, exact
+    ksc01 = as_h2(lo);
+    ksc23 = as_h2(hi);
+  }
   const float kmx = FMT == 7 ? e8m0_scale(r.ksc) : 0.0f;
   float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -315,7 +320,12 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     else
       pA = half4_t{0, 0, 0, 0};
     half2_t vs01 = {0, 0}, vs23 = {0, 0};
-    if constexpr (FMT == 4) e4m3x4_to_h(r.vsc, vs01, vs23);
+    if constexpr (FMT == 4) {
+      uint32_t lo, hi;
+      e4m3x4_to_h_hw(r.vsc, lo, hi);
+      vs01 = as_h2(lo);
+      vs23 = as_h2(hi);
+    }
     float vmx[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (FMT == 7)
 #pragma unroll
