@@ -50,9 +50,22 @@ struct RawKv {
   uint32_t v[2];
 };
 
-__device__ __forceinline__ void load_kv(const uint8_t* chunk, int u, int n, int gq, RawKv& r) {
-  load_dwords<4>(chunk + (16 * u + n) * 64 + 16 * gq, r.k);
-  load_dwords<2>(chunk + kVCodes + 128 * (4 * u + gq) + 8 * n, r.v);
+// The lane's byte offsets within a sub-page (fixed for the kernel): the
+// wave-uniform part of an address stays in scalar registers.
+struct LaneOffs {
+  uint32_t k, v;
+};
+__device__ __forceinline__ LaneOffs lane_offsets(int n, int gq) { return {(uint32_t)(64 * n + 16 * gq), (uint32_t)(128 * gq + 8 * n)}; }
+
+template <int N>
+__device__ __forceinline__ void load_dwords_at(const uint8_t* base, uint32_t off, uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = ld_nt(base + off + 4 * i);
+}
+
+__device__ __forceinline__ void load_kv(const uint8_t* chunk, int u, const LaneOffs& lo, RawKv& r) {
+  load_dwords_at<4>(chunk + 1024 * u, lo.k, r.k);
+  load_dwords_at<2>(chunk + kVCodes + 512 * u, lo.v, r.v);
 }
 
 // K operand of QK MFMA kk: the 8 codes of dword kk as binary16.  The low
@@ -72,24 +85,40 @@ __device__ __forceinline__ half8_t k_operand(uint32_t w, float s512) {
 }
 __host__ __device__ constexpr int slot_channel(int i) { return i < 4 ? 2 * i : 2 * (i - 4) + 1; }
 
+// Products x0 = a0 b0 and x1 = a1 b1 as binary16 pairs: h = (RN16 x0, RN16 x1)
+// and the remainders r = (RN16(x0 - h0), RN16(x1 - h1)).  Each value is one
+// mixed-precision fused multiply-add (binary32 inputs, binary16 result, the
+// remainder's subtrahend read straight from h's half), four instructions per
+// pair.
+__device__ __forceinline__ void split_products(float a0, float b0, float a1, float b1, uint32_t& h, uint32_t& r) {
+  asm("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
+      "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
+      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(h), "=&v"(r)
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+}
+
 // Beyond the binary16 bound on P * v_scale, the reference also keeps P itself
 // below 2^64: a KVarN per-token V scale can be 0.
 constexpr float kPMaxLog2 = 64.0f;
-constexpr float kPMax = 18446744073709551616.0f;  // 2^64
 
-// V codes of one dword (4 channels x 4 tokens) -> binary16 high bytes of the
-// code values, one word per token: hb[k] byte m = value of token k, channel m.
-// 0, 1, 2, 3 have binary16 high bytes 00, 3C, 40, 42 and zero low bytes.
-__device__ __forceinline__ void v_hibytes(uint32_t w, uint32_t (&hb)[4]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) hb[k] = perm(0u, 0x42403C00u, (w >> (2 * k)) & 0x03030303u);
+// V codes of one dword (byte m = channel m, bits 2k..2k+1 = token k) as
+// binary16.  A nibble 00cc is the E2M1 encoding of c / 2, so masking the
+// dword to 0x33333333 leaves tokens 0 and 2 of channel m in byte m's two
+// nibbles, and the scaled E2M1 conversion at scale 2 returns both codes
+// exactly; the dword shifted right by 2 gives tokens 1 and 3 the same way.
+// The MFMA operand of channel m therefore lists its tokens in the order
+// 0, 2, 1, 3, and P's operand is built in the same order.
+constexpr int kTokOrder[4] = {0, 2, 1, 3};
+struct VCodes {
+  uint32_t t02[4], t13[4];  // per channel byte: binary16 pairs (token 0, 2) and (1, 3)
+};
+__device__ __forceinline__ void v_codes(uint32_t w, VCodes& c) {
+  e2m1x8_to_h_scaled(w & 0x33333333u, 2.0f, c.t02);
+  e2m1x8_to_h_scaled((w >> 2) & 0x33333333u, 2.0f, c.t13);
 }
-
-// V operand of PV MFMA for channel byte m of a dword: tokens 0..3.
-__device__ __forceinline__ half4_t v_operand(const uint32_t (&hb)[4], int m) {
-  const uint32_t sel = 0x0Cu | ((uint32_t)m << 8) | (0x0Cu << 16) | ((uint32_t)(4 + m) << 24);
-  return cat4(as_h2(perm(hb[1], hb[0], sel)), as_h2(perm(hb[3], hb[2], sel)));
-}
+__device__ __forceinline__ half4_t v_operand(const VCodes& c, int m) { return cat4(as_h2(c.t02[m]), as_h2(c.t13[m])); }
 
 // The output rows are kept in the gamma domain of the page being read
 // (o = gamma (.) o'): moving to the next page rescales o' once by
@@ -123,15 +152,18 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
     const float lo = __uint_as_float(row_shl<G>(__float_as_uint(s[i])));
     lg[i] = rh[i] * (s[i] + lo + qb) * qk;
   }
-  float p[4], pv[4];
-  bool over = false;
+  float p[4], pv[4], arg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
+    arg[i] = lg[i] - st.m_run;
+    p[i] = __builtin_amdgcn_exp2f(arg[i]);
     pv[i] = p[i] * vsc[i];
-    over |= !(pv[i] <= kTauPow) || !(p[i] <= kPMax);
   }
-  over = over && (n < G);
+  // P * v_scale above 2^8 or P itself above 2^64 (an exponent above 64; the
+  // exponent is +inf, never NaN, while the reference is still -inf)
+  const float amax = fmaxf(fmaxf(arg[0], arg[1]), fmaxf(arg[2], arg[3]));
+  const float pvmax = fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3]));
+  const bool over = (amax > kPMaxLog2 || pvmax > kTauPow) && (n < G);
 
   // P (high/low halves) times V into the output rows.  Both sides of the
   // rare rescale branch below run their own copy, so the accumulators are
@@ -143,9 +175,13 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
     for (int i = 0; i < 4; ++i) {
       st.l_run += p[i];
       st.pb += p[i] * vbe[i];
-      const half_t hh = (half_t)pv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = pv[kTokOrder[i]];
+      const half_t hh = (half_t)x;
       ph[i] = hh;
-      plo[i] = (half_t)(pv[i] - (float)hh);
+      plo[i] = (half_t)(x - (float)hh);
     }
     const uint2 lob = __builtin_bit_cast(uint2, plo);
     uint2 shifted;
@@ -158,15 +194,15 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
       pA = __builtin_bit_cast(half4_t, shifted);
     else
       pA = half4_t{0, 0, 0, 0};
-    uint32_t hb0[4], hb1[4];
-    v_hibytes(r.v[0], hb0);
-    v_hibytes(r.v[1], hb1);
+    VCodes c0, c1;
+    v_codes(r.v[0], c0);
+    v_codes(r.v[1], c1);
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn)
-      st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb0, nn), st.o[nn], 0, 0, 0);
+      st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(c0, nn), st.o[nn], 0, 0, 0);
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn)
-      st.o[4 + nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(hb1, nn), st.o[4 + nn], 0, 0, 0);
+      st.o[4 + nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(c1, nn), st.o[4 + nn], 0, 0, 0);
   };
 
   if (__any(over)) {
@@ -264,6 +300,7 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   const uint8_t* head_base = a.cache + (int64_t)kvh * a.geom.chunk_bytes;
   const int64_t page_stride = (int64_t)a.H * a.geom.chunk_bytes;
   float* mt = s_meta[w];
+  const LaneOffs lofs = lane_offsets(n, gq);
 
   for (int c0 = p_begin; c0 < p_end; c0 += kPageChunk) {
     const int nc = min(kPageChunk, p_end - c0);
@@ -291,7 +328,7 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
     // multiple of kRing, so sub-page u of every page uses slot u % kRing)
     RawKv rr[kRing];
 #pragma unroll
-    for (int k = 0; k + 1 < kRing; ++k) load_kv(pc, k, n, gq, rr[k]);
+    for (int k = 0; k + 1 < kRing; ++k) load_kv(pc, k, lofs, rr[k]);
 
     for (int j = 0; j < nj; ++j) {
       // publish this page's metadata to the wave's LDS block (same-wave LDS
@@ -308,14 +345,14 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
       auto issue = [&](int u) {
         const int ahead = u + kRing - 1;
         if (ahead < kUnits) {
-          load_kv(pc, ahead, n, gq, rr[ahead % kRing]);
+          load_kv(pc, ahead, lofs, rr[ahead % kRing]);
         } else {
           if (ahead == kUnits) {
             load_dwords<4>(pn + kMeta + 16 * l, mreg);
             load_dwords<4>(pn + kMeta + 1024 + 16 * l, mreg + 4);
             load_dwords<4>(pn + kMeta + 2048 + 16 * l, mreg + 8);
           }
-          load_kv(pn, ahead - kUnits, n, gq, rr[ahead % kRing]);
+          load_kv(pn, ahead - kUnits, lofs, rr[ahead % kRing]);
         }
         // keep the loads ahead of this sub-page's wait for its own data
         __builtin_amdgcn_sched_barrier(0);
@@ -324,7 +361,6 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
         // B operand q~ (.) alpha (high half in columns n < G, low half in
         // columns G + n, zero beyond) and the beta term sum_j q~_j beta_j
         half8_t qB[4];
-        float qb = 0.0f;
         const float* qrow = s_q[q_row] + 32 * gq;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -333,22 +369,33 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
           const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
           const float4 a0 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk);
           const float4 a1 = *reinterpret_cast<const float4*>(mt + kKa + 32 * gq + 8 * kk + 4);
-          const float4 b0 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk);
-          const float4 b1 = *reinterpret_cast<const float4*>(mt + kKb + 32 * gq + 8 * kk + 4);
           const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-          const float be[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          uint32_t qw[4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int c = slot_channel(i);
-            const float x = qv[c] * al[c];
-            const half_t hi = (half_t)x;
-            const half_t t = lo_col ? hi : (half_t)0.0f;
-            qB[kk][i] = (half_t)(x - (float)t);
-            qb += qv[c] * be[c];
+          for (int i = 0; i < 8; i += 2) {
+            // both halves of a slot pair, then one select of the column's half
+            const int c0 = slot_channel(i), c1 = slot_channel(i + 1);
+            uint32_t h, r;
+            split_products(qv[c0], al[c0], qv[c1], al[c1], h, r);
+            qw[i / 2] = lo_col ? r : h;
+          }
+          qB[kk] = __builtin_bit_cast(half8_t, qw);
+        }
+        // beta term: a high column's lane sums channels 32 gq .. +15 of its
+        // head, the matching low column's lane channels 32 gq + 16 .. +31
+        float qb = 0.0f;
+        {
+          const int off = 32 * gq + (lo_col ? 16 : 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4 qq = *reinterpret_cast<const float4*>(s_q[q_row] + off + 4 * j);
+            const float4 bb = *reinterpret_cast<const float4*>(mt + kKb + off + 4 * j);
+            qb += qq.x * bb.x + qq.y * bb.y + qq.z * bb.z + qq.w * bb.w;
           }
         }
         qb += __shfl_xor(qb, 16);
         qb += __shfl_xor(qb, 32);
+        qb += __uint_as_float(row_shl<G>(__float_as_uint(qb)));  // columns n < G
         // move the output into this page's gamma domain
         {
           const float4 g0 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n);
