@@ -102,6 +102,9 @@ __device__ __forceinline__ void split_products(float a0, float b0, float a1, flo
 // Beyond the binary16 bound on P * v_scale, the reference also keeps P itself
 // below 2^64: a KVarN per-token V scale can be 0.
 constexpr float kPMaxLog2 = 64.0f;
+constexpr uint16_t kTauPowBits = 0x5C00;  // binary16 2^8
+static_assert(kTauPow == 256.0f, "binary16 pattern of the P bound");
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 // V codes of one dword (byte m = channel m, bits 2k..2k+1 = token k) as
 // binary16.  A nibble 00cc is the E2M1 encoding of c / 2, so masking the
@@ -130,10 +133,12 @@ struct KvState {
 };
 
 // One sub-page of a valid page (invalid pages are skipped by the caller).
+// q~ and the beta term carry the softmax scale (log2 domain): a score is
+// rho_t times the MFMA column sum, whose accumulator starts at the beta term.
 template <int G>
 __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, int u, int n, int gq,
-                                             const half8_t (&qB)[4], float qb, float qk, KvState& st) {
-  float4_t s = {0.f, 0.f, 0.f, 0.f};
+                                             const half8_t (&qB)[4], float qbc, KvState& st) {
+  float4_t s = {qbc, qbc, qbc, qbc};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(r.k[kk], 512.0f), qB[kk], s, 0, 0, 0);
@@ -146,54 +151,49 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
   const float vbe[4] = {vb.x, vb.y, vb.z, vb.w};
 
   // column n < G: high half of head n; column G + n: its low half
-  float lg[4];
+  float t[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(row_shl<G>(__float_as_uint(s[i])));
-    lg[i] = rh[i] * (s[i] + lo + qb) * qk;
-  }
-  float p[4], pv[4], arg[4];
+  for (int i = 0; i < 4; ++i) t[i] = s[i] + __uint_as_float(row_shl<G>(__float_as_uint(s[i])));
+  float p[4], arg[4];
+  // P * v_scale as binary16 pairs in the V operand's token order (0, 2) and
+  // (1, 3): high halves h and remainders lo
+  uint32_t h02, h13, lo02, lo13;
+  auto weights = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arg[i] = lg[i] - st.m_run;
-    p[i] = __builtin_amdgcn_exp2f(arg[i]);
-    pv[i] = p[i] * vsc[i];
-  }
-  // P * v_scale above 2^8 or P itself above 2^64 (an exponent above 64; the
-  // exponent is +inf, never NaN, while the reference is still -inf)
+    for (int i = 0; i < 4; ++i) {
+      arg[i] = __builtin_fmaf(rh[i], t[i], -st.m_run);
+      p[i] = __builtin_amdgcn_exp2f(arg[i]);
+    }
+    split_products(p[0], vsc[0], p[2], vsc[2], h02, lo02);
+    split_products(p[1], vsc[1], p[3], vsc[3], h13, lo13);
+  };
+  weights();
+  // P * v_scale above 2^8 or P itself above 2^64.  The first is read off the
+  // binary16 high halves: P * v_scale >= 0, so their bit patterns order like
+  // their values (+inf past the binary16 range above every finite one), and a
+  // saturating subtraction of 2^8's pattern leaves a nonzero half exactly
+  // where a half exceeds 2^8.  The second is an exponent above 64 (+inf,
+  // never NaN, while the reference is still -inf).
   const float amax = fmaxf(fmaxf(arg[0], arg[1]), fmaxf(arg[2], arg[3]));
-  const float pvmax = fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3]));
-  const bool over = (amax > kPMaxLog2 || pvmax > kTauPow) && (n < G);
+  const u16x2_t hm = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, h02), __builtin_bit_cast(u16x2_t, h13));
+  const u16x2_t ex = __builtin_elementwise_sub_sat(hm, u16x2_t{kTauPowBits, kTauPowBits});
+  const bool over = (amax > kPMaxLog2 || __builtin_bit_cast(uint32_t, ex) != 0u) && (n < G);
 
   // P (high/low halves) times V into the output rows.  Both sides of the
   // rare rescale branch below run their own copy, so the accumulators are
   // never merged between the branches (which costs a register copy of every
   // accumulator on the common path).
   auto accumulate = [&]() {
-    half4_t ph, plo;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       st.l_run += p[i];
       st.pb += p[i] * vbe[i];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = pv[kTokOrder[i]];
-      const half_t hh = (half_t)x;
-      ph[i] = hh;
-      plo[i] = (half_t)(x - (float)hh);
-    }
-    const uint2 lob = __builtin_bit_cast(uint2, plo);
-    uint2 shifted;
-    shifted.x = row_shr<G>(lob.x);
-    shifted.y = row_shr<G>(lob.y);
-    half4_t pA;
-    if (n < G)
-      pA = ph;
-    else if (n < 2 * G)
-      pA = __builtin_bit_cast(half4_t, shifted);
-    else
-      pA = half4_t{0, 0, 0, 0};
+    // rows 0..G-1 keep their high halves, rows G..2G-1 take the remainders
+    // of rows 0..G-1 (rows past 2G hold values that no output row uses)
+    const uint32_t a0 = __builtin_amdgcn_update_dpp(h02, lo02, 0x110 + G, 0xF, 0xF, false);
+    const uint32_t a1 = __builtin_amdgcn_update_dpp(h13, lo13, 0x110 + G, 0xF, 0xF, false);
+    const half4_t pA = cat4(as_h2(a0), as_h2(a1));
     VCodes c0, c1;
     v_codes(r.v[0], c0);
     v_codes(r.v[1], c1);
@@ -205,11 +205,14 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
       st.o[4 + nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, v_operand(c1, nn), st.o[4 + nn], 0, 0, 0);
   };
 
-  if (__any(over)) {
+  if (__builtin_amdgcn_ballot_w64(over) != 0) {
     float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (n < G) mx = fmaxf(mx, fmaxf(lg[i] + __log2f(vsc[i]), lg[i] - kPMaxLog2));
+    for (int i = 0; i < 4; ++i) {
+      const float lg = rh[i] * t[i];
+      mx = fmaxf(mx, fmaxf(lg + __log2f(vsc[i]), lg - kPMaxLog2));
+    }
+    mx = n < G ? mx : kNegInf;
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m_run, mx);
@@ -227,11 +230,7 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.o[nn][i] *= ar[i];
     st.m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
-      pv[i] = p[i] * vsc[i];
-    }
+    weights();
     accumulate();
   } else {
     accumulate();
@@ -261,10 +260,12 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(p_begin + a.pages_per_split, n_pages);
 
-  // q~ = H q / sqrt(128) for the G heads, once per workgroup into LDS: wave w
-  // rotates heads w, w+4; lane l holds channels 2l and 2l+1, so the first
-  // butterfly stage is in-lane and the others pair lanes l and l ^ (h/2).
+  // q~ = H q / sqrt(128), times the softmax scale, for the G heads, once per
+  // workgroup into LDS: wave w rotates heads w, w+4; lane l holds channels
+  // 2l and 2l+1, so the first butterfly stage is in-lane and the others pair
+  // lanes l and l ^ (h/2).
   const bool lo_col = n >= G && n < 2 * G;
+  const float qscale = kInvSqrt128 * a.qk_scale;
   const int q_row = n < G ? n : (n < 2 * G ? n - G : G);  // row G of s_q is zero
   for (int h2 = w; h2 < G; h2 += kWaves) {
     const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + h2) * D + 2 * l;
@@ -279,8 +280,8 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
       x0 = (l & m) ? p0 - x0 : x0 + p0;
       x1 = (l & m) ? p1 - x1 : x1 + p1;
     }
-    s_q[h2][2 * l] = x0 * kInvSqrt128;
-    s_q[h2][2 * l + 1] = x1 * kInvSqrt128;
+    s_q[h2][2 * l] = x0 * qscale;
+    s_q[h2][2 * l + 1] = x1 * qscale;
   }
   if (tid < D) s_q[G][tid] = 0.0f;
   __syncthreads();
@@ -395,7 +396,8 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
         }
         qb += __shfl_xor(qb, 16);
         qb += __shfl_xor(qb, 32);
-        qb += __uint_as_float(row_shl<G>(__float_as_uint(qb)));  // columns n < G
+        qb += __uint_as_float(row_shl<G>(__float_as_uint(qb)));
+        const float qbc = n < G ? qb : 0.0f;  // score accumulators of the high columns start here
         // move the output into this page's gamma domain
         {
           const float4 g0 = *reinterpret_cast<const float4*>(mt + kVg + 8 * n);
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
           issue(u);
-          process_unit<G>(rr[u % kRing], mt, u, n, gq, qB, qb, a.qk_scale, st);
+          process_unit<G>(rr[u % kRing], mt, u, n, gq, qB, qbc, st);
         }
         // end of page: o' += sum_t p_t beta'_t (every channel of the head)
         float pbh = st.pb + __shfl_xor(st.pb, 16);
