@@ -205,11 +205,14 @@ template <int FMT, int D>
 __device__ __forceinline__ half4_t v_operand(const Raw<FMT, D>& r, int nn, half2_t s01, half2_t s23,
                                              const uint32_t (&pairs)[4]) {
   if constexpr (FMT == 6) {
-    // the channel's nibble of each of the 4 token bytes, as for the keys
+    // the channel's nibble of each of the 4 token bytes as code + 8, the
+    // same way as the keys; 8 times the sum of the weights is removed from
+    // each head's output once, after the last token
     const uint32_t w = r.v[nn / 2] ^ 0x88888888u;
     const uint32_t x = (nn & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
-    const half2_t k1032 = {(half_t)1032.0f, (half_t)1032.0f};
-    return cat4(as_h2(perm(0x64646464u, x, 0x04010400u)) - k1032, as_h2(perm(0x64646464u, x, 0x04030402u)) - k1032);
+    uint32_t lo, hi;
+    e4m3x4_to_h_scaled(x, 512.0f, lo, hi);
+    return cat4(as_h2(lo), as_h2(hi));
   } else if constexpr (FMT == 7) {
     // `pairs` already carry each token's block scale
     const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
@@ -235,6 +238,7 @@ template <int D>
 struct WaveState {
   float4_t acc[D / 16];
   float m_run, l_run;
+  float vb;  // INT4: sum of the weights P * v_scale (the value codes enter as code + 8)
 };
 
 template <int FMT, int D, int G>
@@ -281,16 +285,19 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
       }
   }
   // The reference m_run is always finite (it starts at kRefStart), so a
-  // masked score (-inf) gives exactly 0 without a select.
-  float p[4], pv[4];
-  bool over = false;
+  // masked score (-inf) gives exactly 0 without a select.  The weights
+  // P * v_scale enter the PV product as binary16 high halves h and
+  // remainders lo, two tokens per register.
+  float p[4];
+  uint32_t h01, h23, lo01, lo23;
+  auto weights = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
-    pv[i] = p[i] * vsc[i];
-    over |= !(pv[i] <= kTauPow);
-  }
-  over = over && (n < G);
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
+    split_products(p[0], vsc[0], p[1], vsc[1], h01, lo01);
+    split_products(p[2], vsc[2], p[3], vsc[3], h23, lo23);
+  };
+  weights();
+  const bool over = pairs_exceed_tau(h01, h23) && (n < G);
 
   // P (high/low halves) times V into the output rows.  Both sides of the
   // rare rescale branch below run their own copy, so the accumulators are
@@ -299,26 +306,10 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
   auto accumulate = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.l_run += p[i];
-    // P = hi + lo: hi = binary16(P) two at a time, lo = binary16 of the exact
-    // binary32 remainder P - hi (one fused multiply-add from the binary16 hi)
-    const half2_t h01 = __builtin_convertvector(float2_t{pv[0], pv[1]}, half2_t);
-    const half2_t h23 = __builtin_convertvector(float2_t{pv[2], pv[3]}, half2_t);
-    const float2_t r01 = {__builtin_fmaf(-(float)h01[0], 1.0f, pv[0]), __builtin_fmaf(-(float)h01[1], 1.0f, pv[1])};
-    const float2_t r23 = {__builtin_fmaf(-(float)h23[0], 1.0f, pv[2]), __builtin_fmaf(-(float)h23[1], 1.0f, pv[3])};
-    const half4_t ph = cat4(h01, h23);
-    const half4_t plo = cat4(__builtin_convertvector(r01, half2_t), __builtin_convertvector(r23, half2_t));
-    // rows G..2G-1 carry the binary16 remainder of rows 0..G-1
-    const uint2 lob = __builtin_bit_cast(uint2, plo);
-    uint2 shifted;
-    shifted.x = row_shr<G>(lob.x);
-    shifted.y = row_shr<G>(lob.y);
-    half4_t pA;
-    if (n < G)
-      pA = ph;
-    else if (n < 2 * G)
-      pA = __builtin_bit_cast(half4_t, shifted);
-    else
-      pA = half4_t{0, 0, 0, 0};
+    if constexpr (FMT == 6)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.vb += p[i] * vsc[i];
+    const half4_t pA = cat4(as_h2(hi_lo_rows<G>(h01, lo01)), as_h2(hi_lo_rows<G>(h23, lo23)));
     half2_t vs01 = {0, 0}, vs23 = {0, 0};
     if constexpr (FMT == 4) {
       uint32_t lo, hi;
@@ -342,7 +333,7 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     }
   };
 
-  if (__any(over)) {
+  if (__builtin_amdgcn_ballot_w64(over) != 0) {
     // move the reference to the exact maximum of score + log2(v_scale)
     float mx = kNegInf;
 #pragma unroll
@@ -353,6 +344,7 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = (m_new > st.m_run) ? exp2f(st.m_run - m_new) : 1.0f;
     st.l_run *= alpha;
+    st.vb *= alpha;
     float ar[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -364,11 +356,7 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.acc[nn][i] *= ar[i];
     st.m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m_run);
-      pv[i] = p[i] * vsc[i];
-    }
+    weights();
     accumulate();
   } else {
     accumulate();
@@ -385,6 +373,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   __shared__ float lds_o[W][2 * G][D];
   __shared__ float lds_m[W][16];
   __shared__ float lds_l[W][16];
+  __shared__ float lds_vb[W][16];
   __shared__ int s_pages[kPageChunk];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -441,6 +430,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   for (int nn = 0; nn < NV; ++nn) st.acc[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
   st.m_run = kRefStart;
   st.l_run = 0.0f;
+  st.vb = 0.0f;
 
   // This wave's pages: p_begin + w + 4*j, j < n_it.  Their block-table
   // entries are fetched 64 at a time into one VGPR (lane j holds entry j) and
@@ -507,9 +497,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   // ---- combine the W waves (and the hi/lo rows) in LDS
   float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
+  float vb_tot = 0.0f;
+  if constexpr (FMT == 6) {
+    vb_tot = st.vb + __shfl_xor(st.vb, 16);
+    vb_tot += __shfl_xor(vb_tot, 32);
+  }
   if (gq == 0) {
     lds_m[w][n] = st.m_run;
     lds_l[w][n] = l_tot;
+    if constexpr (FMT == 6) lds_vb[w][n] = 8.0f * vb_tot;
   }
 #pragma unroll
   for (int nn = 0; nn < NV; ++nn)
@@ -533,7 +529,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
       for (int ww = 0; ww < W; ++ww) {
         const float f = exp2f(lds_m[ww][g] - M);
         L += f * lds_l[ww][g];
-        O += f * (lds_o[ww][g][d] + lds_o[ww][g + G][d]);
+        float o = lds_o[ww][g][d] + lds_o[ww][g + G][d];
+        if constexpr (FMT == 6) o -= lds_vb[ww][g];
+        O += f * o;
       }
     }
     if (S == 1) {

@@ -71,6 +71,42 @@ __device__ __forceinline__ uint32_t row_shl(uint32_t v) {
   return __builtin_amdgcn_update_dpp(0u, v, 0x100 + G, 0xF, 0xF, false);
 }
 
+// Products x0 = a0 b0 and x1 = a1 b1 as binary16 pairs: h = (RN16 x0, RN16 x1)
+// and the remainders r = (RN16(x0 - h0), RN16(x1 - h1)).  Each value is one
+// mixed-precision fused multiply-add (binary32 inputs, binary16 result, the
+// remainder's subtrahend read straight from h's half), four instructions per
+// pair.
+__device__ __forceinline__ void split_products(float a0, float b0, float a1, float b1, uint32_t& h, uint32_t& r) {
+  asm("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
+      "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
+      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(h), "=&v"(r)
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+}
+
+// P's MFMA A operand: rows 0..G-1 keep their own binary16 high halves, rows
+// G..2G-1 take the remainders of rows 0..G-1 (one DPP move per register; rows
+// past 2G hold values that no output row uses).
+template <int G>
+__device__ __forceinline__ uint32_t hi_lo_rows(uint32_t hi, uint32_t lo) {
+  return __builtin_amdgcn_update_dpp(hi, lo, 0x110 + G, 0xF, 0xF, false);
+}
+
+// Whether a binary16 pair of non-negative weights P * v_scale, held in two
+// registers, has a value above kTauPow.  Non-negative binary16 numbers order
+// like their bit patterns (+inf, past the binary16 range, above every finite
+// one; a NaN above +inf), so a saturating subtraction of kTauPow's pattern
+// from the larger halves leaves a nonzero half exactly where one exceeds it.
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+constexpr uint16_t kTauPowBits = 0x5C00;  // binary16 2^8
+static_assert(kTauPow == 256.0f, "binary16 pattern of the weight bound");
+__device__ __forceinline__ bool pairs_exceed_tau(uint32_t a, uint32_t b) {
+  const u16x2_t m = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b));
+  const u16x2_t x = __builtin_elementwise_sub_sat(m, u16x2_t{kTauPowBits, kTauPowBits});
+  return __builtin_bit_cast(uint32_t, x) != 0u;
+}
+
 // Online merge of split partial records into (M, L, O) for one output
 // element: record s holds m at float g, l at kMaxGroup + g and the output row
 // value at o_off.  Splits are read 8 at a time, all loads of a group issued

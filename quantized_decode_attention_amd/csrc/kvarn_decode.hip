@@ -85,26 +85,9 @@ __device__ __forceinline__ half8_t k_operand(uint32_t w, float s512) {
 }
 __host__ __device__ constexpr int slot_channel(int i) { return i < 4 ? 2 * i : 2 * (i - 4) + 1; }
 
-// Products x0 = a0 b0 and x1 = a1 b1 as binary16 pairs: h = (RN16 x0, RN16 x1)
-// and the remainders r = (RN16(x0 - h0), RN16(x1 - h1)).  Each value is one
-// mixed-precision fused multiply-add (binary32 inputs, binary16 result, the
-// remainder's subtrahend read straight from h's half), four instructions per
-// pair.
-__device__ __forceinline__ void split_products(float a0, float b0, float a1, float b1, uint32_t& h, uint32_t& r) {
-  asm("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
-      "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
-      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-      : "=&v"(h), "=&v"(r)
-      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
-}
-
 // Beyond the binary16 bound on P * v_scale, the reference also keeps P itself
 // below 2^64: a KVarN per-token V scale can be 0.
 constexpr float kPMaxLog2 = 64.0f;
-constexpr uint16_t kTauPowBits = 0x5C00;  // binary16 2^8
-static_assert(kTauPow == 256.0f, "binary16 pattern of the P bound");
-typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 // V codes of one dword (byte m = channel m, bits 2k..2k+1 = token k) as
 // binary16.  A nibble 00cc is the E2M1 encoding of c / 2, so masking the
@@ -168,16 +151,11 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
     split_products(p[1], vsc[1], p[3], vsc[3], h13, lo13);
   };
   weights();
-  // P * v_scale above 2^8 or P itself above 2^64.  The first is read off the
-  // binary16 high halves: P * v_scale >= 0, so their bit patterns order like
-  // their values (+inf past the binary16 range above every finite one), and a
-  // saturating subtraction of 2^8's pattern leaves a nonzero half exactly
-  // where a half exceeds 2^8.  The second is an exponent above 64 (+inf,
-  // never NaN, while the reference is still -inf).
+  // P * v_scale above 2^8 (read off the binary16 high halves) or P itself
+  // above 2^64 (an exponent above 64; +inf, never NaN, while the reference is
+  // still -inf).
   const float amax = fmaxf(fmaxf(arg[0], arg[1]), fmaxf(arg[2], arg[3]));
-  const u16x2_t hm = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, h02), __builtin_bit_cast(u16x2_t, h13));
-  const u16x2_t ex = __builtin_elementwise_sub_sat(hm, u16x2_t{kTauPowBits, kTauPowBits});
-  const bool over = (amax > kPMaxLog2 || __builtin_bit_cast(uint32_t, ex) != 0u) && (n < G);
+  const bool over = (amax > kPMaxLog2 || pairs_exceed_tau(h02, h13)) && (n < G);
 
   // P (high/low halves) times V into the output rows.  Both sides of the
   // rare rescale branch below run their own copy, so the accumulators are
@@ -189,11 +167,7 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
       st.l_run += p[i];
       st.pb += p[i] * vbe[i];
     }
-    // rows 0..G-1 keep their high halves, rows G..2G-1 take the remainders
-    // of rows 0..G-1 (rows past 2G hold values that no output row uses)
-    const uint32_t a0 = __builtin_amdgcn_update_dpp(h02, lo02, 0x110 + G, 0xF, 0xF, false);
-    const uint32_t a1 = __builtin_amdgcn_update_dpp(h13, lo13, 0x110 + G, 0xF, 0xF, false);
-    const half4_t pA = cat4(as_h2(a0), as_h2(a1));
+    const half4_t pA = cat4(as_h2(hi_lo_rows<G>(h02, lo02)), as_h2(hi_lo_rows<G>(h13, lo13)));
     VCodes c0, c1;
     v_codes(r.v[0], c0);
     v_codes(r.v[1], c1);
