@@ -14,8 +14,11 @@ Also reported on the same line:
   write_mtok_s   whole-context quantise-on-write throughput (tokens/s / 1e6)
   roofline       decode (split kernel, plus the merge kernel when the context
                  is split): algorithmic KV bytes per launch / mean launch
-                 duration (HIP events around each decode call in the timed
-                 region, on the launch stream) against 8 TB/s
+                 duration (HIP events around each decode call, on the launch
+                 stream, over an instrumented pass of as many steps right
+                 after the timed ones: an event recorded between two launches
+                 holds the next one back by a few microseconds, so the timed
+                 steps carry only the pair around all of them) against 8 TB/s
   copy           a 1 GiB device-to-device copy (read + write bytes / time):
                  the achievable bandwidth beside the specification
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
@@ -152,29 +155,41 @@ class Problem:
         return n_tok / (ms * 1e-3) / 1e6, ms
 
     def time_steps(self, steps, warmup):
-        """Timed decode steps; returns (ms per step, mean decode launch ms).
-        The step index keeps counting across warm-up and timed steps."""
+        """Timed decode steps; returns (ms per step, mean decode call ms).
+        The timed region is `steps` steps bracketed by one event pair: an
+        event recorded between two launches holds the next launch back by a
+        few microseconds, so per-call events stay out of it.  The per-call
+        durations come from an instrumented pass of `steps` more steps right
+        after it (an event pair around every decode call).  The step index
+        keeps counting across warm-up, timed and instrumented steps."""
         import torch
         if self.kvarn:
-            self.prepare_incremental(warmup + steps)
+            self.prepare_incremental(warmup + 2 * steps)
             torch.cuda.synchronize()
         for i in range(warmup):
             self.append(i)
             self.decode(i)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
         for i in range(steps):
             self.append(warmup + i)
-            ev[i][0].record()
             self.decode(warmup + i)
-            ev[i][1].record()
         end.record()
         torch.cuda.synchronize()
         total = start.elapsed_time(end)
-        if self.kvarn:  # mean KV bytes (tiles + binary16 tail) of the timed steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            self.append(warmup + steps + i)
+            ev[i][0].record()
+            self.decode(warmup + steps + i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        if self.kvarn:  # mean KV bytes (tiles + binary16 tail) of the timed and of the instrumented steps
             self.kv_bytes = int(self.step_kv_bytes[warmup:warmup + steps].mean())
+            self.call_kv_bytes = int(self.step_kv_bytes[warmup + steps:warmup + 2 * steps].mean())
+        else:
+            self.call_kv_bytes = self.kv_bytes
         self.dec_ms = sorted(a.elapsed_time(b) for a, b in ev)
         return total / steps, sum(self.dec_ms) / len(self.dec_ms)
 
@@ -335,7 +350,7 @@ def main():
     log(f"[bench] whole-context write: {write_mtok:.1f} Mtok/s ({write_ms:.3f} ms)")
     ms_step, ms_dec = pb.time_steps(args.steps, args.warmup)
     value = pb.kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = pb.kv_bytes / (ms_dec * 1e-3) / 1e9
+    achieved = pb.call_kv_bytes / (ms_dec * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.1f} us ({value:.0f} GB/s), decode launch {ms_dec * 1e3:.1f} us "
         f"({achieved:.0f} GB/s, {achieved / HBM_PEAK_GBS:.1%} of peak)")
     sp, w = pb.sp, pb.w
@@ -369,7 +384,7 @@ def main():
             "kernel": f"decode_kernel<{pb.fmt}, {sp.D}, {sp.Hq // sp.Hkv}, "
                       f"{8 if pb.ws.num_splits == 1 and pb.fmt in (1, 2, 3) and w.B * sp.Hkv >= 256 else 4}>"
                       + (" + decode_merge_kernel" if pb.ws.num_splits > 1 else ""),
-            "algorithmic_bytes": pb.kv_bytes, "traffic_unit": "HBM bytes per decode call (rocprofv3 "
+            "algorithmic_bytes": pb.call_kv_bytes, "traffic_unit": "HBM bytes per decode call (rocprofv3 "
             "FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB copy)",
             "mean_launch_us": round(ms_dec * 1e3, 2),
             **pb.dec_percentiles_us(),
@@ -393,8 +408,8 @@ def main():
             wm, _ = p.time_write()
             ms_s, ms_d = p.time_steps(max(20, args.steps // 2), args.warmup)
             key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "")
-            fmts[key] = {"workload": name, "decode_gbs": round(p.kv_bytes / (ms_d * 1e-3) / 1e9, 1),
-                         "decode_frac_of_peak": round(p.kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            fmts[key] = {"workload": name, "decode_gbs": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9, 1),
+                         "decode_frac_of_peak": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "decode_us": round(ms_d * 1e3, 2), **p.dec_percentiles_us(), "step_us": round(ms_s * 1e3, 2),
                          "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits,
                          "step": ("append to the binary16 tail (tile quantised when complete) + decode over "
