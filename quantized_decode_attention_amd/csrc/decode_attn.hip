@@ -105,51 +105,47 @@ __device__ __forceinline__ LaneOffs lane_offsets(int gq, int n, int P) {
   return o;
 }
 
-template <int N>
-__device__ __forceinline__ void load_dwords_at(const uint8_t* base, uint32_t off, uint32_t* w) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) w[i] = ld_nt(base + off + 4 * i);
-}
-
 // Issue the loads of unit `sub` (16 tokens) of a chunk.  K: D/4 channels of
 // token row n starting at channel (D/4)*gq; V: channels (D/16)*n .. +D/16 of
-// tokens 4*gq .. 4*gq+3.
+// tokens 4*gq .. 4*gq+3.  The unit's position within the chunk is a scalar
+// offset.
 template <int FMT, int D>
 __device__ __forceinline__ void load_unit(const uint8_t* chunk, const ChunkGeom& g, int sub, const LaneOffs& lo,
                                           Raw<FMT, D>& r) {
   constexpr int DL = D / 4;
   constexpr int NV = D / 16;
+  const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(chunk, g.chunk_bytes);
   if constexpr (!kNibble<FMT>) {
     // coalesced 8-bit layout: piece h of all 64 lanes is one contiguous run
     constexpr int B = DL < 16 ? DL : 16;
-    const uint8_t* kb = chunk + (int64_t)16 * D * sub;
-    const uint8_t* vb = chunk + g.v_codes + (int64_t)16 * D * sub;
+    const int kb = 16 * D * sub;
+    const int vb = (int)g.v_codes + 16 * D * sub;
 #pragma unroll
-    for (int h = 0; h < DL / B; ++h) load_dwords_at<B / 4>(kb + 64 * B * h, lo.k, r.k + (B / 4) * h);
+    for (int h = 0; h < DL / B; ++h) buf_dwords<B / 4>(rs, lo.k, kb + 64 * B * h, r.k + (B / 4) * h);
 #pragma unroll
-    for (int h = 0; h < (4 * NV) / B; ++h) load_dwords_at<B / 4>(vb + 64 * B * h, lo.v, r.v + (B / 4) * h);
+    for (int h = 0; h < (4 * NV) / B; ++h) buf_dwords<B / 4>(rs, lo.v, vb + 64 * B * h, r.v + (B / 4) * h);
     if constexpr (FMT == 2 || FMT == 3) {
-      r.ks = ld_nt_f4(chunk + g.k_scales + 64 * sub + lo.ks);
-      r.vs = ld_nt_f4(chunk + g.v_scales + 64 * sub + lo.vs);
+      r.ks = buf_f4(rs, lo.ks, (int)g.k_scales + 64 * sub);
+      r.vs = buf_f4(rs, lo.vs, (int)g.v_scales + 64 * sub);
     }
   } else {
-    load_dwords_at<Raw<FMT, D>::KW>(chunk + (int64_t)sub * 16 * (D / 2), lo.k, r.k);
-    load_dwords_at<Raw<FMT, D>::VW>(chunk + g.v_codes + (int64_t)sub * 8 * D, lo.v, r.v);
+    buf_dwords<Raw<FMT, D>::KW>(rs, lo.k, sub * 16 * (D / 2), r.k);
+    buf_dwords<Raw<FMT, D>::VW>(rs, lo.v, (int)g.v_codes + sub * 8 * D, r.v);
     if constexpr (FMT == 4) {
-      const uint8_t* sp = chunk + g.k_scales + sub * 16 * (D / 16) + lo.ks;
+      const int so = (int)g.k_scales + sub * 16 * (D / 16);
       if constexpr (DL >= 32)
-        r.ksc = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp));
+        r.ksc = __builtin_amdgcn_raw_buffer_load_b16(rs, lo.ks, so, kLoadNt);
       else
-        r.ksc = __builtin_nontemporal_load(sp);
-      r.vsc = ld_nt(chunk + g.v_scales + 16 * sub + lo.vs);
+        r.ksc = __builtin_amdgcn_raw_buffer_load_b8(rs, lo.ks, so, kLoadNt);
+      r.vsc = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.vs, (int)g.v_scales + 16 * sub, kLoadNt);
     } else if constexpr (FMT == 7) {
       // the lane's D/4 key channels and D/16 value channels each lie in one
       // 32-channel block: one E8M0 byte for the key, one per token for V
-      r.ksc = __builtin_nontemporal_load(chunk + g.k_scales + sub * 16 * (D / 32) + lo.ks);
-      r.vsc = ld_nt(chunk + g.v_scales + 16 * sub + lo.vs);
+      r.ksc = __builtin_amdgcn_raw_buffer_load_b8(rs, lo.ks, (int)g.k_scales + sub * 16 * (D / 32), kLoadNt);
+      r.vsc = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.vs, (int)g.v_scales + 16 * sub, kLoadNt);
     } else {
-      r.ks = ld_nt_f4(chunk + g.k_scales + 64 * sub + lo.ks);
-      r.vs = ld_nt_f4(chunk + g.v_scales + 64 * sub + lo.vs);
+      r.ks = buf_f4(rs, lo.ks, (int)g.k_scales + 64 * sub);
+      r.vs = buf_f4(rs, lo.vs, (int)g.v_scales + 64 * sub);
     }
   }
 }
@@ -297,7 +293,7 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     split_products(p[2], vsc[2], p[3], vsc[3], h23, lo23);
   };
   weights();
-  const bool over = pairs_exceed_tau(h01, h23) && (n < G);
+  const bool over = pairs_exceed_tau(h01, h23) & (n < G);
 
   // P (high/low halves) times V into the output rows.  Both sides of the
   // rare rescale branch below run their own copy, so the accumulators are

@@ -53,6 +53,39 @@ __device__ __forceinline__ float4 ld_nt_f4(const uint8_t* p) {
                 __builtin_nontemporal_load(f + 3)};
 }
 
+// Buffer resource of one (page, kv head) chunk: base and size live in scalar
+// registers and a lane's load adds only its 32-bit byte offset, so no vector
+// address arithmetic runs per load; a load past the chunk's size returns 0.
+// Word 3 selects the raw 32-bit data format of CDNA buffer loads.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLoadNt = 2;  // cache policy of the streaming loads: nontemporal
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint8_t* chunk, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(chunk), 0, (int)bytes, kRsrcWord3);
+}
+// N dwords (N = 1, 2 or a multiple of 4) at byte voff + soff of the chunk
+template <int N>
+__device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff, uint32_t* w) {
+  if constexpr (N == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kLoadNt);
+  } else if constexpr (N == 2) {
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kLoadNt);
+    w[0] = x.x, w[1] = x.y;
+  } else {
+    static_assert(N % 4 == 0, "dword count");
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * i, soff, kLoadNt);
+      w[4 * i] = x.x, w[4 * i + 1] = x.y, w[4 * i + 2] = x.z, w[4 * i + 3] = x.w;
+    }
+  }
+}
+__device__ __forceinline__ float4 buf_f4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kLoadNt);
+  return float4{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+}
+
 template <int N>
 __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* w) {
 #pragma unroll

@@ -50,22 +50,22 @@ struct RawKv {
   uint32_t v[2];
 };
 
-// The lane's byte offsets within a sub-page (fixed for the kernel): the
-// wave-uniform part of an address stays in scalar registers.
+// The lane's byte offsets within a sub-page (fixed for the kernel); the
+// tile's base and size sit in a buffer resource in scalar registers, and a
+// sub-page's position in the tile is a scalar offset.
 struct LaneOffs {
   uint32_t k, v;
 };
 __device__ __forceinline__ LaneOffs lane_offsets(int n, int gq) { return {(uint32_t)(64 * n + 16 * gq), (uint32_t)(128 * gq + 8 * n)}; }
 
-template <int N>
-__device__ __forceinline__ void load_dwords_at(const uint8_t* base, uint32_t off, uint32_t* w) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) w[i] = ld_nt(base + off + 4 * i);
+__device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rs, int u, const LaneOffs& lo, RawKv& r) {
+  buf_dwords<4>(rs, lo.k, 1024 * u, r.k);
+  buf_dwords<2>(rs, lo.v, kVCodes + 512 * u, r.v);
 }
-
-__device__ __forceinline__ void load_kv(const uint8_t* chunk, int u, const LaneOffs& lo, RawKv& r) {
-  load_dwords_at<4>(chunk + 1024 * u, lo.k, r.k);
-  load_dwords_at<2>(chunk + kVCodes + 512 * u, lo.v, r.v);
+// the tile's 3 KB metadata block: 48 bytes per lane
+__device__ __forceinline__ void load_meta(__amdgpu_buffer_rsrc_t rs, int l, uint32_t (&m)[12]) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) buf_dwords<4>(rs, 16 * l, kMeta + 1024 * k, m + 4 * k);
 }
 
 // K operand of QK MFMA kk: the 8 codes of dword kk as binary16.  The low
@@ -155,7 +155,7 @@ __device__ __forceinline__ void process_unit(const RawKv& r, const float* mt, in
   // above 2^64 (an exponent above 64; +inf, never NaN, while the reference is
   // still -inf).
   const float amax = fmaxf(fmaxf(arg[0], arg[1]), fmaxf(arg[2], arg[3]));
-  const bool over = (amax > kPMaxLog2 || pairs_exceed_tau(h02, h13)) && (n < G);
+  const bool over = ((amax > kPMaxLog2) | pairs_exceed_tau(h02, h13)) & (n < G);  // no short-circuit branches
 
   // P (high/low halves) times V into the output rows.  Both sides of the
   // rare rescale branch below run their own copy, so the accumulators are
@@ -222,7 +222,8 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float s_q[G + 1][D];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, n = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int S = a.num_splits;
   const int64_t rec_floats = ws_record_floats(D);
 
@@ -295,15 +296,13 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
     bool vcur;
     const uint8_t* pc = page_ptr(0, vcur);
     uint32_t mreg[12];
-    load_dwords<4>(pc + kMeta + 16 * l, mreg);
-    load_dwords<4>(pc + kMeta + 1024 + 16 * l, mreg + 4);
-    load_dwords<4>(pc + kMeta + 2048 + 16 * l, mreg + 8);
+    load_meta(chunk_rsrc(pc, kTileBytes), l, mreg);
     // ring of kRing sub-page buffers, kRing-1 sub-pages in flight ahead of
     // the one being computed (the ring runs across page boundaries; 8 is a
     // multiple of kRing, so sub-page u of every page uses slot u % kRing)
     RawKv rr[kRing];
 #pragma unroll
-    for (int k = 0; k + 1 < kRing; ++k) load_kv(pc, k, lofs, rr[k]);
+    for (int k = 0; k + 1 < kRing; ++k) load_kv(chunk_rsrc(pc, kTileBytes), k, lofs, rr[k]);
 
     for (int j = 0; j < nj; ++j) {
       // publish this page's metadata to the wave's LDS block (same-wave LDS
@@ -320,14 +319,12 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
       auto issue = [&](int u) {
         const int ahead = u + kRing - 1;
         if (ahead < kUnits) {
-          load_kv(pc, ahead, lofs, rr[ahead % kRing]);
+          load_kv(chunk_rsrc(pc, kTileBytes), ahead, lofs, rr[ahead % kRing]);
         } else {
           if (ahead == kUnits) {
-            load_dwords<4>(pn + kMeta + 16 * l, mreg);
-            load_dwords<4>(pn + kMeta + 1024 + 16 * l, mreg + 4);
-            load_dwords<4>(pn + kMeta + 2048 + 16 * l, mreg + 8);
+            load_meta(chunk_rsrc(pn, kTileBytes), l, mreg);
           }
-          load_kv(pn, ahead - kUnits, lofs, rr[ahead % kRing]);
+          load_kv(chunk_rsrc(pn, kTileBytes), ahead - kUnits, lofs, rr[ahead % kRing]);
         }
         // keep the loads ahead of this sub-page's wait for its own data
         __builtin_amdgcn_sched_barrier(0);
