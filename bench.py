@@ -22,7 +22,9 @@ Also reported on the same line:
   copy           a 1 GiB device-to-device copy (read + write bytes / time):
                  the achievable bandwidth beside the specification
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
-  formats        the other formats' workloads (decode GB/s, write Mtok/s)
+  formats        the other formats' workloads (decode GB/s, write Mtok/s), and
+                 one GPU's share of the 16K workloads under two-way tensor
+                 parallelism (32 q / 4 kv heads)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -400,14 +402,15 @@ def main():
         others = [("fp8_sink_4k", K.KVQ_FP8_PER_TENSOR, 0), ("fp8_sink_4k", K.KVQ_FP8_PTH, 0),
                   ("nvfp4_16k", K.KVQ_NVFP4, 0), ("nvfp4_16k", K.KVQ_NVFP4, K.KVQ_FLAG_NVFP4_4OVER6),
                   ("nvfp4_16k", K.KVQ_MXFP4, 0), ("kvarn_16k", K.KVQ_KVARN_K4V2_G128, 0),
-                  ("int8_32k", K.KVQ_INT4_PTH, 0)]
+                  ("int8_32k", K.KVQ_INT4_PTH, 0),
+                  ("nvfp4_16k_tp2", K.KVQ_NVFP4, 0), ("kvarn_16k_tp2", K.KVQ_KVARN_K4V2_G128, 0)]
         for name, fmt, flags in others:
             if name == args.workload and fmt == main_fmt[0] and flags == main_fmt[1]:
                 continue
             p = Problem(K, name, fmt, flags)
             wm, _ = p.time_write()
             ms_s, ms_d = p.time_steps(max(20, args.steps // 2), args.warmup)
-            key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "")
+            key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "") + ("_tp2_share" if name.endswith("_tp2") else "")
             fmts[key] = {"workload": name, "decode_gbs": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9, 1),
                          "decode_frac_of_peak": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "decode_us": round(ms_d * 1e3, 2), **p.dec_percentiles_us(), "step_us": round(ms_s * 1e3, 2),

@@ -24,6 +24,8 @@ round-to-nearest-even):
                   Student-t with 4 degrees of freedom (drawn as Z / sqrt(chi2_4 / 4)).
   kvarn_16k       B=16, 64q/8kv, T=16384, D=128, page 128, seed 5005; K, V ~ N(0,1)
                   with 10 of the 1024 columns scaled x8.
+  nvfp4_16k_tp2,  one GPU's share of the two 16K workloads under tensor
+  kvarn_16k_tp2   parallelism over two GPUs: 32q/4kv, otherwise as above.
 
 Q ~ N(0,1) for all.  The block tables are a random permutation of all pool pages
 (exactly B*T/P pages), so every sequence's pages are scattered.
@@ -57,6 +59,10 @@ SPECS = {
     "int8_32k": Spec("int8_32k", (INT8_PTH,), 8, 64, 8, 32768, 128, 16, 3003, "chan10"),
     "nvfp4_16k": Spec("nvfp4_16k", (NVFP4,), 16, 64, 8, 16384, 128, 16, 4004, "student_t4"),
     "kvarn_16k": Spec("kvarn_16k", (KVARN_K4V2_G128,), 16, 64, 8, 16384, 128, 128, 5005, "chan8"),
+    # one GPU's share of the 16K workloads under tensor parallelism over two
+    # GPUs (half the kv heads, each with all of its query heads)
+    "nvfp4_16k_tp2": Spec("nvfp4_16k_tp2", (NVFP4,), 16, 32, 4, 16384, 128, 16, 4004, "student_t4"),
+    "kvarn_16k_tp2": Spec("kvarn_16k_tp2", (KVARN_K4V2_G128,), 16, 32, 4, 16384, 128, 128, 5005, "chan8"),
 }
 
 
