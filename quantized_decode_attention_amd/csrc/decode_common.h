@@ -150,22 +150,30 @@ __device__ __forceinline__ void merge_splits(const float* recs, int64_t rf, int 
     float m[8], l[8], o[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+      // splits past S reread split s0 (in bounds) and are dropped by their
+      // max; every load is unconditional, so all of them are in flight before
+      // the first use
       const bool in = s0 + k < S;
       const float* r = recs + (int64_t)(in ? s0 + k : s0) * rf;
-      m[k] = in ? r[g] : kNegInf;
+      const float mv = r[g];
+      m[k] = in ? mv : kNegInf;
       l[k] = r[kMaxGroup + g];
       o[k] = r[o_off];
     }
     float mc = M;
 #pragma unroll
     for (int k = 0; k < 8; ++k) mc = fmaxf(mc, m[k]);
-    if (mc == kNegInf) continue;
-    const float sc = exp2f(M - mc);
+    // No branch on an all-empty group (a branch would let the compiler sink
+    // the l and o loads below it, a second round trip): with every m = -inf
+    // any finite reference gives weights 0, and an empty split's l and o are
+    // 0, so (L, O) stay (0, 0).
+    const float mr = mc == kNegInf ? 0.0f : mc;
+    const float sc = exp2f(M - mr);
     L *= sc;
     O *= sc;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float f = exp2f(m[k] - mc);
+      const float f = exp2f(m[k] - mr);
       L += f * l[k];
       O += f * o[k];
     }

@@ -499,22 +499,27 @@ __global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
   const int n_tail = a.tail ? ctx % P : 0;
   const int hq = kvh * a.G + g;
 
+  // the tail's loads are issued first, so they are in flight while the
+  // split partials make their own round trip
+  const int r = t >> 4, c = t & 15;
+  half8_t kv[NR], vv[NR], qv;
+  if (n_tail > 0) {  // uniform across the block
+    const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + r) * D + 8 * c;
+    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P + r) * D + 8 * c;
+    // every row below 128 is inside the tail buffer; rows at or past the
+    // tail length are loaded but carry no weight
+#pragma unroll
+    for (int i = 0; i < NR; ++i) kv[i] = *reinterpret_cast<const half8_t*>(kt + (int64_t)8 * i * D);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) vv[i] = *reinterpret_cast<const half8_t*>(vt + (int64_t)8 * i * D);
+    qv = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)b * a.Hq + hq) * D + 8 * c);
+  }
+
   float M = kNegInf, L = 0.0f, O = 0.0f;
   merge_splits(recs, rf, S, g, 2 * kMaxGroup + g * D + t, M, L, O);
 
   float ot = 0.0f;
   if (n_tail > 0) {  // uniform across the block
-    const int r = t >> 4, c = t & 15;
-    const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + r) * D + 8 * c;
-    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P + r) * D + 8 * c;
-    // every row below 128 is inside the tail buffer; rows at or past the
-    // tail length are loaded but carry no weight
-    half8_t kv[NR], vv[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) kv[i] = *reinterpret_cast<const half8_t*>(kt + (int64_t)8 * i * D);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) vv[i] = *reinterpret_cast<const half8_t*>(vt + (int64_t)8 * i * D);
-    const half8_t qv = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)b * a.Hq + hq) * D + 8 * c);
     float lg[NR];
     float mloc = kNegInf;
 #pragma unroll
