@@ -144,40 +144,53 @@ __device__ __forceinline__ bool pairs_exceed_tau(uint32_t a, uint32_t b) {
 // element: record s holds m at float g, l at kMaxGroup + g and the output row
 // value at o_off.  Splits are read 8 at a time, all loads of a group issued
 // before any is used; empty splits have m = -inf and contribute nothing.
+struct RecGroup {
+  float m[8], l[8], o[8];
+};
+
+// Loads of splits s0 .. s0+7.  Splits past S reread split s0 (in bounds) and
+// are dropped by their max; every load is unconditional, so all of them are
+// in flight before the first use.
+__device__ __forceinline__ void load_recs(const float* recs, int64_t rf, int S, int s0, int g, int64_t o_off,
+                                          RecGroup& r) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bool in = s0 + k < S;
+    const float* rec = recs + (int64_t)(in ? s0 + k : s0) * rf;
+    const float mv = rec[g];
+    r.m[k] = in ? mv : kNegInf;
+    r.l[k] = rec[kMaxGroup + g];
+    r.o[k] = rec[o_off];
+  }
+}
+
+__device__ __forceinline__ void merge_recs(const RecGroup& r, float& M, float& L, float& O) {
+  float mc = M;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) mc = fmaxf(mc, r.m[k]);
+  // No branch on an all-empty group (a branch would let the compiler sink
+  // the l and o loads below it, a second round trip): with every m = -inf
+  // any finite reference gives weights 0, and an empty split's l and o are
+  // 0, so (L, O) stay (0, 0).
+  const float mr = mc == kNegInf ? 0.0f : mc;
+  const float sc = exp2f(M - mr);
+  L *= sc;
+  O *= sc;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float f = exp2f(r.m[k] - mr);
+    L += f * r.l[k];
+    O += f * r.o[k];
+  }
+  M = mc;
+}
+
 __device__ __forceinline__ void merge_splits(const float* recs, int64_t rf, int S, int g, int64_t o_off,
                                              float& M, float& L, float& O) {
   for (int s0 = 0; s0 < S; s0 += 8) {
-    float m[8], l[8], o[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      // splits past S reread split s0 (in bounds) and are dropped by their
-      // max; every load is unconditional, so all of them are in flight before
-      // the first use
-      const bool in = s0 + k < S;
-      const float* r = recs + (int64_t)(in ? s0 + k : s0) * rf;
-      const float mv = r[g];
-      m[k] = in ? mv : kNegInf;
-      l[k] = r[kMaxGroup + g];
-      o[k] = r[o_off];
-    }
-    float mc = M;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mc = fmaxf(mc, m[k]);
-    // No branch on an all-empty group (a branch would let the compiler sink
-    // the l and o loads below it, a second round trip): with every m = -inf
-    // any finite reference gives weights 0, and an empty split's l and o are
-    // 0, so (L, O) stay (0, 0).
-    const float mr = mc == kNegInf ? 0.0f : mc;
-    const float sc = exp2f(M - mr);
-    L *= sc;
-    O *= sc;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float f = exp2f(m[k] - mr);
-      L += f * l[k];
-      O += f * o[k];
-    }
-    M = mc;
+    RecGroup r;
+    load_recs(recs, rf, S, s0, g, o_off, r);
+    merge_recs(r, M, L, O);
   }
 }
 

@@ -454,125 +454,185 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   }
 }
 
-// Block-wide reductions over the 128 threads of the merge kernel.
-__device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(red[0], red[1]);
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return red[0] + red[1];
-}
-
-// Merge of one (sequence, q head): the split partials (rotated basis), the
-// binary16 tail tokens (original basis), and the rotation back:
-//   M = max(m_s, tail scores), L = sum 2^(m_s-M) l_s + sum_t 2^(s_t-M),
-//   o = ( H sum 2^(m_s-M) o_s + sum_t 2^(s_t-M) v_t ) / L.
-// 128 threads; for the partials and the output thread d owns channel d.  The
-// partials are read in one round trip per 8 splits; the inverse rotation runs
-// as six in-wave butterfly stages and one exchange between the waves.
-// Tail: thread (row group r = t/16, channel group c = t%16) loads 8 channels
-// (16 bytes) of tail rows r, r+8, ..., r+120 of both K and V, all requests in
-// flight at once; a row's score is the sum over the 16 lanes of its group
-// (in-wave butterflies, which leave it in every lane), and the value sum is
-// reduced over the 8 row groups in LDS.
-__global__ __launch_bounds__(128) void kvarn_merge_kernel(DecodeArgs a) {
-  constexpr int NR = P / 8;  // tail rows per thread
-  __shared__ float part[8][D];
-  __shared__ float xch[D];
-  __shared__ float red[2];
-  const int kvh = blockIdx.x, b = blockIdx.y, g = blockIdx.z, t = threadIdx.x;
+// Merge of one (sequence, kv head), all G of its query heads: the binary16
+// tail tokens (original basis), the split partials (rotated basis) and the
+// rotation back:
+//   M = max(m_s, m_tail), L = sum 2^(m_s-M) l_s + 2^(m_tail-M) l_tail,
+//   o = ( H sum 2^(m_s-M) o_s + 2^(m_tail-M) o_tail ) / L.
+// Four waves.  The tail is read once for the whole group: wave w attends
+// tail rows 16w .. 16w+15 and 16(w+4) .. 16(w+4)+15 with the same two MFMA
+// products as the split kernel's sub-pages (K as the A operand of S^T = K Q^T,
+// P as the A operand of O = P V), K, V and q entering as the binary16 values
+// they are and P as binary16 high halves plus remainders.  A wave first takes
+// the maximum of its 32 scores per head, so every weight is at most 1 and no
+// rescale is needed.  The waves' partials meet in LDS.  Then wave w finishes
+// heads w, w+4: lane l holds channels l and l+64, merges the split records
+// for them, applies the inverse rotation (in-lane stage 64, shuffles for the
+// others) and adds the tail.
+template <int G>
+__global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
+  __shared__ float lds_o[kWaves][2 * G][D];
+  __shared__ float lds_m[kWaves][16];
+  __shared__ float lds_l[kWaves][16];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, l = tid & 63, n = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.num_splits;
   const int64_t rf = ws_record_floats(D);
-  const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
-  int ctx = a.ctx_lens[b];
+  int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
   const int n_tail = a.tail ? ctx % P : 0;
-  const int hq = kvh * a.G + g;
 
-  // the tail's loads are issued first, so they are in flight while the
-  // split partials make their own round trip
-  const int r = t >> 4, c = t & 15;
-  half8_t kv[NR], vv[NR], qv;
-  if (n_tail > 0) {  // uniform across the block
-    const uint16_t* kt = a.tail + ((((int64_t)b * 2 + 0) * a.H + kvh) * P + r) * D + 8 * c;
-    const uint16_t* vt = a.tail + ((((int64_t)b * 2 + 1) * a.H + kvh) * P + r) * D + 8 * c;
-    // every row below 128 is inside the tail buffer; rows at or past the
-    // tail length are loaded but carry no weight
+  // the first 8 split records of the wave's heads, requested before the
+  // tail is read so both round trips overlap
+  const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
+  RecGroup rg[2][2];  // [head w + 4j][channel l, l + 64]
 #pragma unroll
-    for (int i = 0; i < NR; ++i) kv[i] = *reinterpret_cast<const half8_t*>(kt + (int64_t)8 * i * D);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) vv[i] = *reinterpret_cast<const half8_t*>(vt + (int64_t)8 * i * D);
-    qv = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)b * a.Hq + hq) * D + 8 * c);
+  for (int j = 0; j < 2; ++j) {
+    const int g = w + kWaves * j;
+    if (g < G) {  // uniform per wave
+      load_recs(recs, rf, S, 0, g, 2 * kMaxGroup + g * D + l, rg[j][0]);
+      load_recs(recs, rf, S, 0, g, 2 * kMaxGroup + g * D + l + 64, rg[j][1]);
+    }
   }
 
-  float M = kNegInf, L = 0.0f, O = 0.0f;
-  merge_splits(recs, rf, S, g, 2 * kMaxGroup + g * D + t, M, L, O);
-
-  float ot = 0.0f;
   if (n_tail > 0) {  // uniform across the block
-    float lg[NR];
-    float mloc = kNegInf;
+    const uint16_t* kt = a.tail + (((int64_t)b * 2 + 0) * a.H + kvh) * P * D;
+    const uint16_t* vt = a.tail + (((int64_t)b * 2 + 1) * a.H + kvh) * P * D;
+    // B operand Q^T: column n = head n (zero beyond G), rows = channels
+    // 32 gq + 8 kk .. +7, as the K operand below
+    half8_t qB[4];
+    {
+      const half8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+      const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + (n < G ? n : 0)) * D + 32 * gq;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)kv[i][e] * (float)qv[e];
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-      lg[i] = r + 8 * i < n_tail ? acc * a.qk_scale : kNegInf;
-      mloc = fmaxf(mloc, lg[i]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8_t v = *reinterpret_cast<const half8_t*>(qp + 8 * kk);
+        qB[kk] = n < G ? v : z;
+      }
     }
-    const float mt = block_max(mloc, red);
+    // rows 16u + n (K: channels 32 gq .. +31) and 16u + 4 gq + i (V:
+    // channels 8n .. 8n+7) of the wave's two sub-pages; every row below 128
+    // is inside the tail buffer, rows at or past the tail length get weight 0
+    half8_t kr[2][4], vr[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = w + kWaves * h;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kr[h][kk] = *reinterpret_cast<const half8_t*>(kt + (int64_t)(16 * u + n) * D + 32 * gq + 8 * kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vr[h][i] = *reinterpret_cast<const half8_t*>(vt + (int64_t)(16 * u + 4 * gq + i) * D + 8 * n);
+    }
+    float lg[2][4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[h][kk], qB[kk], s, 0, 0, 0);
+      const int row0 = 16 * (w + kWaves * h) + 4 * gq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lg[h][i] = row0 + i < n_tail ? s[i] * a.qk_scale : kNegInf;
+        mx = fmaxf(mx, lg[h][i]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mref = mx == kNegInf ? 0.0f : mx;  // a wave with no tail row: every weight 0
+    float4_t acc[D / 16];
+#pragma unroll
+    for (int nn = 0; nn < D / 16; ++nn) acc[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.0f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const bool live = lg[i] != kNegInf;
-      const float e = live ? exp2f(lg[i] - mt) : 0.0f;
-      lsum += e;
+    for (int h = 0; h < 2; ++h) {
+      float p[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += live ? e * (float)vv[i][j] : 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(lg[h][i] - mref);
+        lsum += p[i];
+      }
+      uint32_t h01, h23, lo01, lo23;
+      split_products(p[0], 1.0f, p[1], 1.0f, h01, lo01);
+      split_products(p[2], 1.0f, p[3], 1.0f, h23, lo23);
+      const half4_t pA = cat4(as_h2(hi_lo_rows<G>(h01, lo01)), as_h2(hi_lo_rows<G>(h23, lo23)));
+#pragma unroll
+      for (int nn = 0; nn < D / 16; ++nn) {
+        const half4_t vB = {vr[h][0][nn], vr[h][1][nn], vr[h][2][nn], vr[h][3][nn]};
+        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(pA, vB, acc[nn], 0, 0, 0);
+      }
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (gq == 0) {
+      lds_m[w][n] = mx;
+      lds_l[w][n] = lsum;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) part[r][8 * c + j] = acc[j];
-    // each row's weight is held by all 16 lanes of its group: count it once
-    const float lt = block_sum(c == 0 ? lsum : 0.0f, red);  // its barriers also publish part
+    for (int nn = 0; nn < D / 16; ++nn)
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) ot += part[rr][t];
-    const float mx = fmaxf(M, mt);
-    const float sp = exp2f(M - mx), st = exp2f(mt - mx);
-    L = L * sp + lt * st;
-    O *= sp;
-    ot *= st;
-    M = mx;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * gq + i;
+        if (row < 2 * G) lds_o[w][row][8 * n + nn] = acc[nn][i];
+      }
   }
-  uint16_t* orow = a.out + ((int64_t)b * a.Hq + hq) * D;
-  if (M == kNegInf) {  // empty context (uniform)
-    orow[t] = 0;
-    return;
-  }
-  // inverse rotation of the split part across the 128 channels
-#pragma unroll
-  for (int hb = 1; hb < 64; hb <<= 1) {
-    const float p = __shfl_xor(O, hb);
-    O = (t & hb) ? p - O : O + p;
-  }
-  xch[t] = O;
   __syncthreads();
-  const float p = xch[t ^ 64];
-  O = (t & 64) ? p - O : O + p;
-  const float out = (O * kInvSqrt128 + ot) / L;
-  orow[t] = __builtin_bit_cast(uint16_t, (half_t)out);
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int g = w + kWaves * j;
+    if (g >= G) continue;  // uniform per wave
+    float M = kNegInf, L = 0.0f, O0 = 0.0f, O1 = 0.0f;
+    float M1 = kNegInf, L1 = 0.0f;
+    merge_recs(rg[j][0], M, L, O0);
+    merge_recs(rg[j][1], M1, L1, O1);
+    for (int s0 = 8; s0 < S; s0 += 8) {
+      RecGroup r0, r1;
+      load_recs(recs, rf, S, s0, g, 2 * kMaxGroup + g * D + l, r0);
+      load_recs(recs, rf, S, s0, g, 2 * kMaxGroup + g * D + l + 64, r1);
+      merge_recs(r0, M, L, O0);
+      merge_recs(r1, M1, L1, O1);
+    }
+    // the tail partial of head g over the four waves
+    float Mt = kNegInf, Lt = 0.0f, T0 = 0.0f, T1 = 0.0f;
+    if (n_tail > 0) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) Mt = fmaxf(Mt, lds_m[ww][g]);
+      if (Mt != kNegInf) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float f = exp2f(lds_m[ww][g] - Mt);
+          Lt += f * lds_l[ww][g];
+          T0 += f * (lds_o[ww][g][l] + lds_o[ww][g + G][l]);
+          T1 += f * (lds_o[ww][g][l + 64] + lds_o[ww][g + G][l + 64]);
+        }
+      }
+    }
+    const float mx = fmaxf(M, Mt);
+    uint16_t* orow = a.out + ((int64_t)b * a.Hq + kvh * G + g) * D;
+    if (mx == kNegInf) {  // empty context (uniform)
+      orow[l] = 0;
+      orow[l + 64] = 0;
+      continue;
+    }
+    const float sp = exp2f(M - mx), st = exp2f(Mt - mx);
+    L = L * sp + Lt * st;
+    O0 *= sp;
+    O1 *= sp;
+    // inverse rotation of the split part across the 128 channels: stages
+    // 1 .. 32 pair lanes l and l ^ h, stage 64 pairs the lane's two channels
+#pragma unroll
+    for (int hb = 1; hb < 64; hb <<= 1) {
+      const float p0 = __shfl_xor(O0, hb), p1 = __shfl_xor(O1, hb);
+      O0 = (l & hb) ? p0 - O0 : O0 + p0;
+      O1 = (l & hb) ? p1 - O1 : O1 + p1;
+    }
+    const float r0 = O0 + O1, r1 = O0 - O1;
+    orow[l] = __builtin_bit_cast(uint16_t, (half_t)((r0 * kInvSqrt128 + T0 * st) / L));
+    orow[l + 64] = __builtin_bit_cast(uint16_t, (half_t)((r1 * kInvSqrt128 + T1 * st) / L));
+  }
 }
 
 }  // namespace
@@ -610,7 +670,13 @@ hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  kvarn_merge_kernel<<<dim3((unsigned)a.H, (unsigned)a.B, (unsigned)a.G), 128, 0, s>>>(a);
+  const dim3 mgrid((unsigned)a.H, (unsigned)a.B);
+  switch (a.G) {
+    case 1: kvarn_merge_kernel<1><<<mgrid, 256, 0, s>>>(a); break;
+    case 2: kvarn_merge_kernel<2><<<mgrid, 256, 0, s>>>(a); break;
+    case 4: kvarn_merge_kernel<4><<<mgrid, 256, 0, s>>>(a); break;
+    case 8: kvarn_merge_kernel<8><<<mgrid, 256, 0, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 
