@@ -264,15 +264,18 @@ __device__ __forceinline__ void e2m1_encode16(const float* y, uint32_t (&w)[2]) 
   }
 }
 
-// Codes of one block for block-scale code sb, with the squared reconstruction
-// error summed by the balanced tree over the block's index order.  The
-// quotients keep x's sign on zero; the reconstructions come back exactly
-// through the hardware E2M1 -> binary16 conversion.
+// Codes of one block for block-scale code sb and, when ERR (the 4over6
+// choice needs it), the squared reconstruction error summed by the balanced
+// tree over the block's index order.  The quotients keep x's sign on zero;
+// the reconstructions come back exactly through the hardware E2M1 -> binary16
+// conversion.
+template <bool ERR>
 __device__ __forceinline__ float nvfp4_block(const float* x, float st, uint32_t sb, uint32_t (&w)[2]) {
   const float sbv = e4m3_val(sb);
   float e2[16];
   if (sbv == 0.0f) {
     w[0] = w[1] = 0u;
+    if constexpr (!ERR) return 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) e2[i] = x[i] * x[i];
   } else {
@@ -282,6 +285,7 @@ __device__ __forceinline__ float nvfp4_block(const float* x, float st, uint32_t 
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = __builtin_copysignf(div_rn(x[i], d, rc), x[i]);
     e2m1_encode16(y, w);
+    if constexpr (!ERR) return 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t v[4];
@@ -315,16 +319,18 @@ __device__ __forceinline__ uint32_t nvfp4_encode_block(const float* x, float st,
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
   uint32_t sb = e4m3_mag((amax / 6.0f) / st);
   uint32_t w[2];
-  const float err6 = nvfp4_block(x, st, sb, w);
   if (flags & 1) {
+    const float err6 = nvfp4_block<true>(x, st, sb, w);
     const uint32_t sb4 = e4m3_mag((amax / 4.0f) / st);
     uint32_t w4[2];
-    const float err4 = nvfp4_block(x, st, sb4, w4);
+    const float err4 = nvfp4_block<true>(x, st, sb4, w4);
     if (err4 < err6) {
       sb = sb4;
       w[0] = w4[0];
       w[1] = w4[1];
     }
+  } else {
+    nvfp4_block<false>(x, st, sb, w);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) byte[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
