@@ -147,9 +147,12 @@ def test_kvarn_decode_matches_oracle(K, O, G):
     sm = 1.0 / math.sqrt(D)
     ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, sm, tail16=tail)
     cache_dev = dev(cache)
-    for splits in (0, 1, 3, 7):
+    # 10 splits of one tile each: more than one group of 8 partial records
+    for splits in (0, 1, 3, 7, 10):
         log(f"kvarn decode G={G} splits={splits}")
-        got, _ = gpu_decode(K, lay, cache_dev, q16, bt, ctx, sm, tail16=tail, num_splits=splits)
+        got, ws = gpu_decode(K, lay, cache_dev, q16, bt, ctx, sm, tail16=tail, num_splits=splits)
+        if splits == 10:
+            assert ws.num_splits == 10
         assert_attn_close(got, ref, f"splits={splits}")
         ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
         assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-4 + 1e-4 * np.abs(ref))
