@@ -348,11 +348,15 @@ __device__ __forceinline__ float int4_encode_block(const float* x, uint32_t* byt
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
   const float s = fmaxf(group_max<NB>(amax), 1e-8f) / 7.0f;
   const Recip rc = make_recip(s);
+  // The clamp to [-7, 7] comes first (integer bounds, so it commutes with
+  // the rounding); adding 1.5 * 2^23 then rounds to an integer with ties to
+  // even and leaves it, in two's complement, in the low mantissa bits of the
+  // sum, whose low 4 bits are the nibble.
   uint32_t nib[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float q = fminf(fmaxf(__builtin_rintf(div_rn(x[i], s, rc)), -7.0f), 7.0f);
-    nib[i] = (uint32_t)(int32_t)q & 15u;
+    const float yc = __builtin_amdgcn_fmed3f(div_rn(x[i], s, rc), -7.0f, 7.0f);
+    nib[i] = __float_as_uint(yc + 12582912.0f) & 15u;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) byte[i] = nib[2 * i] | (nib[2 * i + 1] << 4);
