@@ -271,6 +271,14 @@ def measured_traffic(workload):
         return None
 
 
+def cpu_formats(K):
+    """The other formats' workloads for --cpu-formats (the headline's is added first)."""
+    return [("fp8_sink_4k", K.KVQ_FP8_PER_TENSOR, 0), ("fp8_sink_4k", K.KVQ_FP8_PTH, 0),
+            ("nvfp4_16k", K.KVQ_NVFP4, 0), ("nvfp4_16k", K.KVQ_NVFP4, K.KVQ_FLAG_NVFP4_4OVER6),
+            ("nvfp4_16k", K.KVQ_MXFP4, 0), ("kvarn_16k", K.KVQ_KVARN_K4V2_G128, 0),
+            ("int8_32k", K.KVQ_INT4_PTH, 0)]
+
+
 def cpu_baseline(name, fmt, flags, n_seq, threads):
     """The oracle on a bounded sample of the workload: quantise-write every
     token of n_seq sequences, then decode every q head of those sequences.
@@ -328,6 +336,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-formats", action="store_true", help="skip the other formats' workloads")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences of the CPU baseline (0 = the whole batch)")
+    ap.add_argument("--cpu-formats", action="store_true",
+                    help="also time the oracle on every format's workload (whole batch on the host threads, "
+                         "and one sequence on one thread); adds about a minute")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -428,6 +439,16 @@ def main():
         import workloads
         n_seq = args.cpu_seqs or workloads.SPECS[args.workload].B
         result["cpu_baseline"] = cpu_baseline(args.workload, *main_fmt, n_seq, threads)
+    if args.cpu_formats:
+        import workloads
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        cpu = {}
+        for name, fmt, flags in [(args.workload, *main_fmt)] + cpu_formats(K):
+            key = f"{name}/{K.FORMAT_NAMES[fmt]}" + ("_4over6" if flags else "")
+            log(f"[bench] oracle timing {key} ...")
+            cpu[key] = {"all_threads": cpu_baseline(name, fmt, flags, workloads.SPECS[name].B, threads),
+                        "one_thread": cpu_baseline(name, fmt, flags, 1, 1)}
+        result["cpu_formats"] = cpu
     print(json.dumps(result), flush=True)
 
 
