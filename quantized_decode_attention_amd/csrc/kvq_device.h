@@ -19,7 +19,6 @@ typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
@@ -150,29 +149,6 @@ __device__ __forceinline__ void i8x4_to_h_biased(uint32_t w, half2_t& lo, half2_
   uint32_t u = w ^ 0x80808080u;
   lo = as_h2(perm(0x64646464u, u, 0x04010400u));
   hi = as_h2(perm(0x64646464u, u, 0x04030402u));
-}
-
-// Four E4M3 bytes -> two binary16 pairs.  Placing sign and magnitude bits
-// into the binary16 fields gives value * 2^-8 (subnormals included); the
-// multiplication by 256 is exact and brings every value into the normal
-// range.
-__device__ __forceinline__ void e4m3x4_to_h(uint32_t w, half2_t& lo, half2_t& hi) {
-  const half2_t k256 = {(half_t)256.0f, (half_t)256.0f};
-  uint32_t t0 = perm(0u, w, 0x010C000Cu);  // (b0 << 8, b1 << 8) in the two halves
-  uint32_t t1 = perm(0u, w, 0x030C020Cu);  // (b2 << 8, b3 << 8)
-  uint32_t h0 = (t0 & 0x80008000u) | ((t0 >> 1) & 0x3F803F80u);
-  uint32_t h1 = (t1 & 0x80008000u) | ((t1 >> 1) & 0x3F803F80u);
-  lo = as_h2(h0) * k256;
-  hi = as_h2(h1) * k256;
-}
-
-// Four E2M1 nibbles held in the low nibbles of the bytes of n (high nibbles
-// zero) -> the binary16 high bytes of their values, by table lookup: the
-// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 have binary16 high bytes 00, 38, 3C,
-// 3E, 40, 42, 44, 46 and zero low bytes.  Sign bit 3 moves to bit 7.
-__device__ __forceinline__ uint32_t e2m1x4_hibytes(uint32_t n) {
-  uint32_t mag = perm(0x46444240u, 0x3E3C3800u, n & 0x07070707u);
-  return mag | ((n & 0x08080808u) << 4);
 }
 
 // ---------------------------------------------------------------------------
