@@ -28,7 +28,7 @@
 // one contiguous run of D/4 codes of one token, and each lane's V bytes are
 // one contiguous run holding four consecutive tokens per channel, so loads
 // are 16-byte vectors that together cover whole 128-byte lines and need no
-// LDS staging.
+// LDS staging.  Loads are raw buffer loads from a per-chunk resource.
 //
 // Splits: with more than one, each workgroup writes its partial (m, l, O) to
 // the workspace and a second, small kernel merges the partials of every
@@ -71,10 +71,10 @@ __device__ __forceinline__ void zero_raw(Raw<FMT, D>& r) {
   r.ks = r.vs = float4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Per-lane byte offsets of a unit's loads, fixed for the whole kernel: the
-// unit's position (page, 16-token group) enters through a wave-uniform base
-// pointer, so every load is a global load with a scalar base and a 32-bit
-// vector offset, and no 64-bit address arithmetic runs per unit.
+// Per-lane byte offsets of a unit's loads within its chunk, fixed for the
+// whole kernel: the chunk (page, kv head) is a buffer resource in scalar
+// registers and the 16-token group a scalar offset, so a load's only vector
+// operand is this 32-bit offset and no address arithmetic runs per unit.
 struct LaneOffs {
   uint32_t k, v, ks, vs;
 };
