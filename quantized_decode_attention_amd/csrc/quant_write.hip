@@ -53,6 +53,16 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+__device__ __forceinline__ void halves8_to_f32(uint4 raw, float* x) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    half2_t h = as_h2(w[i]);
+    x[2 * i] = (float)h[0];
+    x[2 * i + 1] = (float)h[1];
+  }
+}
+
 __device__ __forceinline__ void load_halves8(const uint16_t* p, float* x) {
   const uint4 raw = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -178,6 +188,20 @@ __global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
   const int64_t g = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
+  constexpr int QPR = D / 16;               // lanes per token row
+  constexpr int LPS = 16 * QPR;             // lanes per side
+  const int side = tid / LPS;               // D = 128: 128 lanes per side
+  const bool active = tid < 2 * LPS;
+  const int lt = tid % LPS, sidx = lt / QPR, q = lt % QPR;
+  // The group's inputs are requested before its slots are checked (they do
+  // not depend on them), so the two round trips overlap.  A partial last
+  // group never takes the contiguous path and loads nothing here.
+  uint4 raw[2] = {};
+  if (active && 16 * g + 16 <= a.n_tok) {
+    const uint16_t* src = (side ? a.v : a.k) + ((16 * g + sidx) * a.H + h) * (int64_t)D + 16 * q;
+    raw[0] = *reinterpret_cast<const uint4*>(src);
+    raw[1] = *reinterpret_cast<const uint4*>(src + 8);
+  }
   const int64_t slot0 = group_slot(a, g, &s_ok, &s_slot0);
 
   if (slot0 < 0) {
@@ -192,16 +216,10 @@ __global__ __launch_bounds__(kBlock) void quant_write_8bit(WriteArgs a) {
     return;
   }
 
-  constexpr int QPR = D / 16;               // lanes per token row
-  constexpr int LPS = 16 * QPR;             // lanes per side
-  const int side = tid / LPS;               // D = 128: 128 lanes per side
-  const bool active = tid < 2 * LPS;
-  const int lt = tid % LPS, sidx = lt / QPR, q = lt % QPR;
   if (active) {
-    const uint16_t* src = (side ? a.v : a.k) + ((16 * g + sidx) * a.H + h) * (int64_t)D + 16 * q;
     float x[16];
-    load_halves8(src, x);
-    load_halves8(src + 8, x + 8);
+    halves8_to_f32(raw[0], x);
+    halves8_to_f32(raw[1], x + 8);
     float s;
     if constexpr (FMT == 1) {
       s = side ? a.v_scale : a.k_scale;
@@ -450,6 +468,16 @@ __global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
   const int64_t g = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
+  // lane (side, token s, block q); 2 * 16 * NB <= 256 lanes.  Inputs are
+  // requested before the slot check, as for the 8-bit formats.
+  const bool active = tid < 32 * NB;
+  const int side = tid / (16 * NB), lt = tid % (16 * NB), sidx = lt / NB, q = lt % NB;
+  uint4 raw[2] = {};
+  if (active && 16 * g + 16 <= a.n_tok) {
+    const uint16_t* src = (side ? a.v : a.k) + ((16 * g + sidx) * a.H + h) * (int64_t)D + 16 * q;
+    raw[0] = *reinterpret_cast<const uint4*>(src);
+    raw[1] = *reinterpret_cast<const uint4*>(src + 8);
+  }
   const int64_t slot0 = group_slot(a, g, &s_ok, &s_slot0);
 
   if (slot0 < 0) {
@@ -462,13 +490,10 @@ __global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
     return;
   }
 
-  // lane (side, token s, block q); 2 * 16 * NB <= 256 lanes
-  if (tid < 32 * NB) {
-    const int side = tid / (16 * NB), lt = tid % (16 * NB), sidx = lt / NB, q = lt % NB;
-    const uint16_t* src = (side ? a.v : a.k) + ((16 * g + sidx) * a.H + h) * (int64_t)D + 16 * q;
+  if (active) {
     float x[16];
-    load_halves8(src, x);
-    load_halves8(src + 8, x + 8);
+    halves8_to_f32(raw[0], x);
+    halves8_to_f32(raw[1], x + 8);
     uint32_t byte[8];
     uint32_t sb = 0;
     if constexpr (FMT == 4) {
