@@ -142,11 +142,13 @@ __device__ __forceinline__ float quantise_group(const float (&y)[H], uint8_t* co
   mx = fmaxf(b.left, b.right);
   const float s = (mx - mn) / (float)LEVELS;
   const Recip rc = make_recip(s);
+  // clip(rne(.), 0, LEVELS): the clamp first (integer bounds, so it commutes
+  // with the rounding), then adding 1.5 * 2^23 rounds to an integer with ties
+  // to even and leaves it in the sum's low mantissa bits
 #pragma unroll
   for (int k = 0; k < H; ++k) {
-    float q = __builtin_rintf(div_rn(y[k] - mn, s, rc));
-    q = fminf(fmaxf(q, 0.0f), (float)LEVELS);
-    codes[stride * k] = s != 0.0f ? (uint8_t)q : (uint8_t)0;
+    const float yc = __builtin_amdgcn_fmed3f(div_rn(y[k] - mn, s, rc), 0.0f, (float)LEVELS);
+    codes[stride * k] = s != 0.0f ? (uint8_t)__float_as_uint(yc + 12582912.0f) : (uint8_t)0;
   }
   *mn_out = mn;
   return s;
