@@ -19,8 +19,10 @@ from gpu_util import assert_attn_close, dev, log, olayout
 pytestmark = pytest.mark.gpu
 
 CASES = [("int8_32k", 2, 0), ("int8_32k", 6, 0), ("fp8_sink_4k", 1, 0), ("fp8_sink_4k", 3, 0),
-         ("nvfp4_16k", 4, 0), ("nvfp4_16k", 4, 1), ("nvfp4_16k", 7, 0), ("kvarn_16k", 5, 0)]
-IDS = ["int8_32k", "int4pth_32k", "fp8pt_4k", "fp8pth_4k", "nvfp4_16k", "nvfp4_4over6_16k", "mxfp4_16k", "kvarn_16k"]
+         ("nvfp4_16k", 4, 0), ("nvfp4_16k", 4, 1), ("nvfp4_16k", 7, 0), ("kvarn_16k", 5, 0),
+         ("nvfp4_16k_tp2", 4, 0), ("kvarn_16k_tp2", 5, 0)]
+IDS = ["int8_32k", "int4pth_32k", "fp8pt_4k", "fp8pth_4k", "nvfp4_16k", "nvfp4_4over6_16k", "mxfp4_16k", "kvarn_16k",
+       "nvfp4_16k_tp2", "kvarn_16k_tp2"]
 
 _cache = {}
 
