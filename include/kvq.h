@@ -12,7 +12,9 @@
  * Conventions for every entry point:
  *   - All pointers except `layout` are device pointers (HIP global memory) on the
  *     current HIP device, unless stated.  The caller owns every buffer; the
- *     library allocates no device memory and keeps no state between calls.
+ *     library allocates no device memory and keeps no device state between
+ *     calls (it only memoises, per device, the host-side answers of the HIP
+ *     compute-unit and occupancy queries behind the split plan).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; the returned status covers argument validation and
  *     kernel-launch errors only.
@@ -251,10 +253,12 @@ int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t n
  *                  preparation.  Two calls that overlap in time must not share
  *                  a workspace.
  *   num_splits     as for kvq_decode_workspace_bytes.
- * Launches one kernel, plus a small merge kernel when the context is split.
+ * Launches one kernel, plus a small merge kernel when the context is split
+ * (KVarN: always; its merge also attends the tail and rotates back).
  * Accumulation is binary32 (scores and softmax) on MFMA with binary16
- * operands split into high and low halves, so results track a binary64
- * reference to about 1e-5 relative. */
+ * operands split into high and low halves, so before the final binary16
+ * rounding results track a binary64 reference to about 1e-5 relative (the
+ * tests hold them to 1e-4). */
 kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, const void* q,
                                 int32_t num_q_heads, const int32_t* block_tables,
                                 int32_t max_pages_per_seq, const int32_t* context_lens,
@@ -265,9 +269,9 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
 /* Expand cached tokens back to binary32 [n_tok][H][D] for inspection and tests
  * (x_hat = s q, [P3] §它改变缓存表示).  8-bit formats: code value times scale,
  * one rounding.  NVFP4: E2M1 value times the E4M3 block scale (exact), times
- * s_t (one rounding).  MXFP4: E2M1 value times 2^(e-127) (exact).  KVarN: rebuilt in the rotated basis, then rotated back
- * (binary32, a few ulps).  Skipped slots (as in kvq_quantize_write) leave their
- * rows untouched. */
+ * s_t (one rounding).  MXFP4: E2M1 value times 2^(e-127) (exact).  KVarN:
+ * rebuilt in the rotated basis, then rotated back (binary32, a few ulps).
+ * Skipped slots (as in kvq_quantize_write) leave their rows untouched. */
 kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int64_t* slot_mapping,
                           int64_t n_tok, float* k_out, float* v_out, void* stream);
 
