@@ -46,6 +46,17 @@ __device__ __forceinline__ bool row_ctx(const WriteArgs& a, int64_t row, RowCtx&
   return true;
 }
 
+// Eight binary16 input values of row `row` (both sides stacked, as for
+// row_ctx) starting at channel d0, requested without waiting for the row's
+// slot (the address does not depend on it); zero past the last row.
+__device__ __forceinline__ uint4 load_row_piece(const WriteArgs& a, int64_t row, int D, int d0) {
+  const int64_t per_side = a.n_tok * a.H;
+  if (row >= 2 * per_side) return uint4{0u, 0u, 0u, 0u};
+  const bool side = row >= per_side;
+  const int64_t r = side ? row - per_side : row;
+  return *reinterpret_cast<const uint4*>((side ? a.v : a.k) + r * D + d0);
+}
+
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll
@@ -54,17 +65,6 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 __device__ __forceinline__ void halves8_to_f32(uint4 raw, float* x) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    half2_t h = as_h2(w[i]);
-    x[2 * i] = (float)h[0];
-    x[2 * i + 1] = (float)h[1];
-  }
-}
-
-__device__ __forceinline__ void load_halves8(const uint16_t* p, float* x) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -117,11 +117,12 @@ __device__ __forceinline__ uint32_t encode8x4(const float* x, float s, Recip rc)
 template <int FMT, int D>
 __device__ __forceinline__ void write_row_8bit(const WriteArgs& a, int64_t row, int j) {
   constexpr int LPR = D / 8;
+  const uint4 raw = load_row_piece(a, row, D, 8 * j);  // requested before the slot is read
   RowCtx c;
   if (!row_ctx(a, row, c)) return;
 
   float x[8];
-  load_halves8((c.side ? a.v : a.k) + c.r * D + 8 * j, x);
+  halves8_to_f32(raw, x);
 
   float s;
   if constexpr (FMT == 1) {
@@ -416,12 +417,12 @@ __device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, 
   constexpr int NB = D / 16;
   constexpr int NS = FMT == 7 ? D / 32 : D / 16;  // block-scale bytes per row
   constexpr int SL = FMT == 7 ? 2 : 1;            // lanes per block scale
+  const uint4 raw0 = load_row_piece(a, row, D, 16 * j), raw1 = load_row_piece(a, row, D, 16 * j + 8);
   RowCtx c;
   if (!row_ctx(a, row, c)) return;
   float x[16];
-  const uint16_t* src = (c.side ? a.v : a.k) + c.r * D + 16 * j;
-  load_halves8(src, x);
-  load_halves8(src + 8, x + 8);
+  halves8_to_f32(raw0, x);
+  halves8_to_f32(raw1, x + 8);
   uint32_t byte[8];
   uint32_t sb = 0;
   float s = 0.0f;
