@@ -279,3 +279,28 @@ def test_kvarn_incremental_append_matches_oracle(K, O):
     K.kvq_decode_attention(lay, cache, dev(q16), btd, dev(ctx), 0.088, out, ws.buffer, tail)
     torch.cuda.synchronize()
     assert_attn_close(out.cpu().numpy().astype(np.float64), ref)
+
+
+def test_kvarn_decode_edge_contexts_and_repeated_tiles(K, O):
+    """Contexts around the tile boundary (127, 128, 129, 255, 256, 257, 8191)
+    and block tables that list a tile's page twice or share pages between
+    sequences: the tail is per sequence, the tiles are read as listed."""
+    rng = np.random.default_rng(733)
+    B, H, G = 7, 2, 8
+    ctx = np.array([127, 128, 129, 255, 256, 257, 8191], np.int32)
+    bt, num_pages, slots, kq, vq, tail = kvarn_problem(rng, B, H, ctx)
+    lay = K.layout(5, H, D, P, num_pages)
+    cache = O.quantize_write(olayout(lay), kq, vq, slots)
+    bt = bt.copy()
+    bt[4, 1] = bt[4, 0]      # ctx 256: its first tile read twice
+    bt[5, :2] = bt[6, :2]    # ctx 257: the first two tiles of the 8191-token sequence
+    q16 = workloads.random_halves(rng, (B, H * G, D))
+    sm = 1.0 / math.sqrt(D)
+    ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, sm, tail16=tail)
+    cache_dev = dev(cache)
+    for splits in (0, 1, 9):
+        log(f"kvarn edge contexts splits={splits}")
+        got, _ = gpu_decode(K, lay, cache_dev, q16, bt, ctx, sm, tail16=tail, num_splits=splits)
+        assert_attn_close(got, ref, f"splits={splits}")
+        ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-4 + 1e-4 * np.abs(ref))

@@ -338,3 +338,35 @@ def test_decode_single_split_eight_waves(K, O, fmt):
     assert ws.num_splits == 1 and ws.buffer.numel() == 0
     assert_attn_close(got, ref)
     assert not np.any(got[0])
+
+
+@pytest.mark.parametrize("fmt,flags", FORMATS, ids=FMT_IDS)
+def test_decode_edge_context_lengths(K, O, fmt, flags):
+    """Context lengths around the 16-token sub-page and page boundaries, a
+    long one, and block tables that repeat pages: a page listed twice in one
+    sequence and a sequence that shares another's pages (the reads see the
+    same bytes twice; nothing in the decode assumes distinct pages)."""
+    rng = np.random.default_rng(700 + fmt * 3 + flags)
+    H, G, D, P = 2, 4, 128, 16
+    ctx = np.array([1, 15, 16, 17, 127, 128, 129, 4095], np.int32)
+    B = ctx.size
+    bt, num_pages, slots = paged_problem(rng, B, H, G, D, P, ctx)
+    n = slots.shape[0]
+    k16 = workloads.random_halves(rng, (n, H, D))
+    v16 = workloads.random_halves(rng, (n, H, D))
+    lay = layout_for(K, fmt, flags, H, D, P, num_pages, k16, v16)
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    # repeated pages (after the write: the cache holds each page once)
+    bt = bt.copy()
+    bt[5, 4:8] = bt[5, 0]        # ctx 128 = pages 0..7: page 0 read five times
+    bt[6, :9] = bt[7, :9]        # ctx 129: the first 9 pages of the 4095-token sequence
+    q16 = workloads.random_halves(rng, (B, H * G, D))
+    sm = 1.0 / math.sqrt(D)
+    ref = O.decode_attention(olayout(lay), cache, q16, bt, ctx, sm)
+    cache_dev = dev(cache)
+    for splits in (0, 1, 5):
+        log(f"edge contexts fmt={fmt} flags={flags} splits={splits}")
+        got, _ = gpu_decode(K, lay, cache_dev, q16, bt, ctx, sm, num_splits=splits)
+        assert_attn_close(got, ref, f"splits={splits}")
+        ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-4 + 1e-4 * np.abs(ref))
