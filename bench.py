@@ -2,8 +2,11 @@
 """Benchmark of the KV-cache quantisation hot path on one MI355X.
 
 A step is one decode step of the workload: quantise-write the new token of
-every sequence (kvq_quantize_write, B tokens) and run dequant-fused paged
-decode attention over the whole context (kvq_decode_attention).  The headline
+every sequence and run dequant-fused paged decode attention over the whole
+context, new token included, in one call (kvq_decode_attention_append: the
+split kernel, then a merge kernel that also quantises, stores and attends the
+new tokens; KVarN steps append through kvq_kvarn_append and then call
+kvq_decode_attention).  The headline
 workload is INT8 per-token-head at 32K context (B=8, 64 q / 8 kv heads,
 D=128, page 16): `value` is quantised-KV bytes read per second over the timed
 steps.  Inputs are resident in HBM before timing starts; the cache is rotated
@@ -12,9 +15,9 @@ pages.
 
 Also reported on the same line:
   write_mtok_s   whole-context quantise-on-write throughput (tokens/s / 1e6)
-  roofline       decode (split kernel, plus the merge kernel when the context
-                 is split): algorithmic KV bytes per launch / mean launch
-                 duration (HIP events around each decode call, on the launch
+  roofline       the step's decode call (split kernel, plus the merge kernel
+                 that writes and attends the new tokens): algorithmic KV bytes
+                 per call / mean call duration (HIP events around each call, on the launch
                  stream, over an instrumented pass of as many steps right
                  after the timed ones: an event recorded between two launches
                  holds the next one back by a few microseconds, so the timed
@@ -131,6 +134,18 @@ class Problem:
             return
         self.K.kvq_quantize_write(self.lay, self.k_new, self.v_new, self.slots_new, c)
 
+    def step(self, i):
+        """One decode step: KVarN appends through its binary16 tail and then
+        decodes (two calls); the other formats quantise-write the new tokens
+        and decode in one call (kvq_decode_attention_append)."""
+        if self.kvarn:
+            self.append(i)
+            self.decode(i)
+            return
+        self.K.kvq_decode_attention_append(self.lay, self.caches[i % len(self.caches)], self.k_new, self.v_new,
+                                           self.slots_new, self.q, self.bt, self.ctx, self.sm, self.out,
+                                           self.ws.buffer)
+
     def decode(self, i):
         c = self.caches[i % len(self.caches)]
         if self.kvarn:
@@ -169,22 +184,25 @@ class Problem:
             self.prepare_incremental(warmup + 2 * steps)
             torch.cuda.synchronize()
         for i in range(warmup):
-            self.append(i)
-            self.decode(i)
+            self.step(i)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
         for i in range(steps):
-            self.append(warmup + i)
-            self.decode(warmup + i)
+            self.step(warmup + i)
         end.record()
         torch.cuda.synchronize()
         total = start.elapsed_time(end)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for i in range(steps):
-            self.append(warmup + steps + i)
-            ev[i][0].record()
-            self.decode(warmup + steps + i)
+            j = warmup + steps + i
+            if self.kvarn:
+                self.append(j)
+                ev[i][0].record()
+                self.decode(j)
+            else:
+                ev[i][0].record()
+                self.step(j)
             ev[i][1].record()
         torch.cuda.synchronize()
         if self.kvarn:  # mean KV bytes (tiles + binary16 tail) of the timed and of the instrumented steps
@@ -228,7 +246,9 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
 # figure is reported only while those sources are unchanged (comments and
 # blank lines aside).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int8_32k_traffic.md")
-DECODE_SOURCES = ("decode_attn.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
+# the decode call: split kernel (decode_attn.hip) and the merge that writes and attends the new tokens
+# (quant_write.hip)
+DECODE_SOURCES = ("decode_attn.hip", "quant_write.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
 
 
 def _code_only(text):
@@ -248,7 +268,7 @@ def decode_sources_digest():
     for name in DECODE_SOURCES:
         with open(os.path.join(_build.CSRC, name), encoding="utf-8") as f:
             h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
-    h.update(" ".join(_build.SOURCES["decode_attn.hip"] + _build.COMMON[:4]).encode())
+    h.update(" ".join(_build.SOURCES["decode_attn.hip"] + _build.SOURCES["quant_write.hip"] + _build.COMMON[:4]).encode())
     return h.hexdigest()
 
 
@@ -384,7 +404,8 @@ def main():
             "workload": args.workload, "format": K.FORMAT_NAMES[pb.fmt], "batch": w.B, "context": w.T,
             "q_heads": sp.Hq, "kv_heads": sp.Hkv, "head_dim": sp.D, "page_size": sp.P,
             "splits": pb.ws.num_splits, "cache_copies": len(pb.caches),
-            "step": "quantize-write 1 new token per sequence + paged decode attention over the context",
+            "step": "quantize-write 1 new token per sequence + paged decode attention over the context "
+                    "(one kvq_decode_attention_append call)",
         },
         "kv_bytes_per_step": pb.kv_bytes,
         "write_mtok_s": round(write_mtok, 2),
@@ -396,7 +417,7 @@ def main():
             # at least one (sequence, kv head) per compute unit (kvq.h)
             "kernel": f"decode_kernel<{pb.fmt}, {sp.D}, {sp.Hq // sp.Hkv}, "
                       f"{8 if pb.ws.num_splits == 1 and pb.fmt in (1, 2, 3) and w.B * sp.Hkv >= 256 else 4}>"
-                      + (" + decode_merge_kernel" if pb.ws.num_splits > 1 else ""),
+                      + (" + append_merge_kernel" if pb.ws.num_splits > 1 else " after quant_write"),
             "algorithmic_bytes": pb.call_kv_bytes, "traffic_unit": "HBM bytes per decode call (rocprofv3 "
             "FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB copy)",
             "mean_launch_us": round(ms_dec * 1e3, 2),
@@ -427,7 +448,8 @@ def main():
                          "decode_us": round(ms_d * 1e3, 2), **p.dec_percentiles_us(), "step_us": round(ms_s * 1e3, 2),
                          "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits,
                          "step": ("append to the binary16 tail (tile quantised when complete) + decode over "
-                                  "tiles and tail" if fmt == K.KVQ_KVARN_K4V2_G128 else "append + decode")}
+                                  "tiles and tail" if fmt == K.KVQ_KVARN_K4V2_G128
+                                  else "write + decode in one kvq_decode_attention_append call")}
             log(f"[bench] {key}: {fmts[key]}")
             del p
             torch.cuda.empty_cache()

@@ -266,6 +266,39 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
                                 void* workspace, int64_t workspace_bytes, int32_t num_splits,
                                 void* stream);
 
+/* One decode step in one call: quantise-write each sequence's new token and
+ * run decode attention over its context, the new token included ([P5]
+ * §KV 的写入与读取路径: the step writes the new K/V into the page, then decode
+ * reads the whole history).  Formats 1-4, 6 and 7 (not KVarN, whose steps go
+ * through kvq_kvarn_append).
+ *   cache          the paged cache (written).
+ *   k_new, v_new   binary16 [batch][H][D]: the new token of each sequence.
+ *   slot_mapping   int64 [batch]: its slot (page * P + offset), normally the
+ *                  slot of position context_lens[b] - 1 in the block table.
+ *   other arguments as for kvq_decode_attention (kvarn_tail excluded); the
+ *   workspace is sized by kvq_decode_workspace_bytes with the same arguments.
+ * The cache bytes written are exactly those of kvq_quantize_write(k_new,
+ * v_new, slot_mapping, n_tok = batch).  Attention covers positions
+ * 0 .. ctx-2 read from the cache plus the new token as position ctx-1, so
+ * the output equals kvq_quantize_write followed by kvq_decode_attention
+ * whenever each slot is that of position ctx-1 (other slots give the same
+ * cache bytes but attend the new token at position ctx-1 all the same).  A
+ * sequence whose slot is negative or outside the pool stores nothing and
+ * attends its ctx cached tokens; ctx = 0 stores the token and gives a zero
+ * row.  Two sequences must not share a slot.
+ * With a split context this is two launches, the split kernel (reading one
+ * token less) and a merge kernel that also quantises, stores and attends the
+ * new tokens, so no write launch precedes the split kernel.  With a single
+ * split it is the write launch followed by the decode.
+ * Errors: as kvq_decode_attention; KVQ_ERR_INVALID_ARG for a KVarN layout or
+ * NULL k_new, v_new or slot_mapping with batch > 0. */
+kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, const void* k_new,
+                                       const void* v_new, const int64_t* slot_mapping, const void* q,
+                                       int32_t num_q_heads, const int32_t* block_tables,
+                                       int32_t max_pages_per_seq, const int32_t* context_lens,
+                                       int32_t batch, float sm_scale, void* out, void* workspace,
+                                       int64_t workspace_bytes, int32_t num_splits, void* stream);
+
 /* Expand cached tokens back to binary32 [n_tok][H][D] for inspection and tests
  * (x_hat = s q, [P3] §它改变缓存表示).  8-bit formats: code value times scale,
  * one rounding.  NVFP4: E2M1 value times the E4M3 block scale (exact), times

@@ -68,6 +68,8 @@ def _load():
         "kvq_decode_workspace_bytes": (I64, [LP, I32, I32, I32, I32]),
         "kvq_decode_num_splits": (I32, [LP, I32, I32, I32, I32]),
         "kvq_decode_attention": (ctypes.c_int, [LP, P, P, I32, P, I32, P, I32, F32, P, P, P, I64, I32, P]),
+        "kvq_decode_attention_append": (ctypes.c_int, [LP, P, P, P, P, P, I32, P, I32, P, I32, F32, P, P, I64, I32,
+                                                        P]),
         "kvq_dequantize": (ctypes.c_int, [LP, P, P, I64, P, P, P]),
         "kvq_kvarn_append": (ctypes.c_int, [LP, P, P, P, P, I64, P, I32, P, I32, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -161,6 +163,23 @@ def kvq_decode_attention(lay: KvqLayout, cache, q, block_tables, context_lens, s
         _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
         0 if workspace is None else workspace.numel(), num_splits, _stream(stream)),
         "kvq_decode_attention")
+
+
+def kvq_decode_attention_append(lay: KvqLayout, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens,
+                                sm_scale, out, workspace, num_splits: int = 0, stream=None):
+    """One decode step: k_new, v_new: float16 [B, H, D] (one new token per sequence); slot_mapping: int64 [B];
+    q, out: float16 [B, Hq, D]; block_tables: int32 [B, max_pages]; context_lens: int32 [B] (new token
+    included); workspace as for kvq_decode_attention."""
+    import torch
+    B, Hq, _ = q.shape
+    _check(_lib.kvq_decode_attention_append(
+        ctypes.byref(lay), _ptr(cache, torch.uint8, "cache"), _ptr(k_new, torch.float16, "k_new"),
+        _ptr(v_new, torch.float16, "v_new"), _ptr(slot_mapping, torch.int64, "slot_mapping"),
+        _ptr(q, torch.float16, "q"), Hq, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _ptr(context_lens, torch.int32, "context_lens"), B, float(sm_scale), _ptr(out, torch.float16, "out"),
+        _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
+        0 if workspace is None else workspace.numel(), num_splits, _stream(stream)),
+        "kvq_decode_attention_append")
 
 
 def kvq_kvarn_append(lay: KvqLayout, k, v, seq, pos, tail, block_tables, cache, stream=None):

@@ -202,13 +202,16 @@ __device__ __forceinline__ half4_t v_operand(const Raw<FMT, D>& r, int nn, half2
                                              const uint32_t (&pairs)[4]) {
   if constexpr (FMT == 6) {
     // the channel's nibble of each of the 4 token bytes as code + 8, the
-    // same way as the keys; 8 times the sum of the weights is removed from
-    // each head's output once, after the last token
+    // same way as the keys, then the exact binary16 subtraction of 8: the
+    // values enter the product signed (an offset removed after the sum would
+    // cancel against it, which loses the small outputs of rows whose scale
+    // is large)
     const uint32_t w = r.v[nn / 2] ^ 0x88888888u;
     const uint32_t x = (nn & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
     uint32_t lo, hi;
     e4m3x4_to_h_scaled(x, 512.0f, lo, hi);
-    return cat4(as_h2(lo), as_h2(hi));
+    const half2_t eight = {(half_t)8.0f, (half_t)8.0f};
+    return cat4(as_h2(lo) - eight, as_h2(hi) - eight);
   } else if constexpr (FMT == 7) {
     // `pairs` already carry each token's block scale
     const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
@@ -234,7 +237,6 @@ template <int D>
 struct WaveState {
   float4_t acc[D / 16];
   float m_run, l_run;
-  float vb;  // INT4: sum of the weights P * v_scale (the value codes enter as code + 8)
 };
 
 template <int FMT, int D, int G>
@@ -302,9 +304,6 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
   auto accumulate = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.l_run += p[i];
-    if constexpr (FMT == 6)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.vb += p[i] * vsc[i];
     const half4_t pA = cat4(as_h2(hi_lo_rows<G>(h01, lo01)), as_h2(hi_lo_rows<G>(h23, lo23)));
     half2_t vs01 = {0, 0}, vs23 = {0, 0};
     if constexpr (FMT == 4) {
@@ -340,7 +339,6 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = (m_new > st.m_run) ? exp2f(st.m_run - m_new) : 1.0f;
     st.l_run *= alpha;
-    st.vb *= alpha;
     float ar[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -369,7 +367,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   __shared__ float lds_o[W][2 * G][D];
   __shared__ float lds_m[W][16];
   __shared__ float lds_l[W][16];
-  __shared__ float lds_vb[W][16];
   __shared__ int s_pages[kPageChunk];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -384,6 +381,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   // wave-uniform bounds (kept in scalar registers)
   int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
+  if (a.new_slots != nullptr) {
+    // append-and-decode: the last position is the new token, attended by the
+    // merge kernel when its slot is in the pool
+    const int64_t ns = a.new_slots[b];
+    if (ctx >= 1 && ns >= 0 && ns < (int64_t)a.num_pages * P) ctx -= 1;
+  }
   const int n_pages = (ctx + P - 1) / P;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(p_begin + a.pages_per_split, n_pages);
@@ -426,7 +429,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   for (int nn = 0; nn < NV; ++nn) st.acc[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
   st.m_run = kRefStart;
   st.l_run = 0.0f;
-  st.vb = 0.0f;
 
   // This wave's pages: p_begin + w + 4*j, j < n_it.  Their block-table
   // entries are fetched 64 at a time into one VGPR (lane j holds entry j) and
@@ -493,15 +495,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   // ---- combine the W waves (and the hi/lo rows) in LDS
   float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  float vb_tot = 0.0f;
-  if constexpr (FMT == 6) {
-    vb_tot = st.vb + __shfl_xor(st.vb, 16);
-    vb_tot += __shfl_xor(vb_tot, 32);
-  }
   if (gq == 0) {
     lds_m[w][n] = st.m_run;
     lds_l[w][n] = l_tot;
-    if constexpr (FMT == 6) lds_vb[w][n] = 8.0f * vb_tot;
   }
 #pragma unroll
   for (int nn = 0; nn < NV; ++nn)
@@ -525,8 +521,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
       for (int ww = 0; ww < W; ++ww) {
         const float f = exp2f(lds_m[ww][g] - M);
         L += f * lds_l[ww][g];
-        float o = lds_o[ww][g][d] + lds_o[ww][g + G][d];
-        if constexpr (FMT == 6) o -= lds_vb[ww][g];
+        const float o = lds_o[ww][g][d] + lds_o[ww][g + G][d];
         O += f * o;
       }
     }
@@ -654,7 +649,7 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s) {
     case 6: e = launch_fmt<6>(a, s); break;
     case 7: e = launch_fmt<7>(a, s); break;
   }
-  if (e != hipSuccess || a.num_splits == 1) return e;
+  if (e != hipSuccess || a.num_splits == 1 || a.new_slots != nullptr) return e;
   const float post = (fmt == 1 || fmt == 4) ? a.v_scale : 1.0f;
   const int64_t outs = (int64_t)a.B * a.Hq * a.D;
   decode_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, s>>>(a, a.D, post);

@@ -212,6 +212,75 @@ int64_t workspace_bytes_for(const kvq_layout* L, int batch, int splits) {
   return (int64_t)batch * L->num_kv_heads * splits * ws_record_floats(L->head_dim) * 4;
 }
 
+WriteArgs write_args(const kvq_layout* L, const void* k, const void* v, const int64_t* slots, int64_t n_tok,
+                     void* cache) {
+  WriteArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.slots = slots;
+  a.n_tok = n_tok;
+  a.cache = static_cast<uint8_t*>(cache);
+  a.geom = geometry(L);
+  a.H = L->num_kv_heads;
+  a.D = L->head_dim;
+  a.P = L->page_size;
+  a.num_pages = L->num_pages;
+  a.k_scale = L->k_scale;
+  a.v_scale = L->v_scale;
+  a.flags = L->flags;
+  return a;
+}
+
+// Argument checks shared by the decode entry points; on success the plan.
+kvq_status check_decode(const kvq_layout* L, const void* cache, const void* q, int32_t num_q_heads,
+                        const int32_t* block_tables, int32_t max_pages_per_seq, const int32_t* context_lens,
+                        int32_t batch, float sm_scale, void* out, void* workspace, int64_t workspace_bytes,
+                        int32_t num_splits, int* splits, int* pps, int* waves) {
+  kvq_status st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  const int H = L->num_kv_heads;
+  if (batch < 0 || num_q_heads < 1 || max_pages_per_seq < 1 || num_splits < 0 || !isfinite(sm_scale))
+    return KVQ_ERR_INVALID_ARG;
+  if (num_q_heads % H != 0) return KVQ_ERR_INVALID_ARG;
+  const int G = num_q_heads / H;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
+  if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
+  plan(L, batch, G, max_pages_per_seq, num_splits, splits, pps, waves);
+  const int64_t need = workspace_bytes_for(L, batch, *splits);
+  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;
+  return current_device_ok();
+}
+
+DecodeArgs decode_args(const kvq_layout* L, const void* cache, const void* q, int32_t num_q_heads,
+                       const int32_t* block_tables, int32_t max_pages_per_seq, const int32_t* context_lens,
+                       int32_t batch, float sm_scale, void* out, void* workspace, int splits, int pps, int waves) {
+  DecodeArgs a{};
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.geom = geometry(L);
+  a.H = L->num_kv_heads;
+  a.D = L->head_dim;
+  a.P = L->page_size;
+  a.num_pages = L->num_pages;
+  a.q = static_cast<const uint16_t*>(q);
+  a.Hq = num_q_heads;
+  a.G = num_q_heads / a.H;
+  a.block_tables = block_tables;
+  a.max_pages = max_pages_per_seq;
+  a.ctx_lens = context_lens;
+  a.B = batch;
+  a.qk_scale = sm_scale * 1.4426950408889634f;
+  a.k_scale = L->k_scale;
+  a.v_scale = L->v_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.workspace = static_cast<uint8_t*>(workspace);
+  a.num_splits = splits;
+  a.pages_per_split = pps;
+  a.waves = waves;
+  a.sp_shift = __builtin_ctz(L->page_size / 16);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,20 +301,7 @@ kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const voi
   if (n_tok > 0 && (!k || !v || !slot_mapping || !cache)) return KVQ_ERR_INVALID_ARG;
   if ((st = current_device_ok()) != KVQ_OK) return st;
   if (n_tok == 0) return KVQ_OK;
-  WriteArgs a{};
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.slots = slot_mapping;
-  a.n_tok = n_tok;
-  a.cache = static_cast<uint8_t*>(cache);
-  a.geom = geometry(layout);
-  a.H = layout->num_kv_heads;
-  a.D = layout->head_dim;
-  a.P = layout->page_size;
-  a.num_pages = layout->num_pages;
-  a.k_scale = layout->k_scale;
-  a.v_scale = layout->v_scale;
-  a.flags = layout->flags;
+  const WriteArgs a = write_args(layout, k, v, slot_mapping, n_tok, cache);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (layout->format == KVQ_KVARN_K4V2_G128) return from_hip(launch_kvarn_write(a, s));
   return from_hip(launch_quant_write(layout->format, a, s));
@@ -304,50 +360,47 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
                                 const int32_t* context_lens, int32_t batch, float sm_scale,
                                 const void* kvarn_tail, void* out, void* workspace, int64_t workspace_bytes,
                                 int32_t num_splits, void* stream) {
-  kvq_status st = check_layout(layout);
-  if (st != KVQ_OK) return st;
-  const int H = layout->num_kv_heads;
-  if (batch < 0 || num_q_heads < 1 || max_pages_per_seq < 1 || num_splits < 0 || !isfinite(sm_scale))
-    return KVQ_ERR_INVALID_ARG;
-  if (num_q_heads % H != 0) return KVQ_ERR_INVALID_ARG;
-  const int G = num_q_heads / H;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
-  if (kvarn_tail && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
-  if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
+  if (kvarn_tail && layout && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
   int splits, pps, waves;
-  plan(layout, batch, G, max_pages_per_seq, num_splits, &splits, &pps, &waves);
-  const int64_t need = workspace_bytes_for(layout, batch, splits);
-  if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;
-  if ((st = current_device_ok()) != KVQ_OK) return st;
-  if (batch == 0) return KVQ_OK;
-  DecodeArgs a{};
-  a.cache = static_cast<const uint8_t*>(cache);
-  a.geom = geometry(layout);
-  a.H = H;
-  a.D = layout->head_dim;
-  a.P = layout->page_size;
-  a.num_pages = layout->num_pages;
-  a.q = static_cast<const uint16_t*>(q);
-  a.Hq = num_q_heads;
-  a.G = G;
-  a.block_tables = block_tables;
-  a.max_pages = max_pages_per_seq;
-  a.ctx_lens = context_lens;
-  a.B = batch;
-  a.qk_scale = sm_scale * 1.4426950408889634f;
-  a.k_scale = layout->k_scale;
-  a.v_scale = layout->v_scale;
+  const kvq_status st = check_decode(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens,
+                                     batch, sm_scale, out, workspace, workspace_bytes, num_splits, &splits, &pps,
+                                     &waves);
+  if (st != KVQ_OK || batch == 0) return st;
+  DecodeArgs a = decode_args(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens, batch,
+                             sm_scale, out, workspace, splits, pps, waves);
   a.tail = static_cast<const uint16_t*>(kvarn_tail);
-  a.out = static_cast<uint16_t*>(out);
-  a.workspace = static_cast<uint8_t*>(workspace);
-  a.num_splits = splits;
-  a.pages_per_split = pps;
-  a.waves = waves;
-  a.sp_shift = __builtin_ctz(layout->page_size / 16);
   if (layout->format == KVQ_KVARN_K4V2_G128)
     return from_hip(launch_kvarn_decode(a, static_cast<hipStream_t>(stream)));
   return from_hip(launch_decode(layout->format, a, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, const void* k_new,
+                                       const void* v_new, const int64_t* slot_mapping, const void* q,
+                                       int32_t num_q_heads, const int32_t* block_tables,
+                                       int32_t max_pages_per_seq, const int32_t* context_lens, int32_t batch,
+                                       float sm_scale, void* out, void* workspace, int64_t workspace_bytes,
+                                       int32_t num_splits, void* stream) {
+  if (layout && layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
+  if (batch > 0 && (!k_new || !v_new || !slot_mapping)) return KVQ_ERR_INVALID_ARG;
+  int splits, pps, waves;
+  const kvq_status st = check_decode(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens,
+                                     batch, sm_scale, out, workspace, workspace_bytes, num_splits, &splits, &pps,
+                                     &waves);
+  if (st != KVQ_OK || batch == 0) return st;
+  const WriteArgs w = write_args(layout, k_new, v_new, slot_mapping, batch, cache);
+  DecodeArgs a = decode_args(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens, batch,
+                             sm_scale, out, workspace, splits, pps, waves);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (splits == 1) {
+    // no merge launch to carry the new tokens: write, then decode
+    hipError_t e = launch_quant_write(layout->format, w, s);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(launch_decode(layout->format, a, s));
+  }
+  a.new_slots = slot_mapping;
+  hipError_t e = launch_decode(layout->format, a, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(launch_append_merge(layout->format, w, a, s));
 }
 
 kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int64_t* slot_mapping,

@@ -45,6 +45,10 @@ struct DecodeArgs {
   int pages_per_split;
   int sp_shift;  // log2(P / 16)
   int waves;     // wavefronts per split workgroup: 4, or 8 for single-split plans
+  // Append-and-decode: slot of each sequence's new token (or null).  The
+  // split kernel then reads positions 0 .. ctx-2 of a sequence whose new
+  // token is attended, and the merge is append_merge_kernel's.
+  const int64_t* new_slots;
 };
 
 // Workspace: one partial record (m[8], l[8], o[8][D]) per (sequence, kv head,
@@ -76,6 +80,7 @@ hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s);
 hipError_t launch_kvarn_append(const KvarnAppendArgs& a, hipStream_t s);
 hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s);
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_append_merge(int fmt, const WriteArgs& w, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s);
 

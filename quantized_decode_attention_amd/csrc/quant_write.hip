@@ -14,8 +14,7 @@
 // split with one lane per 16 values.
 // This file is built with -ffp-contract=off: every binary32 operation below
 // rounds exactly as written.
-#include "kvq_device.h"
-#include "kvq_internal.h"
+#include "decode_common.h"
 
 namespace kvq {
 namespace {
@@ -74,6 +73,17 @@ __device__ __forceinline__ void halves8_to_f32(uint4 raw, float* x) {
   }
 }
 
+// The codes one lane of the per-row path produced, for a caller that also
+// attends the row it wrote: 8-bit formats, the codes of channels 8j .. 8j+7
+// (byte i = channel 8j+i); 4-bit formats, values 16j .. 16j+15 packed two per
+// byte (low nibble first).  s is the row scale (per-token-head formats) or the
+// layout scale (FP8 per-tensor), sb the block-scale byte (NVFP4, MXFP4).
+struct RowCodes {
+  uint32_t w[2];
+  float s;
+  uint32_t sb;
+};
+
 // ---------------------------------------------------------------------------
 // 8-bit formats: FMT 1 = FP8 per-tensor, 2 = INT8 per-token-head,
 // 3 = FP8 per-token-head.
@@ -114,8 +124,11 @@ __device__ __forceinline__ uint32_t encode8x4(const float* x, float s, Recip rc)
 }
 
 // One token-head row by D/8 lanes (lane j: channels 8j .. 8j+7), any slot.
+// With `out`, the lane's codes are also returned; `store` = false quantises
+// without writing the cache.
 template <int FMT, int D>
-__device__ __forceinline__ void write_row_8bit(const WriteArgs& a, int64_t row, int j) {
+__device__ __forceinline__ void write_row_8bit(const WriteArgs& a, int64_t row, int j, bool store = true,
+                                               RowCodes* out = nullptr) {
   constexpr int LPR = D / 8;
   const uint4 raw = load_row_piece(a, row, D, 8 * j);  // requested before the slot is read
   RowCtx c;
@@ -137,6 +150,12 @@ __device__ __forceinline__ void write_row_8bit(const WriteArgs& a, int64_t row, 
   uint2 packed;
   packed.x = encode8x4<FMT>(x, s, rc);
   packed.y = encode8x4<FMT>(x + 4, s, rc);
+  if (out) {
+    out->w[0] = packed.x;
+    out->w[1] = packed.y;
+    out->s = s;
+  }
+  if (!store) return;
 
   // 16-token groups of K and V are laid out in the decode's operand order
   // (see k8_offset / v8_offset)
@@ -413,7 +432,8 @@ __device__ __forceinline__ uint32_t mxfp4_encode_half(const float* x, uint32_t* 
 // values, MXFP4 an E8M0 scale per 32 values (lane pairs), INT4 one fp32 scale
 // per row.
 template <int FMT, int D>
-__device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, int j) {
+__device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, int j, bool store = true,
+                                               RowCodes* out = nullptr) {
   constexpr int NB = D / 16;
   constexpr int NS = FMT == 7 ? D / 32 : D / 16;  // block-scale bytes per row
   constexpr int SL = FMT == 7 ? 2 : 1;            // lanes per block scale
@@ -433,10 +453,17 @@ __device__ __forceinline__ void write_row_4bit(const WriteArgs& a, int64_t row, 
   else
     s = int4_encode_block<NB>(x, byte);
   const bool scale_lane = (FMT == 4 || FMT == 7) && j % SL == 0;
+  uint2 packed;
+  packed.x = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
+  packed.y = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
+  if (out) {
+    out->w[0] = packed.x;
+    out->w[1] = packed.y;
+    out->s = s;
+    out->sb = sb;
+  }
+  if (!store) return;
   if (c.side == 0) {
-    uint2 packed;
-    packed.x = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
-    packed.y = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
     *reinterpret_cast<uint2*>(c.chunk + (int64_t)c.t * (D / 2) + 8 * j) = packed;
     if (scale_lane) c.chunk[a.geom.k_scales + (int64_t)c.t * NS + j / SL] = (uint8_t)sb;
   } else {
@@ -542,6 +569,169 @@ __global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// A decode step's new tokens, quantised and attended in the merge of the
+// context splits (kvq_decode_attention_append).  The split kernel has read
+// positions 0 .. ctx-2 of each sequence from the cache.  This kernel
+// quantises the new token of every (sequence, kv head) with the per-row write
+// path above, stores it into its slot, and adds it to each head's merge as
+// one more partial: m = its score, l = 1, o = its dequantised value row.  The
+// step then has no separate write launch ahead of the split kernel.
+// ---------------------------------------------------------------------------
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = W / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, W);
+  return v;
+}
+
+// The lane's code values with the block scales applied (exact in binary32)
+// and the row scale not: INT8 and INT4 integers, E4M3 values, E2M1 values
+// times the E4M3 (NVFP4) or E8M0 (MXFP4) block scale.
+template <int FMT, int VPL>
+__device__ __forceinline__ void lane_values(const RowCodes& rc, float (&c)[VPL]) {
+  if constexpr (FMT == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = (float)(int32_t)(int8_t)(uint8_t)(rc.w[i / 4] >> (8 * (i % 4)));
+  } else if constexpr (FMT == 1 || FMT == 3) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t lo, hi;
+      e4m3x4_to_h_hw(rc.w[h], lo, hi);
+      const half2_t a = as_h2(lo), b = as_h2(hi);
+      c[4 * h] = (float)a[0];
+      c[4 * h + 1] = (float)a[1];
+      c[4 * h + 2] = (float)b[0];
+      c[4 * h + 3] = (float)b[1];
+    }
+  } else if constexpr (FMT == 6) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = (float)((int32_t)(rc.w[i / 8] << (28 - 4 * (i % 8))) >> 28);
+  } else {
+    const float bs = FMT == 4 ? e4m3_val(rc.sb) : __uint_as_float((rc.sb & 0xFFu) << 23);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t v[4];
+      e2m1x8_to_h(rc.w[h], v);  // values 8h .. 8h+7 in order
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const half2_t pr = as_h2(v[k]);
+        c[8 * h + 2 * k] = (float)pr[0] * bs;
+        c[8 * h + 2 * k + 1] = (float)pr[1] * bs;
+      }
+    }
+  }
+}
+
+// Grid (ceil(G / HPW), H, B): workgroup x serves heads HPW*x .. of the kv
+// head, one thread per output value.  Every workgroup quantises the new key
+// and value rows (wave 0 and wave 1, D/8 or D/16 lanes); only x == 0 stores
+// them.
+template <int FMT, int D>
+__global__ __launch_bounds__(256) void append_merge_kernel(WriteArgs wa, DecodeArgs a, float post) {
+  constexpr bool K8 = FMT == 1 || FMT == 2 || FMT == 3;
+  constexpr int VPL = K8 ? 8 : 16;  // values per lane
+  constexpr int LPR = D / VPL;      // lanes per row
+  constexpr int HPW = 256 / D;      // heads per workgroup
+  constexpr bool PTH = FMT == 2 || FMT == 3 || FMT == 6;
+  __shared__ float s_v[D];
+  __shared__ float s_lg[HPW];
+
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.G, S = a.num_splits;
+  const int g0 = blockIdx.x * HPW;
+  const int g = g0 + tid / D, d = tid % D;
+  const bool has_out = g < G;
+
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
+  const int64_t slot = wa.slots[b];
+  const bool attend = ctx >= 1 && slot >= 0 && slot < (int64_t)wa.num_pages * wa.P;
+
+  // the splits' records are requested first, so their round trip overlaps
+  // the quantisation
+  const int64_t rf = ws_record_floats(D);
+  const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
+  const int gr = has_out ? g : g0;
+  RecGroup r0;
+  load_recs(recs, rf, S, 0, gr, 2 * kMaxGroup + gr * D + d, r0);
+
+  if (wv < 2 && lane < LPR) {
+    float qv[HPW][VPL];
+    if (wv == 0) {
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        const int gh = g0 + h < G ? g0 + h : g0;
+        const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + gh) * D + VPL * lane;
+#pragma unroll
+        for (int k = 0; k < VPL / 8; ++k) halves8_to_f32(*reinterpret_cast<const uint4*>(qp + 8 * k), qv[h] + 8 * k);
+      }
+    }
+    RowCodes rc;
+    const int64_t row = (int64_t)wv * wa.n_tok * wa.H + (int64_t)b * wa.H + kvh;
+    if constexpr (K8)
+      write_row_8bit<FMT, D>(wa, row, lane, blockIdx.x == 0, &rc);
+    else
+      write_row_4bit<FMT, D>(wa, row, lane, blockIdx.x == 0, &rc);
+    if (attend) {
+      float c[VPL];
+      lane_values<FMT, VPL>(rc, c);
+      const float rs = PTH ? rc.s : 1.0f;
+      if (wv == 0) {
+        const float kconst = (FMT == 1 || FMT == 4) ? a.k_scale * a.qk_scale : a.qk_scale;
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+          float part = 0.0f;
+#pragma unroll
+          for (int i = 0; i < VPL; ++i) part = __builtin_fmaf(qv[h][i], c[i], part);
+          part = group_sum<LPR>(part);
+          if (lane == 0) s_lg[h] = part * (rs * kconst);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) s_v[VPL * lane + i] = c[i] * rs;
+      }
+    }
+  }
+  __syncthreads();
+  if (!has_out) return;
+
+  float M = kNegInf, L = 0.0f, O = 0.0f;
+  merge_recs(r0, M, L, O);
+  for (int s0 = 8; s0 < S; s0 += 8) {
+    RecGroup r;
+    load_recs(recs, rf, S, s0, g, 2 * kMaxGroup + g * D + d, r);
+    merge_recs(r, M, L, O);
+  }
+  if (attend) {
+    const float lg = s_lg[g - g0];
+    const float mc = fmaxf(M, lg);
+    const float f = exp2f(lg - mc);
+    const float sc = exp2f(M - mc);
+    L = L * sc + f;
+    O = O * sc + f * s_v[d];
+  }
+  const float o = L > 0.0f ? O / L * post : 0.0f;
+  a.out[((int64_t)b * a.Hq + kvh * G + g) * D + d] = __builtin_bit_cast(uint16_t, (half_t)o);
+}
+
+template <int FMT>
+hipError_t launch_append_merge_fmt(const WriteArgs& w, const DecodeArgs& a, hipStream_t s) {
+  const float post = (FMT == 1 || FMT == 4) ? a.v_scale : 1.0f;
+  const int hpw = 256 / a.D;
+  const dim3 grid((unsigned)((a.G + hpw - 1) / hpw), (unsigned)a.H, (unsigned)a.B);
+  switch (a.D) {
+    case 32: append_merge_kernel<FMT, 32><<<grid, 256, 0, s>>>(w, a, post); break;
+    case 64: append_merge_kernel<FMT, 64><<<grid, 256, 0, s>>>(w, a, post); break;
+    case 128: append_merge_kernel<FMT, 128><<<grid, 256, 0, s>>>(w, a, post); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
   if (a.n_tok == 0) return hipSuccess;
@@ -567,6 +757,19 @@ hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_append_merge(int fmt, const WriteArgs& w, const DecodeArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  switch (fmt) {
+    case 1: return launch_append_merge_fmt<1>(w, a, s);
+    case 2: return launch_append_merge_fmt<2>(w, a, s);
+    case 3: return launch_append_merge_fmt<3>(w, a, s);
+    case 4: return launch_append_merge_fmt<4>(w, a, s);
+    case 6: return launch_append_merge_fmt<6>(w, a, s);
+    case 7: return launch_append_merge_fmt<7>(w, a, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s) {
   switch (fmt) {

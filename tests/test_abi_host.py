@@ -75,6 +75,18 @@ def test_argument_errors_before_launch(K):
     assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 8, p, 4, p, 2, 0.1, p, p, p, ws, 0, None) == 1  # tail
     assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 8, p, 4, p, 2, 0.1, None, p, p, ws - 1, 0, None) == 3
     assert L.kvq_decode_attention(ctypes.byref(lay), p, p, 8, p, 4, p, 2, float("nan"), None, p, p, ws, 0, None) == 1
+    # one-call decode step: not for KVarN, the new rows are required, then the decode's own checks
+    big = 1 << 30
+    assert L.kvq_decode_attention_append(ctypes.byref(klay), p, p, p, p, p, 8, p, 4, p, 2, 0.1, p, p, big, 0,
+                                         None) == 1
+    assert L.kvq_decode_attention_append(ctypes.byref(lay), p, None, p, p, p, 8, p, 4, p, 2, 0.1, p, p, ws, 0,
+                                         None) == 1
+    assert L.kvq_decode_attention_append(ctypes.byref(lay), p, p, p, None, p, 8, p, 4, p, 2, 0.1, p, p, ws, 0,
+                                         None) == 1
+    assert L.kvq_decode_attention_append(ctypes.byref(lay), p, p, p, p, p, 64, p, 4, p, 2, 0.1, p, p, big, 0,
+                                         None) == 2
+    assert L.kvq_decode_attention_append(ctypes.byref(lay), p, p, p, p, p, 8, p, 4, p, 2, 0.1, p, p, ws - 1, 0,
+                                         None) == 3
     assert L.kvq_dequantize(ctypes.byref(lay), None, p, 1, p, p, None) == 1
 
 

@@ -3,7 +3,9 @@ samples the oracle can afford.
 
 For each workload the GPU quantise-writes the whole context (every token of
 every sequence, one call) and decodes every (sequence, q head) with the split
-plan the benchmark uses.  The oracle quantise-writes two sampled sequences on
+plan the benchmark uses.  As in the benchmark's steps, the formats other than
+KVarN write all but the last token of each sequence first and then write and
+decode the last one in a single kvq_decode_attention_append call.  The oracle quantise-writes two sampled sequences on
 the CPU: every page of those sequences must match the GPU cache byte for byte,
 and sampled (sequence, q head) outputs must match the binary64 oracle within
 |o - o_ref| <= 2e-3 + 2^-10 |o_ref|."""
@@ -48,13 +50,22 @@ def test_full_size_sampled(K, O, name, fmt, flags):
     # GPU: the whole context in one write, then one decode with the
     # benchmark's automatic split plan
     cache = torch.zeros(w.num_pages * pb, dtype=torch.uint8, device="cuda")
-    kd, vd = dev(w.k16), dev(w.v16)
-    K.kvq_quantize_write(lay, kd, vd, dev(w.slots), cache)
+    one_call = fmt != K.KVQ_KVARN_K4V2_G128
+    last = np.arange(w.B) * w.T + (w.T - 1)
+    keep = np.ones(w.B * w.T, bool)
+    if one_call:
+        keep[last] = False
+    kd, vd = dev(w.k16[keep]), dev(w.v16[keep])
+    K.kvq_quantize_write(lay, kd, vd, dev(w.slots[keep]), cache)
     del kd, vd
     ws = K.DecodeWorkspace(lay, w.B, sp.Hq, w.block_tables.shape[1])
     out = torch.empty((w.B, sp.Hq, sp.D), dtype=torch.float16, device="cuda")
     sm = 1.0 / math.sqrt(sp.D)
-    K.kvq_decode_attention(lay, cache, dev(w.q16), dev(w.block_tables), dev(w.ctx_lens), sm, out, ws.buffer)
+    if one_call:
+        K.kvq_decode_attention_append(lay, cache, dev(w.k16[last]), dev(w.v16[last]), dev(w.slots[last]),
+                                      dev(w.q16), dev(w.block_tables), dev(w.ctx_lens), sm, out, ws.buffer)
+    else:
+        K.kvq_decode_attention(lay, cache, dev(w.q16), dev(w.block_tables), dev(w.ctx_lens), sm, out, ws.buffer)
     torch.cuda.synchronize()
     got_cache = cache.cpu().numpy()
     got = out.cpu().numpy().astype(np.float64)
