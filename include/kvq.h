@@ -285,7 +285,9 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
  * cache bytes but attend the new token at position ctx-1 all the same).  A
  * sequence whose slot is negative or outside the pool stores nothing and
  * attends its ctx cached tokens; ctx = 0 stores the token and gives a zero
- * row.  Two sequences must not share a slot.
+ * row.  Two sequences must not share a slot, and no sequence's context may
+ * cover another sequence's new slot (the split kernel reads the cache before
+ * the new tokens are stored).
  * With a split context this is two launches, the split kernel (reading one
  * token less) and a merge kernel that also quantises, stores and attends the
  * new tokens, so no write launch precedes the split kernel.  With a single
