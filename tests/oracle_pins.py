@@ -227,6 +227,83 @@ def pin_int4_pth(O, rng=None):
                 assert np.array_equal(got[i, h], q * float(sb[:4].view(np.float32)[0]))
 
 
+def _torch_int_pth(x16, qmax):
+    """The glossary's per-token-head rule as its script states it, run by torch
+    in binary32 on the CPU: |x| maximum floored at 1e-8, then / qmax; codes
+    torch.round(x / scale) (half to even), clamped to +-qmax."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x16, dtype=np.float16)).to(torch.float32)
+    scale = t.abs().amax(dim=-1, keepdim=True).clamp_min(1e-8) / qmax
+    q = torch.round(t / scale).clamp(-qmax, qmax)
+    return q.to(torch.int64).numpy(), scale.numpy()[..., 0]
+
+
+def _finite_halves_upto(M):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    h = h[np.isfinite(h)]
+    return h[np.abs(h.astype(np.float64)) <= M]
+
+
+def _sweep_rows(M, D=128):
+    """Every finite binary16 value of magnitude <= M, in rows of D whose first
+    entry is M (so M is every row's maximum)."""
+    vals = _finite_halves_upto(M)
+    n = D - 1
+    pad = (-len(vals)) % n
+    vals = np.concatenate([vals, np.zeros(pad, np.float16)]).reshape(-1, n)
+    return np.concatenate([np.full((len(vals), 1), M, np.float16), vals], axis=1)
+
+
+# row maxima of the sweep: the exact-tie maxima 127 * 7 * 2^-9, 127 * 13 * 2^-9,
+# 127 * 15 * 2^-9 (scale 7, 13, 15 * 2^-9), 7 * 7 (INT4 scale 7), plus plain ones
+_SWEEP_MAXIMA = (1.736328125, 3.224609375, 3.720703125, 49.0, 3.0, 0.1, 65504.0, 2.0 ** -24)
+
+
+def pin_int_rule_order(O):
+    """[P3] §可运行 fake-quant 实验 fixes the integer rule's order of operations:
+    the maximum is floored at 1e-8 before the division by 127, and values are
+    divided by the scale (not multiplied by a reciprocal), rounding half to even.
+    Pinned two ways: hand-worked rows whose expected codes and scale bits follow
+    from exact rational arithmetic (tests/golden/int_rule_order.txt: all-zero
+    rows, a subnormal maximum, exact .5 ties), and torch running the script's
+    rule on every finite binary16 value under several row maxima (INT8 and, by
+    reading R39, INT4 with 7 for 127), codes and scale bits equal."""
+    fmt_of = {127: oracle.INT8_PTH, 7: oracle.INT4_PTH}
+    n_lines = 0
+    with open(os.path.join(GOLDEN, "int_rule_order.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("->")
+            name, qmax, sbits, *vals = lhs.split()
+            want = [int(c) for c in rhs.split()]
+            x16 = np.zeros(128, np.float16)
+            x16[:len(vals)] = [float(v) for v in vals]
+            assert np.array_equal(x16[:len(vals)].astype(np.float64), [float(v) for v in vals]), name
+            codes, sb = O.quantize_row(fmt_of[int(qmax)], x16)
+            q = codes.view(np.int8).astype(np.int64) if int(qmax) == 127 else (codes.astype(np.int64) ^ 8) - 8
+            got_bits = int(sb[:4].view(np.uint32)[0])
+            assert got_bits == int(sbits, 16), f"{name}/{qmax}: scale bits {got_bits:#010x} != {sbits}"
+            assert list(q[:len(want)]) == want, f"{name}/{qmax}: codes {list(q[:len(want)])} != {want}"
+            assert not np.any(q[len(vals):]), name
+            n_lines += 1
+    assert n_lines == 6
+    for qmax, fmt in ((127, oracle.INT8_PTH), (7, oracle.INT4_PTH)):
+        for M in _SWEEP_MAXIMA:
+            rows = _sweep_rows(M)
+            rows = np.concatenate([rows, np.zeros((1, 128), np.float16)])
+            tq, ts = _torch_int_pth(rows, qmax)
+            for i, x16 in enumerate(rows):
+                codes, sb = O.quantize_row(fmt, x16)
+                q = codes.view(np.int8).astype(np.int64) if qmax == 127 else (codes.astype(np.int64) ^ 8) - 8
+                assert sb[:4].view(np.float32)[0].view(np.uint32) == np.float32(ts[i]).view(np.uint32), \
+                    (qmax, M, i)
+                bad = np.nonzero(q != tq[i])[0]
+                assert not len(bad), f"qmax {qmax}, max {M}: x={x16[bad[:3]]} oracle {q[bad[:3]]} torch {tq[i][bad[:3]]}"
+
+
 def pin_fp8_pth(O, rng=None):
     rng = rng or np.random.default_rng(4)
     for D in (32, 128):
@@ -247,6 +324,27 @@ def pin_fp8_pth(O, rng=None):
             assert np.all(np.abs(x - xh) <= float(s) * (2.0 ** (e - 4)) * (1 + 2.0 ** -10))
             i = np.argmax(np.abs(x))
             assert codes[i] & 0x7F == 0x7E  # max |x| maps to 448 = FP8_MAX
+    # hand-worked exact ties (tests/golden/fp8_pth_ties.txt)
+    with open(os.path.join(GOLDEN, "fp8_pth_ties.txt")) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(lines) == 1
+    for line in lines:
+        lhs, rhs = line.split("->")
+        _, sbits, *vals = lhs.split()
+        x16 = np.zeros(128, np.float16)
+        x16[:len(vals)] = [float(v) for v in vals]
+        codes, sb = O.quantize_row(oracle.FP8_PTH, x16)
+        assert int(sb[:4].view(np.uint32)[0]) == int(sbits, 16)
+        assert [int(c) for c in codes[:len(vals)]] == [int(c, 16) for c in rhs.split()], codes[:len(vals)]
+    # every finite binary16 value under row maxima with exact ties (448 * 7, 448 * 13,
+    # 448 * 15 * 2^-10) and plain ones: the scale is the page's max / 448 and the
+    # codes torch's E4M3 of the true quotient
+    for M in (3136.0, 5824.0, 6.5625, 448.0, 1.0):
+        for x16 in _sweep_rows(M):
+            codes, sb = O.quantize_row(oracle.FP8_PTH, x16)
+            s = F32(M) / F32(448)
+            assert sb[:4].view(np.float32)[0] == s
+            assert np.array_equal(codes, _torch_e4m3(x16.astype(np.float32) / s)), M
 
 
 def pin_fp8_pt(O, rng=None):
@@ -316,6 +414,33 @@ def pin_nvfp4(O, rng=None):
         vals = np.array([O.e2m1_decode(int(c)) for c in codes])
         rec = st * np.repeat(_torch_e4m3_decode(bsc[:8]), 16) * vals
         assert np.array_equal(rec, x.astype(np.float64))
+
+
+def pin_nvfp4_scale_order(O):
+    """Hand-worked blocks (tests/golden/nvfp4_scale_order.txt) whose E4M3 block
+    scale depends on the association of the reading's (max / 6) / s_t: its
+    quotient lands on one side of an E4M3 midpoint while max / (6 s_t) lands
+    on the other, or exactly on it.  The expected codes follow from exact
+    rational arithmetic, written out in the fixture."""
+    n = 0
+    with open(os.path.join(GOLDEN, "nvfp4_scale_order.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("->")
+            name, st_bits, amax = lhs.split()
+            st = float(np.uint32(int(st_bits, 16)).view(np.float32))
+            x16 = np.zeros(128, np.float16)
+            for b in range(8):
+                x16[16 * b] = float(amax)
+            assert float(x16[0]) == float(amax)
+            for flags in (0, oracle.FLAG_NVFP4_4OVER6):
+                codes, bsc = O.quantize_row(oracle.NVFP4, x16, st, flags)
+                if flags == 0:
+                    assert list(bsc[:8]) == [int(rhs)] * 8, f"{name}: block scale {bsc[:8]} != {rhs}"
+            n += 1
+    assert n == 2
 
 
 def _pow2_exponent_brute(a):
@@ -585,6 +710,50 @@ def pin_kvarn_tile(O, rng=None):
     assert np.all(np.isfinite(o["meta"]))
 
 
+def _kvarn_factors_log_domain(x16, sweeps):
+    """[P2] §技术原理's normalisation in its own terms, in binary64: rotate
+    every token row by the normalised Walsh-Hadamard matrix (scipy), then per
+    sweep add log sigma of every token row to the row's log factor, and then
+    log sigma of every channel column to the column's log factor, sigma being
+    the population deviation of the rotated tile divided by the current
+    factors.  Returns the factors exp(log r), exp(log c)."""
+    from scipy.linalg import hadamard
+    Hm = hadamard(128).astype(np.float64) / math.sqrt(128.0)
+    X = x16.astype(np.float64) @ Hm
+    lr, lc = np.zeros(128), np.zeros(128)
+    for _ in range(sweeps):
+        sd = (X * np.exp(-lr[:, None] - lc[None, :])).std(axis=1)
+        lr += np.log(np.where(sd > 0, sd, 1.0))
+        sd = (X * np.exp(-lr[:, None] - lc[None, :])).std(axis=0)
+        lc += np.log(np.where(sd > 0, sd, 1.0))
+    return np.exp(lr), np.exp(lc)
+
+
+def pin_kvarn_sweeps(O, rng=None):
+    """The KVarN preset runs 4 sweeps (token pass, then channel pass): the
+    oracle's binary32 token and channel factors, and the metadata that stores
+    them (K rho = r, V gamma = c), match the binary64 log-domain formulation
+    at 4 sweeps to 1e-5 relative; 3 or 5 sweeps differ by ~1e-3, so a wrong
+    count fails."""
+    rng = rng or np.random.default_rng(15)
+    x = rng.standard_normal((128, 128)).astype(np.float32)
+    x[:, 7] *= 8
+    x[:, 90] *= 8
+    y = (rng.standard_normal((128, 128)) * np.exp(rng.standard_normal((128, 1)))
+         * np.exp(rng.standard_normal((1, 128))))
+    for tile in (x.astype(np.float16), y.astype(np.float16)):
+        for side in (0, 1):
+            o = O.kvarn_tile(tile, side)
+            r, c = _kvarn_factors_log_domain(tile, 4)
+            assert np.max(np.abs(o["r"] / r - 1)) <= 1e-5, np.max(np.abs(o["r"] / r - 1))
+            assert np.max(np.abs(o["c"] / c - 1)) <= 1e-5, np.max(np.abs(o["c"] / c - 1))
+            stored = o["meta"][2]
+            assert np.array_equal(stored, o["r"] if side == 0 else o["c"])
+            for other in (3, 5):
+                r2, c2 = _kvarn_factors_log_domain(tile, other)
+                assert np.max(np.abs(r2 / r - 1)) > 1e-4 and np.max(np.abs(c2 / c - 1)) > 1e-4
+
+
 # --------------------------------------------------------------------------- #
 # attention
 # --------------------------------------------------------------------------- #
@@ -734,5 +903,6 @@ def _attention_kvarn_case(O, rng, P):
 ALL_PINS = [
     pin_half_widening, pin_e4m3_decode, pin_e4m3_encode, pin_e2m1_encode, pin_int8_pth, pin_int4_pth, pin_fp8_pth,
     pin_fp8_pt, pin_nvfp4, pin_mxfp4, pin_page_bytes, pin_glossary_bytes, pin_layout_bijective, pin_kvarn_rotation,
-    pin_kvarn_tile, pin_kvarn_pages, pin_attention, pin_attention_kvarn,
+    pin_kvarn_tile, pin_kvarn_pages, pin_attention, pin_attention_kvarn, pin_int_rule_order, pin_nvfp4_scale_order,
+    pin_kvarn_sweeps,
 ]

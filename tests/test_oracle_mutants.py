@@ -58,6 +58,20 @@ MUTANTS = [
     ("kvarn_second_tile_over_first", "uint8_t* ch = chunk_at(L, cache, page, h) + (s0 % P) / 128 * KVARN_TILE_BYTES;",
      "uint8_t* ch = chunk_at(L, cache, page, h);", 0, [pins.pin_kvarn_pages, pins.pin_layout_bijective]),
     ("kvarn_read_first_tile", "ch += (int64_t)(t / 128) * KVARN_TILE_BYTES;", "(void)0;", 0, [pins.pin_kvarn_pages]),
+    ("int8_floor_after_divide", "float s = fmaxf(a, 1e-8f) / 127.0f;", "float s = fmaxf(a / 127.0f, 1e-8f);", 0,
+     [pins.pin_int_rule_order]),
+    ("int8_reciprocal_product", "float y = x[d] / s;", "float y = x[d] * (1.0f / s);", 0,
+     [pins.pin_int_rule_order]),
+    ("int4_floor_after_divide", "float s = fmaxf(a, 1e-8f) / 7.0f;", "float s = fmaxf(a / 7.0f, 1e-8f);", 0,
+     [pins.pin_int_rule_order]),
+    ("int4_reciprocal_product", "float y = x[d] / s;", "float y = x[d] * (1.0f / s);", 1,
+     [pins.pin_int_rule_order]),
+    ("fp8_pth_reciprocal_product", "codes[d] = kvqo_e4m3_encode(x[d] / s);",
+     "codes[d] = kvqo_e4m3_encode(x[d] * (1.0f / s));", 0, [pins.pin_fp8_pth]),
+    ("kvarn_three_sweeps", "#define KVARN_ITERS 4", "#define KVARN_ITERS 3", 0, [pins.pin_kvarn_sweeps]),
+    ("kvarn_eight_sweeps", "#define KVARN_ITERS 4", "#define KVARN_ITERS 8", 0, [pins.pin_kvarn_sweeps]),
+    ("nvfp4_scale_divisor_product", "kvqo_e4m3_encode((a / 6.0f) / st)", "kvqo_e4m3_encode(a / (6.0f * st))", 0,
+     [pins.pin_nvfp4_scale_order]),
     ("chunk_head_major", "return (uint8_t*)cache + (page * L->num_kv_heads + h) * kvqo_chunk_bytes(L);",
      "return (uint8_t*)cache + ((int64_t)h * L->num_pages + page) * kvqo_chunk_bytes(L);", 0,
      [pins.pin_layout_bijective]),

@@ -1,0 +1,27 @@
+"""The CPU oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+(gcc, host code only) and driven through every exported function by
+tests/sanitize/oracle_driver.c: an out-of-bounds access, a leak or undefined
+behaviour anywhere in the oracle fails the test (CPU only)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_oracle_under_sanitizers(tmp_path):
+    exe = str(tmp_path / "oracle_driver")
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           os.path.join(ROOT, "oracle", "kvq_oracle.c"), os.path.join(HERE, "sanitize", "oracle_driver.c"),
+           "-o", exe, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    env.pop("LD_PRELOAD", None)
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "all calls done" in r.stdout
