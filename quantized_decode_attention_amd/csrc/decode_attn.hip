@@ -174,9 +174,12 @@ __device__ __forceinline__ half8_t k_operand(const Raw<FMT, D>& r, int kk, half2
   } else if constexpr (FMT != 4) {
     half2_t a, b, c, d;
     if constexpr (FMT == 2) {
-      // biased: binary16 1152 + code; the bias is removed from the scores
-      i8x4_to_h_biased(r.k[2 * kk], a, b);
-      i8x4_to_h_biased(r.k[2 * kk + 1], c, d);
+      // signed codes, exact in binary16.  (Feeding 1152 + code and removing
+      // 1152 * sum(q) from the scores afterwards saves the subtraction, but
+      // the bias then dominates the binary32 sums: with a query of mean 16
+      // the scores lose ~1e-2 to cancellation.)
+      i8x4_to_h(r.k[2 * kk], a, b);
+      i8x4_to_h(r.k[2 * kk + 1], c, d);
     } else {
       uint32_t p0, p1, p2, p3;
       e4m3x4_to_h_hw(r.k[2 * kk], p0, p1);
@@ -411,10 +414,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   }
 
   const float kconst = (FMT == 1 || FMT == 4) ? a.k_scale * a.qk_scale : a.qk_scale;
-  // INT8 keys enter the MFMA as binary16 1152 + code, INT4 keys as code + 8:
-  // remove the offset times sum(q)
+  // INT4 keys enter the MFMA as code + 8: remove 8 * sum(q) from the scores
+  // (small enough not to cost accuracy: 8 against codes up to 7)
   float kbias = 0.0f;
-  if constexpr (FMT == 2 || FMT == 6) {
+  if constexpr (FMT == 6) {
     float qs = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
       for (int e = 0; e < 8; ++e) qs += (float)qB[kk][e];
     qs += __shfl_xor(qs, 16);
     qs += __shfl_xor(qs, 32);
-    kbias = (FMT == 2 ? 1152.0f : 8.0f) * qs;
+    kbias = 8.0f * qs;
   }
   WaveState<D> st;
 #pragma unroll

@@ -143,14 +143,6 @@ __device__ __forceinline__ void i8x4_to_h(uint32_t w, half2_t& lo, half2_t& hi) 
   hi = as_h2(perm(0x64646464u, u, 0x04030402u)) - bias;
 }
 
-// The same without the subtraction: binary16 1152 + code, exact; callers
-// remove the bias once from a dot product.
-__device__ __forceinline__ void i8x4_to_h_biased(uint32_t w, half2_t& lo, half2_t& hi) {
-  uint32_t u = w ^ 0x80808080u;
-  lo = as_h2(perm(0x64646464u, u, 0x04010400u));
-  hi = as_h2(perm(0x64646464u, u, 0x04030402u));
-}
-
 // ---------------------------------------------------------------------------
 // gfx950 hardware conversions, issued directly: the compiler's lowering of the
 // matching builtins repacks the two binary16 results when they are used one by
