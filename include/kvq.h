@@ -14,7 +14,9 @@
  *     current HIP device, unless stated.  The caller owns every buffer; the
  *     library allocates no device memory and keeps no device state between
  *     calls (it only memoises, per device, the host-side answers of the HIP
- *     compute-unit and occupancy queries behind the split plan).
+ *     compute-unit and occupancy queries behind the split plan), apart from
+ *     the fixed device array that kvq_decode_attention_noalloc uses as its
+ *     workspace, which is part of the library's code object.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; the returned status covers argument validation and
  *     kernel-launch errors only.
@@ -97,8 +99,14 @@ typedef enum {
   KVQ_ERR_UNSUPPORTED = 2,         /* valid request this build does not serve */
   KVQ_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace smaller than required */
   KVQ_ERR_DEVICE = 4,              /* current device is not gfx950 */
-  KVQ_ERR_HIP = 5                  /* a HIP call failed (launch error) */
+  KVQ_ERR_HIP = 5,                 /* a HIP call failed (launch error) */
+  KVQ_ERR_SCRATCH_TOO_SMALL = 6    /* problem needs more than KVQ_DECODE_SCRATCH_BYTES of
+                                      split records (kvq_decode_attention_noalloc) */
 } kvq_status;
+
+/* Size of the fixed per-device workspace of kvq_decode_attention_noalloc:
+ * 16 MiB, i.e. 4032 split records at head size 128 (4160 bytes each). */
+#define KVQ_DECODE_SCRATCH_BYTES (16u << 20)
 
 /* One attention layer's cache description.
  *   format       kvq_format
@@ -265,6 +273,29 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
                                 int32_t batch, float sm_scale, const void* kvarn_tail, void* out,
                                 void* workspace, int64_t workspace_bytes, int32_t num_splits,
                                 void* stream);
+
+/* kvq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The split records live in a fixed
+ * device array of KVQ_DECODE_SCRATCH_BYTES that the library defines; every
+ * GPU it runs on holds one copy until the process ends.  The call itself
+ * allocates nothing (no hipMalloc or hipFree, no allocating library routine);
+ * its first call on a device looks up that device's copy of the array.
+ *   Arguments, plan, kernels and results are those of kvq_decode_attention
+ *   (same outputs bit for bit); the records need no initialisation, so the
+ *   array's contents left by an earlier call do not matter.
+ *   All calls on one GPU share its array: two calls that overlap in time on
+ *   one device (on different streams, or from different host threads) race
+ *   and give undefined results.  Calls in one stream are ordered.
+ * Errors: those of kvq_decode_attention (the workspace ones excepted), and
+ * KVQ_ERR_SCRATCH_TOO_SMALL, before anything is launched, when the problem
+ * needs more than KVQ_DECODE_SCRATCH_BYTES of records (kvq_decode_workspace_bytes
+ * with the same arguments tells). */
+kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const void* cache, const void* q,
+                                        int32_t num_q_heads, const int32_t* block_tables,
+                                        int32_t max_pages_per_seq, const int32_t* context_lens,
+                                        int32_t batch, float sm_scale, const void* kvarn_tail, void* out,
+                                        int32_t num_splits, void* stream);
 
 /* One decode step in one call: quantise-write each sequence's new token and
  * run decode attention over its context, the new token included ([P5]

@@ -32,7 +32,8 @@ FORMAT_NAMES = {1: "fp8_per_tensor", 2: "int8_per_token_head", 3: "fp8_per_token
                 5: "kvarn_k4v2_g128", 6: "int4_per_token_head", 7: "mxfp4"}
 
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "KVQ_ERR_WORKSPACE_TOO_SMALL",
-          4: "KVQ_ERR_DEVICE", 5: "KVQ_ERR_HIP"}
+          4: "KVQ_ERR_DEVICE", 5: "KVQ_ERR_HIP", 6: "KVQ_ERR_SCRATCH_TOO_SMALL"}
+KVQ_DECODE_SCRATCH_BYTES = 16 << 20
 
 
 class KvqError(RuntimeError):
@@ -70,6 +71,7 @@ def _load():
         "kvq_decode_attention": (ctypes.c_int, [LP, P, P, I32, P, I32, P, I32, F32, P, P, P, I64, I32, P]),
         "kvq_decode_attention_append": (ctypes.c_int, [LP, P, P, P, P, P, I32, P, I32, P, I32, F32, P, P, I64, I32,
                                                         P]),
+        "kvq_decode_attention_noalloc": (ctypes.c_int, [LP, P, P, I32, P, I32, P, I32, F32, P, P, I32, P]),
         "kvq_dequantize": (ctypes.c_int, [LP, P, P, I64, P, P, P]),
         "kvq_kvarn_append": (ctypes.c_int, [LP, P, P, P, P, I64, P, I32, P, I32, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -163,6 +165,20 @@ def kvq_decode_attention(lay: KvqLayout, cache, q, block_tables, context_lens, s
         _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
         0 if workspace is None else workspace.numel(), num_splits, _stream(stream)),
         "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(lay: KvqLayout, cache, q, block_tables, context_lens, sm_scale, out,
+                                 kvarn_tail=None, num_splits: int = 0, stream=None):
+    """kvq_decode_attention with the library's fixed device workspace instead of a caller's buffer (no
+    allocation in the call; calls that overlap in time on one GPU race)."""
+    import torch
+    B, Hq, _ = q.shape
+    _check(_lib.kvq_decode_attention_noalloc(
+        ctypes.byref(lay), _ptr(cache, torch.uint8, "cache"), _ptr(q, torch.float16, "q"), Hq,
+        _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _ptr(context_lens, torch.int32, "context_lens"), B, float(sm_scale),
+        _ptr(kvarn_tail, torch.float16, "kvarn_tail"), _ptr(out, torch.float16, "out"), num_splits,
+        _stream(stream)), "kvq_decode_attention_noalloc")
 
 
 def kvq_decode_attention_append(lay: KvqLayout, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens,

@@ -30,6 +30,7 @@ SOURCES = {
     "dequant.hip": ["-ffp-contract=off"],
     "decode_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "kvarn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "decode_scratch.hip": [],
 }
 
 COMMON = [

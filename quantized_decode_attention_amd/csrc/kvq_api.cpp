@@ -231,11 +231,12 @@ WriteArgs write_args(const kvq_layout* L, const void* k, const void* v, const in
   return a;
 }
 
-// Argument checks shared by the decode entry points; on success the plan.
-kvq_status check_decode(const kvq_layout* L, const void* cache, const void* q, int32_t num_q_heads,
-                        const int32_t* block_tables, int32_t max_pages_per_seq, const int32_t* context_lens,
-                        int32_t batch, float sm_scale, void* out, void* workspace, int64_t workspace_bytes,
-                        int32_t num_splits, int* splits, int* pps, int* waves) {
+// Argument checks shared by the decode entry points, up to the workspace; on
+// success the plan and the workspace bytes it needs.
+kvq_status check_decode_plan(const kvq_layout* L, const void* cache, const void* q, int32_t num_q_heads,
+                             const int32_t* block_tables, int32_t max_pages_per_seq, const int32_t* context_lens,
+                             int32_t batch, float sm_scale, void* out, int32_t num_splits, int* splits, int* pps,
+                             int* waves, int64_t* need) {
   kvq_status st = check_layout(L);
   if (st != KVQ_OK) return st;
   const int H = L->num_kv_heads;
@@ -246,7 +247,19 @@ kvq_status check_decode(const kvq_layout* L, const void* cache, const void* q, i
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
   if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
   plan(L, batch, G, max_pages_per_seq, num_splits, splits, pps, waves);
-  const int64_t need = workspace_bytes_for(L, batch, *splits);
+  *need = workspace_bytes_for(L, batch, *splits);
+  return KVQ_OK;
+}
+
+// The same, then the caller's workspace and the device.
+kvq_status check_decode(const kvq_layout* L, const void* cache, const void* q, int32_t num_q_heads,
+                        const int32_t* block_tables, int32_t max_pages_per_seq, const int32_t* context_lens,
+                        int32_t batch, float sm_scale, void* out, void* workspace, int64_t workspace_bytes,
+                        int32_t num_splits, int* splits, int* pps, int* waves) {
+  int64_t need = 0;
+  const kvq_status st = check_decode_plan(L, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens,
+                                          batch, sm_scale, out, num_splits, splits, pps, waves, &need);
+  if (st != KVQ_OK) return st;
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;
   return current_device_ok();
@@ -374,6 +387,31 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
   return from_hip(launch_decode(layout->format, a, static_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const void* cache, const void* q,
+                                        int32_t num_q_heads, const int32_t* block_tables, int32_t max_pages_per_seq,
+                                        const int32_t* context_lens, int32_t batch, float sm_scale,
+                                        const void* kvarn_tail, void* out, int32_t num_splits, void* stream) {
+  if (kvarn_tail && layout && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
+  int splits, pps, waves;
+  int64_t need = 0;
+  kvq_status st = check_decode_plan(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens,
+                                    batch, sm_scale, out, num_splits, &splits, &pps, &waves, &need);
+  if (st != KVQ_OK) return st;
+  if (need > (int64_t)KVQ_DECODE_SCRATCH_BYTES) return KVQ_ERR_SCRATCH_TOO_SMALL;
+  if ((st = current_device_ok()) != KVQ_OK || batch == 0) return st;
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = decode_scratch(&scratch);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  DecodeArgs a = decode_args(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens, batch,
+                             sm_scale, out, scratch, splits, pps, waves);
+  a.tail = static_cast<const uint16_t*>(kvarn_tail);
+  if (layout->format == KVQ_KVARN_K4V2_G128)
+    return from_hip(launch_kvarn_decode(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_decode(layout->format, a, static_cast<hipStream_t>(stream)));
+}
+
 kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, const void* k_new,
                                        const void* v_new, const int64_t* slot_mapping, const void* q,
                                        int32_t num_q_heads, const int32_t* block_tables,
@@ -433,6 +471,8 @@ const char* kvq_status_string(kvq_status status) {
     case KVQ_ERR_WORKSPACE_TOO_SMALL: return "decode workspace too small";
     case KVQ_ERR_DEVICE: return "current device is not an MI355X (gfx950)";
     case KVQ_ERR_HIP: return "HIP kernel launch failed";
+    case KVQ_ERR_SCRATCH_TOO_SMALL:
+      return "problem needs more split records than the fixed decode workspace (KVQ_DECODE_SCRATCH_BYTES) holds";
   }
   return "unknown status";
 }

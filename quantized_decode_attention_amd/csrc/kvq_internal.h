@@ -84,6 +84,10 @@ hipError_t launch_append_merge(int fmt, const WriteArgs& w, const DecodeArgs& a,
 hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s);
 
+// Device address of the current device's fixed decode workspace
+// (KVQ_DECODE_SCRATCH_BYTES), looked up on the first call per device.
+hipError_t decode_scratch(void** ptr);
+
 // Resident workgroups per compute unit of the decode split kernel for a
 // format, head size and GQA group on the current device (0 if unknown).
 int decode_blocks_per_cu(int fmt, int D, int G);

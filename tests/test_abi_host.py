@@ -88,6 +88,22 @@ def test_argument_errors_before_launch(K):
     assert L.kvq_decode_attention_append(ctypes.byref(lay), p, p, p, p, p, 8, p, 4, p, 2, 0.1, p, p, ws - 1, 0,
                                          None) == 3
     assert L.kvq_dequantize(ctypes.byref(lay), None, p, 1, p, p, None) == 1
+    # allocation-free decode: the decode's checks, then the fixed workspace's size
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(lay), p, p, 6, p, 4, p, 2, 0.1, None, p, 0, None) == 1
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(lay), p, p, 64, p, 4, p, 2, 0.1, None, p, 0, None) == 2
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(lay), p, p, 8, p, 4, p, 2, 0.1, p, p, 0, None) == 1
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(lay), None, p, 8, p, 4, p, 2, 0.1, None, p, 0, None) == 1
+    rec = (2 * 8 + 8 * 128) * 4
+    fits = K.KVQ_DECODE_SCRATCH_BYTES // rec  # records the fixed workspace holds
+    assert fits == 4032
+    # KVarN always keeps one record per (sequence, kv head): batch * 4 records at one split
+    big_b = fits // 4 + 1
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(klay), p, p, 32, p, 4, p, big_b, 0.1, None, p, 1,
+                                          None) == 6
+    assert K.kvq_decode_workspace_bytes(klay, big_b, 32, 4, 1) > K.KVQ_DECODE_SCRATCH_BYTES
+    assert K.kvq_decode_workspace_bytes(klay, big_b - 1, 32, 4, 1) <= K.KVQ_DECODE_SCRATCH_BYTES
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(lay), p, p, 8, p, 4000, p, 16, 0.1, None, p, 256,
+                                          None) == 6
 
 
 def test_split_plan_and_workspace(K):
@@ -119,8 +135,9 @@ def test_split_plan_and_workspace(K):
 
 
 def test_status_strings(K):
-    for st in range(6):
+    for st in range(7):
         assert K.kvq_status_string(st)
+    assert "KVQ_DECODE_SCRATCH_BYTES" in K.kvq_status_string(6)
     assert "gfx950" in K.kvq_status_string(4)
 
 
