@@ -241,14 +241,14 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
             "us": round(ms * 1e3, 2)}
 
 
-# HBM traffic of one decode call, measured with rocprofv3 counters and kept in
-# a profile summary together with a digest of the decode kernel's sources: the
-# figure is reported only while those sources are unchanged (comments and
-# blank lines aside).
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int8_32k_traffic.md")
-# the decode call: split kernel (decode_attn.hip) and the merge that writes and attends the new tokens
-# (quant_write.hip)
-DECODE_SOURCES = ("decode_attn.hip", "quant_write.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
+# HBM traffic of every workload's decode call and whole-context write,
+# measured with rocprofv3 counters and kept in a profile summary together with
+# a digest of the kernels' sources: a figure is reported only while those
+# sources are unchanged (comments and blank lines aside).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_all_formats.md")
+# every source a decode call or a write launch compiles from, and the build flags
+KERNEL_SOURCES = ("decode_attn.hip", "quant_write.hip", "kvarn_decode.hip", "kvarn_write.hip", "decode_common.h",
+                  "kvq_device.h", "kvq_internal.h")
 
 
 def _code_only(text):
@@ -260,35 +260,48 @@ def _code_only(text):
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
-def decode_sources_digest():
+def kernel_sources_digest():
     import hashlib
 
     from quantized_decode_attention_amd import _build
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in KERNEL_SOURCES:
         with open(os.path.join(_build.CSRC, name), encoding="utf-8") as f:
             h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
-    h.update(" ".join(_build.SOURCES["decode_attn.hip"] + _build.SOURCES["quant_write.hip"] + _build.COMMON[:4]).encode())
+    for src in ("decode_attn.hip", "quant_write.hip", "kvarn_decode.hip", "kvarn_write.hip"):
+        h.update(" ".join(_build.SOURCES[src]).encode())
+    h.update(" ".join(_build.COMMON[:4]).encode())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """Bytes per decode call from the committed counter summary, or None when
-    there is none for this workload or the kernel changed since."""
-    if workload != "int8_32k" or not os.path.exists(TRAFFIC_FILE):
-        return None
-    vals = {}
+def _traffic_table():
+    """{(key, what): bytes} from the summary's machine-readable lines
+    `traffic <key> <decode|write> = <bytes>`, or {} when the digest no longer
+    matches the sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    vals, digest = {}, None
     with open(TRAFFIC_FILE) as f:
         for line in f:
             parts = line.strip().strip("`").split(" = ")
-            if len(parts) == 2:
-                vals[parts[0].strip()] = parts[1].strip()
-    if vals.get("decode_sources_sha256") != decode_sources_digest():
-        return None
-    try:
-        return int(vals["traffic_bytes_per_call"])
-    except (KeyError, ValueError):
-        return None
+            if len(parts) != 2:
+                continue
+            lhs, rhs = parts[0].split(), parts[1].strip()
+            if lhs == ["kernel_sources_sha256"]:
+                digest = rhs
+            elif len(lhs) == 3 and lhs[0] == "traffic":
+                try:
+                    vals[(lhs[1], lhs[2])] = int(rhs)
+                except ValueError:
+                    pass
+    return vals if digest == kernel_sources_digest() else {}
+
+
+def measured_traffic(key, what="decode"):
+    """HBM bytes per decode call (or per whole-context write) of a workload
+    entry (`workload/format`), from the committed counter summary; None when
+    there is none or the kernels changed since the counters were taken."""
+    return _traffic_table().get((key, what))
 
 
 def cpu_formats(K):
@@ -347,12 +360,58 @@ def cpu_baseline(name, fmt, flags, n_seq, threads):
     }
 
 
+# format name -> (kvq_format, flags)
+FORMAT_CHOICES = {"fp8_per_tensor": (1, 0), "int8_per_token_head": (2, 0), "fp8_per_token_head": (3, 0),
+                  "nvfp4": (4, 0), "nvfp4_4over6": (4, 1), "kvarn_k4v2_g128": (5, 0), "int4_per_token_head": (6, 0),
+                  "mxfp4": (7, 0)}
+
+
+WORKLOAD_FORMAT = {"int8_32k": "int8_per_token_head", "fp8_sink_4k": "fp8_per_token_head", "nvfp4_16k": "nvfp4",
+                   "kvarn_16k": "kvarn_k4v2_g128", "nvfp4_16k_tp2": "nvfp4", "kvarn_16k_tp2": "kvarn_k4v2_g128"}
+
+
+def main_format(workload, fmt_name=""):
+    """(kvq_format, flags) of the main workload: its own format, or the one
+    named; None for an unknown name or a KVarN / paged-format mismatch."""
+    if workload not in WORKLOAD_FORMAT:
+        return None
+    f = FORMAT_CHOICES.get(fmt_name or WORKLOAD_FORMAT[workload])
+    if f is None or (f[0] == 5) != workload.startswith("kvarn"):
+        return None
+    return f
+
+
+def entry_key(K, name, fmt, flags):
+    """`workload/format` key of a bench entry (and of its traffic figures)."""
+    return f"{name}/{K.FORMAT_NAMES[fmt]}" + ("_4over6" if flags else "")
+
+
+def decode_kernel_name(p):
+    """The kernels of one decode call of a bench entry."""
+    G = p.sp.Hq // p.sp.Hkv
+    if p.kvarn:
+        return f"kvarn_decode_kernel<{G}> + kvarn_merge_kernel<{G}>"
+    # eight-wave workgroups when the plan runs a single split over at least
+    # one (sequence, kv head) per compute unit (kvq.h)
+    waves = 8 if p.ws.num_splits == 1 and p.fmt in (1, 2, 3) and p.w.B * p.sp.Hkv >= 256 else 4
+    return (f"decode_kernel<{p.fmt}, {p.sp.D}, {G}, {waves}>"
+            + (" + append_merge_kernel" if p.ws.num_splits > 1 else " after quant_write"))
+
+
+def write_bytes(p):
+    """Bytes a whole-context write moves: the binary16 K and V read, the cache written."""
+    w, sp = p.w, p.sp
+    return 2 * w.B * w.T * sp.Hkv * sp.D * 2 + w.B * (w.T // sp.P) * p.page_bytes
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="int8_32k")
+    ap.add_argument("--workload", default="int8_32k", choices=sorted(WORKLOAD_FORMAT))
+    ap.add_argument("--format", default="", help="format of the main workload (default: the workload's own; "
+                    "one of " + ", ".join(FORMAT_CHOICES) + ")")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-formats", action="store_true", help="skip the other formats' workloads")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences of the CPU baseline (0 = the whole batch)")
@@ -367,6 +426,12 @@ def main():
             "build runs and reports a single MI355X only.  Use --gpus 1.")
         sys.exit(2)
 
+    main_fmt = main_format(args.workload, args.format)
+    if main_fmt is None:
+        log(f"no format {args.format!r} for workload {args.workload!r}: KVarN runs only on the kvarn workloads "
+            f"(page 128) and they only with KVarN; formats: {', '.join(FORMAT_CHOICES)}")
+        sys.exit(2)
+
     import torch
 
     import quantized_decode_attention_amd as K
@@ -376,8 +441,7 @@ def main():
         log(f"device check failed: {K.kvq_status_string(st)}")
         sys.exit(1)
 
-    main_fmt = {"int8_32k": (K.KVQ_INT8_PTH, 0), "fp8_sink_4k": (K.KVQ_FP8_PTH, 0),
-                "nvfp4_16k": (K.KVQ_NVFP4, 0), "kvarn_16k": (K.KVQ_KVARN_K4V2_G128, 0)}[args.workload]
+
     pb = Problem(K, args.workload, *main_fmt)
     write_mtok, write_ms = pb.time_write()
     log(f"[bench] whole-context write: {write_mtok:.1f} Mtok/s ({write_ms:.3f} ms)")
@@ -409,17 +473,18 @@ def main():
         },
         "kv_bytes_per_step": pb.kv_bytes,
         "write_mtok_s": round(write_mtok, 2),
-        "write_gbs": round((2 * w.B * w.T * sp.Hkv * sp.D * 2 + pb.cache_bytes) / (write_ms * 1e-3) / 1e9, 2),
+        "write_gbs": round(write_bytes(pb) / (write_ms * 1e-3) / 1e9, 2),
+        "write_frac_of_peak": round(write_bytes(pb) / (write_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "write_traffic": measured_traffic(entry_key(K, args.workload, *main_fmt), "write"),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(entry_key(K, args.workload, *main_fmt)),
             # eight-wave workgroups when the plan runs a single split over
             # at least one (sequence, kv head) per compute unit (kvq.h)
-            "kernel": f"decode_kernel<{pb.fmt}, {sp.D}, {sp.Hq // sp.Hkv}, "
-                      f"{8 if pb.ws.num_splits == 1 and pb.fmt in (1, 2, 3) and w.B * sp.Hkv >= 256 else 4}>"
-                      + (" + append_merge_kernel" if pb.ws.num_splits > 1 else " after quant_write"),
+            "kernel": decode_kernel_name(pb),
             "algorithmic_bytes": pb.call_kv_bytes, "traffic_unit": "HBM bytes per decode call (rocprofv3 "
-            "FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB copy)",
+            "FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a 1 GiB device copy)",
             "mean_launch_us": round(ms_dec * 1e3, 2),
             **pb.dec_percentiles_us(),
         },
@@ -440,13 +505,17 @@ def main():
             if name == args.workload and fmt == main_fmt[0] and flags == main_fmt[1]:
                 continue
             p = Problem(K, name, fmt, flags)
-            wm, _ = p.time_write()
+            wm, wms = p.time_write()
             ms_s, ms_d = p.time_steps(max(20, args.steps // 2), args.warmup)
             key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "") + ("_tp2_share" if name.endswith("_tp2") else "")
             fmts[key] = {"workload": name, "decode_gbs": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9, 1),
                          "decode_frac_of_peak": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "decode_us": round(ms_d * 1e3, 2), **p.dec_percentiles_us(), "step_us": round(ms_s * 1e3, 2),
-                         "write_mtok_s": round(wm, 1), "splits": p.ws.num_splits,
+                         "write_mtok_s": round(wm, 1),
+                         "write_frac_of_peak": round(write_bytes(p) / (wms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(entry_key(K, name, fmt, flags)),
+                         "write_traffic": measured_traffic(entry_key(K, name, fmt, flags), "write"),
+                         "algorithmic_bytes": p.call_kv_bytes, "splits": p.ws.num_splits,
                          "step": ("append to the binary16 tail (tile quantised when complete) + decode over "
                                   "tiles and tail" if fmt == K.KVQ_KVARN_K4V2_G128
                                   else "write + decode in one kvq_decode_attention_append call")}

@@ -138,7 +138,11 @@ typedef struct {
 int64_t kvq_page_bytes(const kvq_layout* layout);
 
 /* KVQ_OK if HIP device `hip_device` is a gfx950 (MI355X), else KVQ_ERR_DEVICE
- * (also when no device is present).  Host-only, no kernel launched. */
+ * (also when no device is present).  Host-only, no kernel launched.  The
+ * load-time capability check of [P5] §需要记录的系统指标 (correctness list),
+ * so that an unsupported device fails at initialisation rather than at the
+ * first request (§Blackwell 支持不是一个单一布尔值: fail fast, never fall back
+ * silently).  Every launching entry point makes the same check. */
 kvq_status kvq_check_device(int hip_device);
 
 /* Quantise-on-write ([P5] §KV 的写入与读取路径, write path; [P4] §写和读).
@@ -213,7 +217,10 @@ kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void*
                             void* stream);
 
 /* Bytes of workspace kvq_decode_attention needs for this problem (-1 if
- * invalid, including num_q_heads not a multiple of H): one partial record of
+ * invalid, including num_q_heads not a multiple of H), the "workspace bytes"
+ * [P5] §需要记录的系统指标 asks to record (its §KV 的写入与读取路径 notes that
+ * a decode which first expands the cache into a temporary buffer changes the
+ * bandwidth and workspace cost; this one keeps only the split records): one partial record of
  * binary32 (max, sum, output row) per (sequence, kv head, context split), 0
  * when a single split is used (KVarN: always at least one record).
  * num_splits: 0 = let the library choose, else the number of context splits
@@ -232,7 +239,8 @@ int64_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t batch, int3
                                    int32_t max_pages_per_seq, int32_t num_splits);
 
 /* Number of context splits kvq_decode_attention will use (-1 if invalid).
- * Same arguments and rules as kvq_decode_workspace_bytes. */
+ * Same arguments and rules as kvq_decode_workspace_bytes; the split count
+ * fixes the workspace bytes above ([P5] §需要记录的系统指标). */
 int32_t kvq_decode_num_splits(const kvq_layout* layout, int32_t batch, int32_t num_q_heads,
                               int32_t max_pages_per_seq, int32_t num_splits);
 
@@ -309,20 +317,20 @@ kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const void* ca
  *   other arguments as for kvq_decode_attention (kvarn_tail excluded); the
  *   workspace is sized by kvq_decode_workspace_bytes with the same arguments.
  * The cache bytes written are exactly those of kvq_quantize_write(k_new,
- * v_new, slot_mapping, n_tok = batch).  Attention covers positions
- * 0 .. ctx-2 read from the cache plus the new token as position ctx-1, so
- * the output equals kvq_quantize_write followed by kvq_decode_attention
- * whenever each slot is that of position ctx-1 (other slots give the same
- * cache bytes but attend the new token at position ctx-1 all the same).  A
- * sequence whose slot is negative or outside the pool stores nothing and
- * attends its ctx cached tokens; ctx = 0 stores the token and gives a zero
- * row.  Two sequences must not share a slot, and no sequence's context may
- * cover another sequence's new slot (the split kernel reads the cache before
- * the new tokens are stored).
+ * v_new, slot_mapping, n_tok = batch).  Whatever the split plan, attention
+ * covers positions 0 .. ctx-2 read from the cache plus the new token as
+ * position ctx-1, so the output equals kvq_quantize_write followed by
+ * kvq_decode_attention whenever each slot is that of position ctx-1; a slot
+ * elsewhere receives the same bytes and the token is still attended as
+ * position ctx-1.  A sequence whose slot is negative or outside the pool
+ * stores nothing and attends its ctx cached tokens; ctx = 0 stores the token
+ * and gives a zero row.  Two sequences must not share a slot, and no new slot
+ * may lie among the positions 0 .. ctx-2 that any sequence reads (they are
+ * read while the new tokens are stored).
  * With a split context this is two launches, the split kernel (reading one
  * token less) and a merge kernel that also quantises, stores and attends the
- * new tokens, so no write launch precedes the split kernel.  With a single
- * split it is the write launch followed by the decode.
+ * new tokens.  With a single split it is one launch: the split kernel itself
+ * quantises, stores and attends them.  No write launch precedes either.
  * Errors: as kvq_decode_attention; KVQ_ERR_INVALID_ARG for a KVarN layout or
  * NULL k_new, v_new or slot_mapping with batch > 0. */
 kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, const void* k_new,
@@ -341,7 +349,9 @@ kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, co
 kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int64_t* slot_mapping,
                           int64_t n_tok, float* k_out, float* v_out, void* stream);
 
-/* Static English description of a status code. */
+/* Static English description of a status code: the explicit, named failure
+ * that [P5] §Blackwell 支持不是一个单一布尔值 asks for in place of a silent
+ * fallback.  Never NULL; unknown codes give "unknown status". */
 const char* kvq_status_string(kvq_status status);
 
 #ifdef __cplusplus

@@ -33,7 +33,7 @@
 // Splits: with more than one, each workgroup writes its partial (m, l, O) to
 // the workspace and a second, small kernel merges the partials of every
 // (sequence, kv head); a single split writes the output directly.
-#include "decode_common.h"
+#include "row_encode.h"
 
 namespace kvq {
 namespace {
@@ -360,6 +360,56 @@ __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, i
   }
 }
 
+// The step's new token of (sequence b, kv head) in a single-split call:
+// wave 0 quantises and stores the key row, wave 1 the value row, with the
+// write path's per-row encoders (so the bytes are kvq_quantize_write's).
+// When the token is attended, the dequantised key row goes through s_k and
+// wave 0's 64 lanes take its dot products with the G queries, leaving each
+// head's score in s_lg (log2 units, as the kernel's scores); wave 1 leaves
+// the value row (codes times the row scale; a per-tensor or global V scale
+// follows at the output) in s_v.
+template <int FMT, int D, int G>
+__device__ __forceinline__ void new_token_row(const DecodeArgs& a, int b, int kvh, int w, int lane, bool attend,
+                                              float* s_k, float* s_lg, float* s_v) {
+  constexpr bool K8 = !kNibble<FMT>;
+  constexpr int VPL = K8 ? 8 : 16;  // values per lane of the row encoders
+  constexpr int LPR = D / VPL;      // lanes per row
+  if (lane < LPR) {
+    const WriteArgs& wa = a.wnew;
+    RowCodes rc;
+    const int64_t row = (int64_t)w * wa.n_tok * wa.H + (int64_t)b * wa.H + kvh;
+    if constexpr (K8)
+      write_row_8bit<FMT, D>(wa, row, lane, true, &rc);
+    else
+      write_row_4bit<FMT, D>(wa, row, lane, true, &rc);
+    if (attend) {
+      float c[VPL];
+      lane_values<FMT, VPL>(rc, c);
+      const float rs = kPth<FMT> ? rc.s : 1.0f;
+      float* dst = w == 0 ? s_k : s_v;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) dst[VPL * lane + i] = c[i] * rs;
+    }
+  }
+  if (w != 0 || !attend) return;
+  // the wave's own LDS writes complete before its reads
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  constexpr int LPH = (64 / G) < (D / 2) ? (64 / G) : (D / 2);  // lanes per head
+  constexpr int VH = D / LPH;                                     // channels per lane
+  const int g = lane / LPH, ch = VH * (lane % LPH);
+  float part = 0.0f;
+  if (g < G) {
+    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + g) * D + ch;
+#pragma unroll
+    for (int i = 0; i < VH; ++i) part = __builtin_fmaf((float)__builtin_bit_cast(half_t, qp[i]), s_k[ch + i], part);
+  }
+#pragma unroll
+  for (int m = LPH / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+  const float kconst = (FMT == 1 || FMT == 4) ? a.k_scale * a.qk_scale : a.qk_scale;
+  if (g < G && lane % LPH == 0) s_lg[g] = part * kconst;
+}
+
 template <int FMT, int D, int G, int W>
 __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   constexpr int NK = D / 32;
@@ -384,11 +434,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   // wave-uniform bounds (kept in scalar registers)
   int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
+  bool attend_new = false;
   if (a.new_slots != nullptr) {
     // append-and-decode: the last position is the new token, attended by the
-    // merge kernel when its slot is in the pool
+    // merge kernel (several splits) or below (one split) when its slot is in
+    // the pool
     const int64_t ns = a.new_slots[b];
-    if (ctx >= 1 && ns >= 0 && ns < (int64_t)a.num_pages * P) ctx -= 1;
+    attend_new = ctx >= 1 && ns >= 0 && ns < (int64_t)a.num_pages * P;
+    if (attend_new) ctx -= 1;
   }
   const int n_pages = (ctx + P - 1) / P;
   const int p_begin = split * a.pages_per_split;
@@ -495,6 +548,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
     }
   }
 
+  // ---- a single split of a decode step: the new token (store and attend)
+  __shared__ float s_new_lg[kMaxGroup];
+  __shared__ float s_new_k[D], s_new_v[D];
+  const bool fold_new = S == 1 && a.new_slots != nullptr;
+  if (fold_new && w < 2) new_token_row<FMT, D, G>(a, b, kvh, w, l, attend_new, s_new_k, s_new_lg, s_new_v);
+
   // ---- combine the W waves (and the hi/lo rows) in LDS
   float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -529,6 +588,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
       }
     }
     if (S == 1) {
+      if (fold_new && attend_new) {
+        // the new token as one more partial: m = its score, l = 1, o = its value row
+        const float lg = s_new_lg[g];
+        const float mc = fmaxf(M, lg);
+        const float f = exp2f(lg - mc), sc = exp2f(M - mc);
+        L = L * sc + f;
+        O = O * sc + f * s_new_v[d];
+      }
       const float o = L > 0.0f ? O / L * post : 0.0f;
       a.out[((int64_t)b * a.Hq + kvh * G + g) * D + d] = __builtin_bit_cast(uint16_t, (half_t)o);
     } else {

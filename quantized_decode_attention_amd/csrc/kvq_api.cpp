@@ -429,14 +429,11 @@ kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, co
   DecodeArgs a = decode_args(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens, batch,
                              sm_scale, out, workspace, splits, pps, waves);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (splits == 1) {
-    // no merge launch to carry the new tokens: write, then decode
-    hipError_t e = launch_quant_write(layout->format, w, s);
-    if (e != hipSuccess) return from_hip(e);
-    return from_hip(launch_decode(layout->format, a, s));
-  }
   a.new_slots = slot_mapping;
+  a.wnew = w;
+  // one split: the split kernel itself writes and attends the new tokens
   hipError_t e = launch_decode(layout->format, a, s);
+  if (e != hipSuccess || splits == 1) return from_hip(e);
   if (e != hipSuccess) return from_hip(e);
   return from_hip(launch_append_merge(layout->format, w, a, s));
 }

@@ -47,8 +47,11 @@ struct DecodeArgs {
   int waves;     // wavefronts per split workgroup: 4, or 8 for single-split plans
   // Append-and-decode: slot of each sequence's new token (or null).  The
   // split kernel then reads positions 0 .. ctx-2 of a sequence whose new
-  // token is attended, and the merge is append_merge_kernel's.
+  // token is attended; with several splits the merge is append_merge_kernel's,
+  // with one the split kernel itself quantises, stores and attends the new
+  // tokens described by `wnew` (rows k_new / v_new [batch][H][D]).
   const int64_t* new_slots;
+  WriteArgs wnew;
 };
 
 // Workspace: one partial record (m[8], l[8], o[8][D]) per (sequence, kv head,

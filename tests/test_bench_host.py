@@ -53,10 +53,38 @@ def test_traffic_digest_ignores_comments_only():
     assert bench._code_only(code) != bench._code_only(code.replace("= 2", "= 3"))
 
 
-def test_traffic_only_for_the_headline_workload():
-    for name in ("fp8_sink_4k", "nvfp4_16k", "kvarn_16k"):
-        assert bench.measured_traffic(name) is None
-    got = bench.measured_traffic("int8_32k")
-    # null once the decode sources changed since the counters were taken,
-    # else bytes within a few percent of the algorithmic 553.6 MB
+def test_traffic_table_follows_the_digest(monkeypatch, tmp_path):
+    """Figures are read per `workload/format` entry, and only while the
+    summary's digest matches the kernels' sources."""
+    f = tmp_path / "traffic.md"
+    body = ("    traffic int8_32k/int8_per_token_head decode = 565181228\n"
+            "    traffic int8_32k/int8_per_token_head write = 1700000000\n"
+            "    traffic nvfp4_16k/nvfp4_4over6 decode = 310000000\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    f.write_text(body + f"    kernel_sources_sha256 = {bench.kernel_sources_digest()}\n")
+    assert bench.measured_traffic("int8_32k/int8_per_token_head") == 565181228
+    assert bench.measured_traffic("int8_32k/int8_per_token_head", "write") == 1700000000
+    assert bench.measured_traffic("nvfp4_16k/nvfp4_4over6") == 310000000
+    assert bench.measured_traffic("nvfp4_16k/nvfp4") is None
+    f.write_text(body + "    kernel_sources_sha256 = 0123\n")
+    assert bench.measured_traffic("int8_32k/int8_per_token_head") is None
+
+
+def test_committed_traffic_is_near_the_algorithmic_bytes():
+    # null once the kernel sources changed since the counters were taken,
+    # else within a few percent of the algorithmic 553.6 MB
+    got = bench.measured_traffic("int8_32k/int8_per_token_head")
     assert got is None or 553_648_128 <= got <= 1.1 * 553_648_128
+
+
+def test_format_choice():
+    assert bench.main_format("int8_32k") == (2, 0)
+    assert bench.main_format("nvfp4_16k", "nvfp4_4over6") == (4, 1)
+    assert bench.main_format("nvfp4_16k", "mxfp4") == (7, 0)
+    assert bench.main_format("kvarn_16k_tp2") == (5, 0)
+    assert bench.main_format("int8_32k", "kvarn_k4v2_g128") is None
+    assert bench.main_format("kvarn_16k", "nvfp4") is None
+    assert bench.main_format("int8_32k", "int2") is None
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "kvarn_16k", "--format",
+                        "int8_per_token_head"], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2 and r.stdout == ""

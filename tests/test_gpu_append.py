@@ -78,3 +78,44 @@ def test_append_decode_matches_oracle(K, O, fmt, flags, D, P, G):
         got2, _ = gpu_decode(K, lay, cache2, q16, bt, ctx, sm, num_splits=splits)
         assert_attn_close(got2, got, f"splits={splits}: write + decode vs one call")
 
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("fmt,flags", [(2, 0), (3, 0), (4, 1), (6, 0)], ids=["int8pth", "fp8pth", "nvfp4_4over6",
+                                                                          "int4pth"])
+def test_append_slot_elsewhere(K, O, fmt, flags, splits):
+    """A new token whose slot is not position ctx-1's (here: on a page no
+    sequence reads) is stored at that slot and still attended as position
+    ctx-1, with one split (the split kernel attends it) and with several (the
+    merge does)."""
+    import torch
+    rng = np.random.default_rng(950 + 10 * fmt + flags + splits)
+    B, H, G, D, P = 3, 2, 8, 128, 16
+    ctx = np.array([100, 37, 64], np.int32)
+    bt, num_pages, slots_old, slots_new = step_problem(rng, B, H, G, D, P, ctx, set())
+    free = np.setdiff1d(np.arange(num_pages), bt.ravel())
+    assert free.size >= 2
+    at_ctx = slots_new.copy()           # position ctx-1's slots
+    slots_new[1] = int(free[-1]) * P + 5  # sequence 1 writes elsewhere
+    k_old = workloads.random_halves(rng, (slots_old.size, H, D))
+    v_old = workloads.random_halves(rng, (slots_old.size, H, D))
+    k_new = workloads.random_halves(rng, (B, H, D))
+    v_new = workloads.random_halves(rng, (B, H, D))
+    lay = layout_for(K, fmt, flags, H, D, P, num_pages, np.concatenate([k_old, k_new]),
+                     np.concatenate([v_old, v_new]))
+    before = O.quantize_write(olayout(lay), k_old, v_old, slots_old)
+    after = O.quantize_write(olayout(lay), k_new, v_new, slots_new, cache=before.copy())
+    attended = O.quantize_write(olayout(lay), k_new, v_new, at_ctx, cache=before.copy())
+    q16 = workloads.random_halves(rng, (B, H * G, D))
+    sm = 1.0 / math.sqrt(D)
+    ref = O.decode_attention(olayout(lay), attended, q16, bt, ctx, sm)
+    log(f"append, slot elsewhere: fmt={fmt} flags={flags} splits={splits}")
+    ws = K.DecodeWorkspace(lay, B, H * G, bt.shape[1], splits)
+    assert ws.num_splits == splits
+    cache = dev(before)
+    out = torch.empty((B, H * G, D), dtype=torch.float16, device="cuda")
+    K.kvq_decode_attention_append(lay, cache, dev(k_new), dev(v_new), dev(slots_new), dev(q16), dev(bt), dev(ctx),
+                                  sm, out, ws.buffer, splits)
+    torch.cuda.synchronize()
+    assert first_mismatch(cache.cpu().numpy(), after) is None
+    assert_attn_close(out.cpu().numpy().astype(np.float64), ref, f"splits={splits}")
