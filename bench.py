@@ -24,6 +24,10 @@ Also reported on the same line:
                  steps carry only the pair around all of them) against 8 TB/s
   copy           a 1 GiB device-to-device copy (read + write bytes / time):
                  the achievable bandwidth beside the specification
+  roofline.access_pattern_floor, formats.*.read_floor_gbs
+                 the decode's own pages read whole with no arithmetic
+                 (libkvq_probe.so, a measurement helper outside libkvq): the
+                 access pattern's ceiling
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
   formats        the other formats' workloads (decode GB/s, write Mtok/s), and
                  one GPU's share of the 16K workloads under two-way tensor
@@ -213,10 +217,67 @@ class Problem:
         self.dec_ms = sorted(a.elapsed_time(b) for a, b in ev)
         return total / steps, sum(self.dec_ms) / len(self.dec_ms)
 
+    def time_read_floor(self, reps=20):
+        """The decode's access pattern with no arithmetic (libkvq_probe.so):
+        every (page, kv head) chunk of the cache read whole, split as the
+        decode splits it, over the same rotated cache copies.  Returns GB/s of
+        cache bytes read per launch (the decode's algorithmic bytes)."""
+        import ctypes
+
+        import torch
+        L = read_probe_lib()
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        chunk = self.page_bytes // self.sp.Hkv
+        if self.kvarn:
+            chunk = chunk // (self.sp.P // 128)  # one 128-token tile per unit of the walk
+        splits = max(1, self.ws.num_splits)
+        # the decode's eight-wave single-split plan (see decode_kernel_name)
+        waves = 8 if splits == 1 and self.fmt in (1, 2, 3) and self.w.B * self.sp.Hkv >= 256 else 4
+
+        def go(i):
+            rc = L.kvq_probe_read_pattern(ctypes.c_void_p(self.caches[i % len(self.caches)].data_ptr()),
+                                          ctypes.c_void_p(self.bt.data_ptr()), self.w.B, self.sp.Hkv,
+                                          self.w.block_tables.shape[1], chunk, self.w.num_pages, splits, waves,
+                                          ctypes.c_void_p(sink.data_ptr()), stream)
+            assert rc == 0, rc
+        for i in range(3):
+            go(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            go(i)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        nbytes = self.w.B * (self.w.T // self.sp.P) * self.page_bytes
+        return nbytes / (ms * 1e-3) / 1e9, ms * 1e3
+
     def dec_percentiles_us(self):
         d = self.dec_ms
         pick = lambda f: round(d[min(len(d) - 1, int(f * len(d)))] * 1e3, 2)
         return {"p10_us": pick(0.1), "p50_us": pick(0.5), "p90_us": pick(0.9)}
+
+
+_READ_PROBE = None
+
+
+def read_probe_lib():
+    """libkvq_probe.so: the benchmark's access-pattern read helper (built with
+    the library; not part of libkvq)."""
+    global _READ_PROBE
+    if _READ_PROBE is None:
+        import ctypes
+        path = os.path.join(ROOT, "quantized_decode_attention_amd", "libkvq_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python quantized_decode_attention_amd/_build.py`")
+        L = ctypes.CDLL(path)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.kvq_probe_read_pattern.restype = I
+        L.kvq_probe_read_pattern.argtypes = [P, P, I, I, I, I, I, I, I, P, P]
+        _READ_PROBE = L
+    return _READ_PROBE
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=10):
@@ -446,6 +507,8 @@ def main():
     write_mtok, write_ms = pb.time_write()
     log(f"[bench] whole-context write: {write_mtok:.1f} Mtok/s ({write_ms:.3f} ms)")
     ms_step, ms_dec = pb.time_steps(args.steps, args.warmup)
+    floor_gbs, floor_us = pb.time_read_floor()
+    log(f"[bench] access-pattern read floor: {floor_us:.1f} us ({floor_gbs:.0f} GB/s)")
     value = pb.kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = pb.call_kv_bytes / (ms_dec * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.1f} us ({value:.0f} GB/s), decode launch {ms_dec * 1e3:.1f} us "
@@ -487,6 +550,10 @@ def main():
             "FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a 1 GiB device copy)",
             "mean_launch_us": round(ms_dec * 1e3, 2),
             **pb.dec_percentiles_us(),
+            # the same pages read whole with no arithmetic (libkvq_probe.so):
+            # the access pattern's own ceiling beside the 8 TB/s specification
+            "access_pattern_floor": {"gbs": round(floor_gbs, 1), "us": round(floor_us, 2),
+                                     "frac_of_peak": round(floor_gbs / HBM_PEAK_GBS, 4)},
         },
     }
     del pb
@@ -507,6 +574,7 @@ def main():
             p = Problem(K, name, fmt, flags)
             wm, wms = p.time_write()
             ms_s, ms_d = p.time_steps(max(20, args.steps // 2), args.warmup)
+            fl_gbs, _ = p.time_read_floor()
             key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "") + ("_tp2_share" if name.endswith("_tp2") else "")
             fmts[key] = {"workload": name, "decode_gbs": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9, 1),
                          "decode_frac_of_peak": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -516,6 +584,7 @@ def main():
                          "traffic": measured_traffic(entry_key(K, name, fmt, flags)),
                          "write_traffic": measured_traffic(entry_key(K, name, fmt, flags), "write"),
                          "algorithmic_bytes": p.call_kv_bytes, "splits": p.ws.num_splits,
+                         "read_floor_gbs": round(fl_gbs, 1),
                          "step": ("append to the binary16 tail (tile quantised when complete) + decode over "
                                   "tiles and tail" if fmt == K.KVQ_KVARN_K4V2_G128
                                   else "write + decode in one kvq_decode_attention_append call")}

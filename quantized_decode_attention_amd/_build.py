@@ -74,6 +74,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+READ_PROBE_SRC = os.path.join(CSRC, "read_probe.hip")
+READ_PROBE_LIB = os.path.join(PKG, "libkvq_probe.so")
+
+
+def build_read_probe() -> str:
+    """The benchmark's measurement helper (libkvq_probe.so, not part of
+    libkvq): the decode's access pattern with no arithmetic."""
+    tmp = READ_PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *COMMON, "-shared", READ_PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the read probe failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, READ_PROBE_LIB)
+    return READ_PROBE_LIB
+
+
 PROBE_SRC = os.path.join(ROOT, "tests", "gpu_probes", "probes.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "gpu_probes", "libkvq_probes.so")
 
@@ -91,4 +107,5 @@ def build_probes() -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_read_probe()
     build_probes()

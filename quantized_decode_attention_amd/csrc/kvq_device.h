@@ -20,6 +20,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Correctly rounded division by a value shared by many numerators.
@@ -189,6 +190,17 @@ __device__ __forceinline__ void e2m1x8_to_h_scaled4(uint32_t w, const float (&s)
       "s_nop 1"
       : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
       : "v"(w), "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]));
+}
+
+// Eight E2M1 codes of w (low nibble of byte 0 first) -> binary32 values,
+// exact (gfx950's scaled conversion at scale 1, one byte per instruction;
+// checked code by code in tests/test_gpu_probes.py).
+__device__ __forceinline__ void e2m1x8_to_f32(uint32_t w, float (&v)[8]) {
+  const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const float2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const float2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  v[0] = a.x, v[1] = a.y, v[2] = b.x, v[3] = b.y, v[4] = c.x, v[5] = c.y, v[6] = d.x, v[7] = d.y;
 }
 
 // E8M0 byte e -> 2^(e - 127) as a binary32 scale operand (e = 0 gives +0,

@@ -219,17 +219,12 @@ __device__ __forceinline__ float nvfp4_block(const float* x, float st, uint32_t 
     if constexpr (!ERR) return 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint32_t v[4];
-      e2m1x8_to_h(w[h], v);  // values 8h .. 8h+7 in order
+      float v[8];
+      e2m1x8_to_f32(w[h], v);  // values 8h .. 8h+7 in order
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const half2_t pr = as_h2(v[k]);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int i = 8 * h + 2 * k + e;
-          const float err = x[i] - d * (float)pr[e];
-          e2[i] = err * err;
-        }
+      for (int k = 0; k < 8; ++k) {
+        const float err = x[8 * h + k] - d * v[k];
+        e2[8 * h + k] = err * err;
       }
     }
   }

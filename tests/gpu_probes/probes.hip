@@ -110,7 +110,27 @@ __global__ void k_cvt_fp8_f16_scaled(const uint32_t* src, int n, float scale, ui
   out[2 * (int64_t)i + 1] = hi;
 }
 
+// Words of E2M1 codes -> binary32 with the scaled conversion at scale 1,
+// one byte per instruction (byte-select operands 0..3), eight values per word.
+typedef float float2_v __attribute__((ext_vector_type(2)));
+__global__ void k_cvt_fp4_f32_bytes(const uint32_t* src, int n, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = src[i];
+  const float2_v a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const float2_v b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const float2_v c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const float2_v d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  float* o = out + 8 * (int64_t)i;
+  o[0] = a.x, o[1] = a.y, o[2] = b.x, o[3] = b.y, o[4] = c.x, o[5] = c.y, o[6] = d.x, o[7] = d.y;
+}
+
 extern "C" {
+int probe_cvt_fp4_f32_bytes(const uint32_t* src, int n, float* out) {
+  if (n <= 0) return 0;
+  k_cvt_fp4_f32_bytes<<<(n + 255) / 256, 256>>>(src, n, out);
+  return (int)hipGetLastError();
+}
 int probe_cvt_fp8_f16_scaled(const uint32_t* src, int n, float scale, uint32_t* out) {
   if (n <= 0) return 0;
   k_cvt_fp8_f16_scaled<<<(n + 255) / 256, 256>>>(src, n, scale, out);

@@ -248,3 +248,24 @@ def test_cvt_e4m3_nibbles_to_f16_integers(PL):
     got = out.cpu().numpy().view(np.float16).astype(np.float64).reshape(words.size, 4)
     want = np.stack([(words >> (8 * k)) & 0xFF for k in range(4)], axis=1).astype(np.float64)
     assert np.array_equal(got, want)
+
+
+def test_cvt_e2m1_to_f32_every_code_and_byte(PL, O):
+    """The scaled E2M1 -> binary32 conversion at scale 1 (used for NVFP4's
+    4over6 reconstruction error) returns the exact grid value of every code
+    from every byte position of a word (the sign of a zero is not compared:
+    it cannot change x - d * v or its square)."""
+    import torch
+    rng = np.random.default_rng(5)
+    words = _all_byte_positions(rng)
+    wd = torch.from_numpy(words.view(np.int32)).cuda()
+    out = torch.zeros(words.size * 8, dtype=torch.float32, device="cuda")
+    log("probe cvt e2m1 -> f32, byte selects")
+    assert PL.probe_cvt_fp4_f32_bytes(_ptr(wd), words.size, _ptr(out)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1, 8)
+    for i, w in enumerate(words):
+        for j in range(8):
+            code = (int(w) >> (4 * j)) & 15
+            ref = np.float32(O.e2m1_decode(code))
+            assert got[i, j] == ref, (hex(int(w)), j, got[i, j], ref)
