@@ -4,9 +4,9 @@
 A step is one decode step of the workload: quantise-write the new token of
 every sequence and run dequant-fused paged decode attention over the whole
 context, new token included, in one call (kvq_decode_attention_append: the
-split kernel, then a merge kernel that also quantises, stores and attends the
-new tokens; KVarN steps append through kvq_kvarn_append and then call
-kvq_decode_attention).  The headline
+split kernel, whose split-0 workgroups also quantise, store and attend the new
+tokens, then the merge kernel when the context is split; KVarN steps append
+through kvq_kvarn_append and then call kvq_decode_attention).  The headline
 workload is INT8 per-token-head at 32K context (B=8, 64 q / 8 kv heads,
 D=128, page 16): `value` is quantised-KV bytes read per second over the timed
 steps.  Inputs are resident in HBM before timing starts; the cache is rotated
@@ -15,8 +15,8 @@ pages.
 
 Also reported on the same line:
   write_mtok_s   whole-context quantise-on-write throughput (tokens/s / 1e6)
-  roofline       the step's decode call (split kernel, plus the merge kernel
-                 that writes and attends the new tokens): algorithmic KV bytes
+  roofline       the step's decode call (split kernel, which also writes and
+                 attends the new tokens, plus the merge): algorithmic KV bytes
                  per call / mean call duration (HIP events around each call, on the launch
                  stream, over an instrumented pass of as many steps right
                  after the timed ones: an event recorded between two launches
@@ -456,7 +456,7 @@ def decode_kernel_name(p):
     # one (sequence, kv head) per compute unit (kvq.h)
     waves = 8 if p.ws.num_splits == 1 and p.fmt in (1, 2, 3) and p.w.B * p.sp.Hkv >= 256 else 4
     return (f"decode_kernel<{p.fmt}, {p.sp.D}, {G}, {waves}>"
-            + (" + append_merge_kernel" if p.ws.num_splits > 1 else " after quant_write"))
+            + (" + decode_merge_kernel" if p.ws.num_splits > 1 else ""))
 
 
 def write_bytes(p):

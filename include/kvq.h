@@ -327,10 +327,11 @@ kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const void* ca
  * and gives a zero row.  Two sequences must not share a slot, and no new slot
  * may lie among the positions 0 .. ctx-2 that any sequence reads (they are
  * read while the new tokens are stored).
- * With a split context this is two launches, the split kernel (reading one
- * token less) and a merge kernel that also quantises, stores and attends the
- * new tokens.  With a single split it is one launch: the split kernel itself
- * quantises, stores and attends them.  No write launch precedes either.
+ * The split kernel reads one token less; its first context split of each
+ * (sequence, kv head) also quantises and stores the new token and attends it
+ * as one more partial.  With a single split that is the whole step, one
+ * launch; with a split context the merge kernel of kvq_decode_attention
+ * follows.  No write launch precedes either.
  * Errors: as kvq_decode_attention; KVQ_ERR_INVALID_ARG for a KVarN layout or
  * NULL k_new, v_new or slot_mapping with batch > 0. */
 kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, const void* k_new,

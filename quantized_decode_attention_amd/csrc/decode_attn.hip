@@ -32,7 +32,11 @@
 //
 // Splits: with more than one, each workgroup writes its partial (m, l, O) to
 // the workspace and a second, small kernel merges the partials of every
-// (sequence, kv head); a single split writes the output directly.
+// (sequence, kv head); a single split writes the output directly.  In a
+// decode step (kvq_decode_attention_append) the split-0 workgroup of each
+// (sequence, kv head) also quantises and stores the new token and folds it
+// into its own partial: the step is the split kernel, plus the merge when
+// there are several splits.
 #include "row_encode.h"
 
 namespace kvq {
@@ -436,9 +440,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
   bool attend_new = false;
   if (a.new_slots != nullptr) {
-    // append-and-decode: the last position is the new token, attended by the
-    // merge kernel (several splits) or below (one split) when its slot is in
-    // the pool
+    // append-and-decode: the last position is the new token, attended by
+    // the split-0 workgroup below when its slot is in the pool
     const int64_t ns = a.new_slots[b];
     attend_new = ctx >= 1 && ns >= 0 && ns < (int64_t)a.num_pages * P;
     if (attend_new) ctx -= 1;
@@ -548,10 +551,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- a single split of a decode step: the new token (store and attend)
+  // ---- a decode step's new token: split 0 stores it and folds it into its
+  // own partial
   __shared__ float s_new_lg[kMaxGroup];
   __shared__ float s_new_k[D], s_new_v[D];
-  const bool fold_new = S == 1 && a.new_slots != nullptr;
+  const bool fold_new = split == 0 && a.new_slots != nullptr;
   if (fold_new && w < 2) new_token_row<FMT, D, G>(a, b, kvh, w, l, attend_new, s_new_k, s_new_lg, s_new_v);
 
   // ---- combine the W waves (and the hi/lo rows) in LDS
@@ -587,15 +591,16 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
         O += f * o;
       }
     }
+    if (fold_new && attend_new) {
+      // the new token as one more partial: m = its score, l = 1, o = its value row
+      const float lg = s_new_lg[g];
+      const float mc = fmaxf(M, lg);
+      const float f = exp2f(lg - mc), sc = exp2f(M - mc);
+      M = mc;
+      L = L * sc + f;
+      O = O * sc + f * s_new_v[d];
+    }
     if (S == 1) {
-      if (fold_new && attend_new) {
-        // the new token as one more partial: m = its score, l = 1, o = its value row
-        const float lg = s_new_lg[g];
-        const float mc = fmaxf(M, lg);
-        const float f = exp2f(lg - mc), sc = exp2f(M - mc);
-        L = L * sc + f;
-        O = O * sc + f * s_new_v[d];
-      }
       const float o = L > 0.0f ? O / L * post : 0.0f;
       a.out[((int64_t)b * a.Hq + kvh * G + g) * D + d] = __builtin_bit_cast(uint16_t, (half_t)o);
     } else {
@@ -611,9 +616,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
 // Merge of the context splits: m = max m_s, l = sum 2^(m_s - m) l_s,
 // o = sum 2^(m_s - m) o_s / l.  A separate launch: the kernel boundary makes
 // every split's partial visible on all XCDs without device-wide cache
-// maintenance inside the split kernel.  One thread per output element; every
-// split's (m, l, o) is requested before any is used, 8 splits at a time, so
-// the merge costs one memory round trip per 8 splits.
+// maintenance inside the split kernel (a count-and-merge by the split
+// kernel's last workgroup measured slower than this launch: a device-scope
+// release writes back the XCD's whole L2, and even with write-through record
+// stores each workgroup waits for its stores and its count).  One thread per
+// output element; every split's (m, l, o) is requested before any is used,
+// 8 splits at a time, so the merge costs one memory round trip per 8 splits.
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int D, float post) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)a.B * a.Hq * D) return;
@@ -719,7 +727,7 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s) {
     case 6: e = launch_fmt<6>(a, s); break;
     case 7: e = launch_fmt<7>(a, s); break;
   }
-  if (e != hipSuccess || a.num_splits == 1 || a.new_slots != nullptr) return e;
+  if (e != hipSuccess || a.num_splits == 1) return e;
   const float post = (fmt == 1 || fmt == 4) ? a.v_scale : 1.0f;
   const int64_t outs = (int64_t)a.B * a.Hq * a.D;
   decode_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, s>>>(a, a.D, post);

@@ -431,11 +431,7 @@ kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   a.new_slots = slot_mapping;
   a.wnew = w;
-  // one split: the split kernel itself writes and attends the new tokens
-  hipError_t e = launch_decode(layout->format, a, s);
-  if (e != hipSuccess || splits == 1) return from_hip(e);
-  if (e != hipSuccess) return from_hip(e);
-  return from_hip(launch_append_merge(layout->format, w, a, s));
+  return from_hip(launch_decode(layout->format, a, s));
 }
 
 kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int64_t* slot_mapping,

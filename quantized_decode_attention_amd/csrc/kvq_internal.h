@@ -47,9 +47,9 @@ struct DecodeArgs {
   int waves;     // wavefronts per split workgroup: 4, or 8 for single-split plans
   // Append-and-decode: slot of each sequence's new token (or null).  The
   // split kernel then reads positions 0 .. ctx-2 of a sequence whose new
-  // token is attended; with several splits the merge is append_merge_kernel's,
-  // with one the split kernel itself quantises, stores and attends the new
-  // tokens described by `wnew` (rows k_new / v_new [batch][H][D]).
+  // token is attended, and its split-0 workgroup quantises, stores and
+  // attends the new token described by `wnew` (rows k_new / v_new
+  // [batch][H][D]), folding it into its own partial.
   const int64_t* new_slots;
   WriteArgs wnew;
 };
@@ -83,7 +83,6 @@ hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s);
 hipError_t launch_kvarn_append(const KvarnAppendArgs& a, hipStream_t s);
 hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s);
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s);
-hipError_t launch_append_merge(int fmt, const WriteArgs& w, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s);
 

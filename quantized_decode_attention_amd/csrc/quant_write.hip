@@ -222,124 +222,6 @@ __global__ __launch_bounds__(kBlock) void quant_write_4bit(WriteArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// A decode step's new tokens, quantised and attended in the merge of the
-// context splits (kvq_decode_attention_append).  The split kernel has read
-// positions 0 .. ctx-2 of each sequence from the cache.  This kernel
-// quantises the new token of every (sequence, kv head) with the per-row write
-// path above, stores it into its slot, and adds it to each head's merge as
-// one more partial: m = its score, l = 1, o = its dequantised value row.  The
-// step then has no separate write launch ahead of the split kernel.
-// ---------------------------------------------------------------------------
-
-// Grid (ceil(G / HPW), H, B): workgroup x serves heads HPW*x .. of the kv
-// head, one thread per output value.  Every workgroup quantises the new key
-// and value rows (wave 0 and wave 1, D/8 or D/16 lanes); only x == 0 stores
-// them.
-template <int FMT, int D>
-__global__ __launch_bounds__(256) void append_merge_kernel(WriteArgs wa, DecodeArgs a, float post) {
-  constexpr bool K8 = FMT == 1 || FMT == 2 || FMT == 3;
-  constexpr int VPL = K8 ? 8 : 16;  // values per lane
-  constexpr int LPR = D / VPL;      // lanes per row
-  constexpr int HPW = 256 / D;      // heads per workgroup
-  constexpr bool PTH = FMT == 2 || FMT == 3 || FMT == 6;
-  __shared__ float s_v[D];
-  __shared__ float s_lg[HPW];
-
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = a.G, S = a.num_splits;
-  const int g0 = blockIdx.x * HPW;
-  const int g = g0 + tid / D, d = tid % D;
-  const bool has_out = g < G;
-
-  int ctx = a.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
-  const int64_t slot = wa.slots[b];
-  const bool attend = ctx >= 1 && slot >= 0 && slot < (int64_t)wa.num_pages * wa.P;
-
-  // the splits' records are requested first, so their round trip overlaps
-  // the quantisation
-  const int64_t rf = ws_record_floats(D);
-  const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
-  const int gr = has_out ? g : g0;
-  RecGroup r0;
-  load_recs(recs, rf, S, 0, gr, 2 * kMaxGroup + gr * D + d, r0);
-
-  if (wv < 2 && lane < LPR) {
-    float qv[HPW][VPL];
-    if (wv == 0) {
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) {
-        const int gh = g0 + h < G ? g0 + h : g0;
-        const uint16_t* qp = a.q + ((int64_t)b * a.Hq + kvh * G + gh) * D + VPL * lane;
-#pragma unroll
-        for (int k = 0; k < VPL / 8; ++k) halves8_to_f32(*reinterpret_cast<const uint4*>(qp + 8 * k), qv[h] + 8 * k);
-      }
-    }
-    RowCodes rc;
-    const int64_t row = (int64_t)wv * wa.n_tok * wa.H + (int64_t)b * wa.H + kvh;
-    if constexpr (K8)
-      write_row_8bit<FMT, D>(wa, row, lane, blockIdx.x == 0, &rc);
-    else
-      write_row_4bit<FMT, D>(wa, row, lane, blockIdx.x == 0, &rc);
-    if (attend) {
-      float c[VPL];
-      lane_values<FMT, VPL>(rc, c);
-      const float rs = PTH ? rc.s : 1.0f;
-      if (wv == 0) {
-        const float kconst = (FMT == 1 || FMT == 4) ? a.k_scale * a.qk_scale : a.qk_scale;
-#pragma unroll
-        for (int h = 0; h < HPW; ++h) {
-          float part = 0.0f;
-#pragma unroll
-          for (int i = 0; i < VPL; ++i) part = __builtin_fmaf(qv[h][i], c[i], part);
-          part = group_sum<LPR>(part);
-          if (lane == 0) s_lg[h] = part * (rs * kconst);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) s_v[VPL * lane + i] = c[i] * rs;
-      }
-    }
-  }
-  __syncthreads();
-  if (!has_out) return;
-
-  float M = kNegInf, L = 0.0f, O = 0.0f;
-  merge_recs(r0, M, L, O);
-  for (int s0 = 8; s0 < S; s0 += 8) {
-    RecGroup r;
-    load_recs(recs, rf, S, s0, g, 2 * kMaxGroup + g * D + d, r);
-    merge_recs(r, M, L, O);
-  }
-  if (attend) {
-    const float lg = s_lg[g - g0];
-    const float mc = fmaxf(M, lg);
-    const float f = exp2f(lg - mc);
-    const float sc = exp2f(M - mc);
-    L = L * sc + f;
-    O = O * sc + f * s_v[d];
-  }
-  const float o = L > 0.0f ? O / L * post : 0.0f;
-  a.out[((int64_t)b * a.Hq + kvh * G + g) * D + d] = __builtin_bit_cast(uint16_t, (half_t)o);
-}
-
-template <int FMT>
-hipError_t launch_append_merge_fmt(const WriteArgs& w, const DecodeArgs& a, hipStream_t s) {
-  const float post = (FMT == 1 || FMT == 4) ? a.v_scale : 1.0f;
-  const int hpw = 256 / a.D;
-  const dim3 grid((unsigned)((a.G + hpw - 1) / hpw), (unsigned)a.H, (unsigned)a.B);
-  switch (a.D) {
-    case 32: append_merge_kernel<FMT, 32><<<grid, 256, 0, s>>>(w, a, post); break;
-    case 64: append_merge_kernel<FMT, 64><<<grid, 256, 0, s>>>(w, a, post); break;
-    case 128: append_merge_kernel<FMT, 128><<<grid, 256, 0, s>>>(w, a, post); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 template <int FMT>
 hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
   if (a.n_tok == 0) return hipSuccess;
@@ -366,18 +248,6 @@ hipError_t launch_fmt(const WriteArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_append_merge(int fmt, const WriteArgs& w, const DecodeArgs& a, hipStream_t s) {
-  if (a.B == 0) return hipSuccess;
-  switch (fmt) {
-    case 1: return launch_append_merge_fmt<1>(w, a, s);
-    case 2: return launch_append_merge_fmt<2>(w, a, s);
-    case 3: return launch_append_merge_fmt<3>(w, a, s);
-    case 4: return launch_append_merge_fmt<4>(w, a, s);
-    case 6: return launch_append_merge_fmt<6>(w, a, s);
-    case 7: return launch_append_merge_fmt<7>(w, a, s);
-  }
-  return hipErrorInvalidValue;
-}
 
 hipError_t launch_quant_write(int fmt, const WriteArgs& a, hipStream_t s) {
   switch (fmt) {

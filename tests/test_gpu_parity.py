@@ -226,6 +226,37 @@ def test_workspace_reuse_many_calls(K, O):
         assert_attn_close(out.cpu().numpy().astype(np.float64), ref[:nb], f"call {it}")
 
 
+@pytest.mark.parametrize("splits", [16, 64])
+def test_split_records_are_fresh_each_call(K, O, splits):
+    """Back-to-back calls in one stream on one workspace, alternating two
+    query sets: the merge must read the records of its own call, written on
+    other XCDs a moment before, never those the previous call left in the
+    same place."""
+    import torch
+    rng = np.random.default_rng(2200 + splits)
+    B, H, G, D, P = 8, 4, 8, 128, 16
+    ctx = rng.integers(1500, 2049, B).astype(np.int32)
+    ctx[0] = 2048  # 128 pages: 16 or 64 splits of whole pages
+    bt, num_pages, slots = paged_problem(rng, B, H, G, D, P, ctx)
+    k16 = workloads.random_halves(rng, (slots.size, H, D))
+    v16 = workloads.random_halves(rng, (slots.size, H, D))
+    lay = K.layout(2, H, D, P, num_pages)
+    cache = O.quantize_write(olayout(lay), k16, v16, slots)
+    qs = [workloads.random_halves(rng, (B, H * G, D)) * 2.0 for _ in range(2)]
+    refs = [O.decode_attention(olayout(lay), cache, q, bt, ctx, 0.09) for q in qs]
+    ws = K.DecodeWorkspace(lay, B, H * G, bt.shape[1], splits)
+    assert ws.num_splits == splits
+    cdev, btd, ctxd = dev(cache), dev(bt), dev(ctx)
+    qd = [dev(q) for q in qs]
+    outs = [torch.empty((B, H * G, D), dtype=torch.float16, device="cuda") for _ in range(8)]
+    for i, out in enumerate(outs):
+        K.kvq_decode_attention(lay, cdev, qd[i % 2], btd, ctxd, 0.09, out, ws.buffer, None, splits)
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        assert_attn_close(out.cpu().numpy().astype(np.float64), refs[i % 2], f"call {i}")
+    assert not np.array_equal(outs[0].cpu().numpy(), outs[1].cpu().numpy())
+
+
 @pytest.mark.parametrize("fmt,flags", [(2, 0), (4, 1), (6, 0), (7, 0)], ids=["int8pth", "nvfp4_4over6", "int4pth", "mxfp4"])
 def test_decode_long_splits_and_limits(K, O, fmt, flags):
     """One split walking more than 256 pages (several block-table chunks in
