@@ -127,38 +127,35 @@ class Problem:
         tail_bytes = (ctx % P) * sp.Hkv * 2 * sp.D * 2
         self.step_kv_bytes = w.B * (tile_bytes + tail_bytes)  # per step: pages + binary16 tail
         self.n_inc = n_steps
-        self.step_no = 0
 
-    def append(self, i):
-        c = self.caches[i % len(self.caches)]
+    def prepare_calls(self, n):
+        """The library calls of steps 0 .. n-1 with their arguments marshalled
+        now, so a timed step costs one C call per entry point on the host.
+        Step i uses cache copy i % copies (and, for KVarN, the i-th appended
+        token and context length)."""
+        K, nc = self.K, len(self.caches)
         if self.kvarn:
-            j = self.step_no
-            self.K.kvq_kvarn_append(self.lay, self.k_steps[j], self.v_steps[j], self.seq, self.pos_steps[j],
-                                    self.tails[i % len(self.caches)], self.bt, c)
-            return
-        self.K.kvq_quantize_write(self.lay, self.k_new, self.v_new, self.slots_new, c)
+            self.append_calls = [K.prepare_kvarn_append(self.lay, self.k_steps[i], self.v_steps[i], self.seq,
+                                                        self.pos_steps[i], self.tails[i % nc], self.bt,
+                                                        self.caches[i % nc]) for i in range(n)]
+            self.decode_calls = [K.prepare_decode_attention(self.lay, self.caches[i % nc], self.q, self.bt,
+                                                            self.ctx_steps[i], self.sm, self.out, self.ws.buffer,
+                                                            self.tails[i % nc]) for i in range(n)]
+        else:
+            calls = [K.prepare_decode_attention_append(self.lay, c, self.k_new, self.v_new, self.slots_new, self.q,
+                                                       self.bt, self.ctx, self.sm, self.out, self.ws.buffer)
+                     for c in self.caches]
+            self.step_calls = [calls[i % nc] for i in range(n)]
 
     def step(self, i):
         """One decode step: KVarN appends through its binary16 tail and then
         decodes (two calls); the other formats quantise-write the new tokens
         and decode in one call (kvq_decode_attention_append)."""
         if self.kvarn:
-            self.append(i)
-            self.decode(i)
-            return
-        self.K.kvq_decode_attention_append(self.lay, self.caches[i % len(self.caches)], self.k_new, self.v_new,
-                                           self.slots_new, self.q, self.bt, self.ctx, self.sm, self.out,
-                                           self.ws.buffer)
-
-    def decode(self, i):
-        c = self.caches[i % len(self.caches)]
-        if self.kvarn:
-            j = self.step_no
-            self.K.kvq_decode_attention(self.lay, c, self.q, self.bt, self.ctx_steps[j], self.sm, self.out,
-                                        self.ws.buffer, self.tails[i % len(self.caches)])
-            self.step_no += 1
-            return
-        self.K.kvq_decode_attention(self.lay, c, self.q, self.bt, self.ctx, self.sm, self.out, self.ws.buffer)
+            self.append_calls[i]()
+            self.decode_calls[i]()
+        else:
+            self.step_calls[i]()
 
     def time_write(self, reps=6):
         import torch
@@ -186,7 +183,8 @@ class Problem:
         import torch
         if self.kvarn:
             self.prepare_incremental(warmup + 2 * steps)
-            torch.cuda.synchronize()
+        self.prepare_calls(warmup + 2 * steps)
+        torch.cuda.synchronize()
         for i in range(warmup):
             self.step(i)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -201,9 +199,9 @@ class Problem:
         for i in range(steps):
             j = warmup + steps + i
             if self.kvarn:
-                self.append(j)
+                self.append_calls[j]()
                 ev[i][0].record()
-                self.decode(j)
+                self.decode_calls[j]()
             else:
                 ev[i][0].record()
                 self.step(j)
@@ -309,7 +307,7 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_all_formats.md")
 # every source a decode call or a write launch compiles from, and the build flags
 KERNEL_SOURCES = ("decode_attn.hip", "quant_write.hip", "kvarn_decode.hip", "kvarn_write.hip", "decode_common.h",
-                  "kvq_device.h", "kvq_internal.h")
+                  "row_encode.h", "kvq_device.h", "kvq_internal.h")
 
 
 def _code_only(text):

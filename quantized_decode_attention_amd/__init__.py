@@ -151,20 +151,25 @@ def kvq_decode_num_splits(lay: KvqLayout, batch: int, num_q_heads: int, max_page
     return int(_lib.kvq_decode_num_splits(ctypes.byref(lay), batch, num_q_heads, max_pages_per_seq, num_splits))
 
 
+def _decode_args(lay, cache, q, block_tables, context_lens, sm_scale, out, workspace, kvarn_tail, num_splits,
+                 stream):
+    import torch
+    B, Hq, _ = q.shape
+    return (ctypes.byref(lay), _ptr(cache, torch.uint8, "cache"), _ptr(q, torch.float16, "q"), Hq,
+            _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+            _ptr(context_lens, torch.int32, "context_lens"), B, float(sm_scale),
+            _ptr(kvarn_tail, torch.float16, "kvarn_tail"), _ptr(out, torch.float16, "out"),
+            _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
+            0 if workspace is None else workspace.numel(), num_splits, _stream(stream))
+
+
 def kvq_decode_attention(lay: KvqLayout, cache, q, block_tables, context_lens, sm_scale, out, workspace,
                          kvarn_tail=None, num_splits: int = 0, stream=None):
     """q, out: float16 [B, Hq, D]; block_tables: int32 [B, max_pages]; context_lens: int32 [B];
     workspace: uint8 of at least kvq_decode_workspace_bytes(...) bytes (or None when that is 0)."""
-    import torch
-    B, Hq, _ = q.shape
-    _check(_lib.kvq_decode_attention(
-        ctypes.byref(lay), _ptr(cache, torch.uint8, "cache"), _ptr(q, torch.float16, "q"), Hq,
-        _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
-        _ptr(context_lens, torch.int32, "context_lens"), B, float(sm_scale),
-        _ptr(kvarn_tail, torch.float16, "kvarn_tail"), _ptr(out, torch.float16, "out"),
-        _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
-        0 if workspace is None else workspace.numel(), num_splits, _stream(stream)),
-        "kvq_decode_attention")
+    _check(_lib.kvq_decode_attention(*_decode_args(lay, cache, q, block_tables, context_lens, sm_scale, out,
+                                                   workspace, kvarn_tail, num_splits, stream)),
+           "kvq_decode_attention")
 
 
 def kvq_decode_attention_noalloc(lay: KvqLayout, cache, q, block_tables, context_lens, sm_scale, out,
@@ -181,32 +186,42 @@ def kvq_decode_attention_noalloc(lay: KvqLayout, cache, q, block_tables, context
         _stream(stream)), "kvq_decode_attention_noalloc")
 
 
+def _append_args(lay, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens, sm_scale, out, workspace,
+                 num_splits, stream):
+    import torch
+    B, Hq, _ = q.shape
+    return (ctypes.byref(lay), _ptr(cache, torch.uint8, "cache"), _ptr(k_new, torch.float16, "k_new"),
+            _ptr(v_new, torch.float16, "v_new"), _ptr(slot_mapping, torch.int64, "slot_mapping"),
+            _ptr(q, torch.float16, "q"), Hq, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+            _ptr(context_lens, torch.int32, "context_lens"), B, float(sm_scale), _ptr(out, torch.float16, "out"),
+            _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
+            0 if workspace is None else workspace.numel(), num_splits, _stream(stream))
+
+
 def kvq_decode_attention_append(lay: KvqLayout, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens,
                                 sm_scale, out, workspace, num_splits: int = 0, stream=None):
     """One decode step: k_new, v_new: float16 [B, H, D] (one new token per sequence); slot_mapping: int64 [B];
     q, out: float16 [B, Hq, D]; block_tables: int32 [B, max_pages]; context_lens: int32 [B] (new token
     included); workspace as for kvq_decode_attention."""
+    _check(_lib.kvq_decode_attention_append(*_append_args(lay, cache, k_new, v_new, slot_mapping, q, block_tables,
+                                                          context_lens, sm_scale, out, workspace, num_splits,
+                                                          stream)),
+           "kvq_decode_attention_append")
+
+
+def _kvarn_append_args(lay, k, v, seq, pos, tail, block_tables, cache, stream):
     import torch
-    B, Hq, _ = q.shape
-    _check(_lib.kvq_decode_attention_append(
-        ctypes.byref(lay), _ptr(cache, torch.uint8, "cache"), _ptr(k_new, torch.float16, "k_new"),
-        _ptr(v_new, torch.float16, "v_new"), _ptr(slot_mapping, torch.int64, "slot_mapping"),
-        _ptr(q, torch.float16, "q"), Hq, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
-        _ptr(context_lens, torch.int32, "context_lens"), B, float(sm_scale), _ptr(out, torch.float16, "out"),
-        _ptr(workspace, torch.uint8, "workspace") if workspace is not None and workspace.numel() else None,
-        0 if workspace is None else workspace.numel(), num_splits, _stream(stream)),
-        "kvq_decode_attention_append")
+    return (ctypes.byref(lay), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
+            _ptr(seq, torch.int32, "seq"), _ptr(pos, torch.int32, "pos"), seq.shape[0],
+            _ptr(tail, torch.float16, "tail"), tail.shape[0], _ptr(block_tables, torch.int32, "block_tables"),
+            block_tables.shape[1], _ptr(cache, torch.uint8, "cache"), _stream(stream))
 
 
 def kvq_kvarn_append(lay: KvqLayout, k, v, seq, pos, tail, block_tables, cache, stream=None):
     """k, v: float16 [n, H, 128]; seq, pos: int32 [n]; tail: float16 [B, 2, H, 128, 128];
     block_tables: int32 [B, max_pages]; cache: uint8."""
-    import torch
-    _check(_lib.kvq_kvarn_append(
-        ctypes.byref(lay), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
-        _ptr(seq, torch.int32, "seq"), _ptr(pos, torch.int32, "pos"), seq.shape[0],
-        _ptr(tail, torch.float16, "tail"), tail.shape[0], _ptr(block_tables, torch.int32, "block_tables"),
-        block_tables.shape[1], _ptr(cache, torch.uint8, "cache"), _stream(stream)), "kvq_kvarn_append")
+    _check(_lib.kvq_kvarn_append(*_kvarn_append_args(lay, k, v, seq, pos, tail, block_tables, cache, stream)),
+           "kvq_kvarn_append")
 
 
 def kvq_dequantize(lay: KvqLayout, cache, slot_mapping, k_out, v_out, stream=None):
@@ -216,6 +231,44 @@ def kvq_dequantize(lay: KvqLayout, cache, slot_mapping, k_out, v_out, stream=Non
                                _ptr(slot_mapping, torch.int64, "slot_mapping"), slot_mapping.shape[0],
                                _ptr(k_out, torch.float32, "k_out"), _ptr(v_out, torch.float32, "v_out"),
                                _stream(stream)), "kvq_dequantize")
+
+
+# ---- prepared calls -----------------------------------------------------------
+# A serving loop that repeats a call with the same buffers can marshal its
+# arguments once: prepare_<entry point>(same arguments) returns a callable
+# that makes only the C call (and raises KvqError on a nonzero status).  The
+# stream is fixed when the call is prepared (the current stream by default);
+# the callable holds references to the tensors it was given, so they stay
+# allocated while it exists.
+
+def _prepared(fn, args, where, keep):
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise KvqError(st, where)
+    call.tensors = keep
+    return call
+
+
+def prepare_decode_attention(lay: KvqLayout, cache, q, block_tables, context_lens, sm_scale, out, workspace,
+                             kvarn_tail=None, num_splits: int = 0, stream=None):
+    return _prepared(_lib.kvq_decode_attention, _decode_args(lay, cache, q, block_tables, context_lens, sm_scale,
+                                                             out, workspace, kvarn_tail, num_splits, stream),
+                     "kvq_decode_attention", (lay, cache, q, block_tables, context_lens, out, workspace, kvarn_tail))
+
+
+def prepare_decode_attention_append(lay: KvqLayout, cache, k_new, v_new, slot_mapping, q, block_tables,
+                                    context_lens, sm_scale, out, workspace, num_splits: int = 0, stream=None):
+    return _prepared(_lib.kvq_decode_attention_append,
+                     _append_args(lay, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens, sm_scale,
+                                  out, workspace, num_splits, stream), "kvq_decode_attention_append",
+                     (lay, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens, out, workspace))
+
+
+def prepare_kvarn_append(lay: KvqLayout, k, v, seq, pos, tail, block_tables, cache, stream=None):
+    return _prepared(_lib.kvq_kvarn_append, _kvarn_append_args(lay, k, v, seq, pos, tail, block_tables, cache,
+                                                               stream), "kvq_kvarn_append",
+                     (lay, k, v, seq, pos, tail, block_tables, cache))
 
 
 # ---- small conveniences over the entry points --------------------------------

@@ -119,3 +119,64 @@ def test_append_slot_elsewhere(K, O, fmt, flags, splits):
     torch.cuda.synchronize()
     assert first_mismatch(cache.cpu().numpy(), after) is None
     assert_attn_close(out.cpu().numpy().astype(np.float64), ref, f"splits={splits}")
+
+
+def test_prepared_calls_match_the_plain_binding(K, O):
+    """The prepared calls (arguments marshalled once, then one C call per
+    use) give bit for bit the plain binding's results: the append step, the
+    decode and the KVarN append, each used twice."""
+    import torch
+    rng = np.random.default_rng(955)
+    H, G, D, P = 2, 8, 128, 16
+    ctx = np.array([300, 17, 1000, 1], np.int32)
+    B = ctx.size
+    bt, num_pages, slots_old, slots_new = step_problem(rng, B, H, G, D, P, ctx, set())
+    k_old = workloads.random_halves(rng, (slots_old.size, H, D))
+    v_old = workloads.random_halves(rng, (slots_old.size, H, D))
+    k_new = workloads.random_halves(rng, (B, H, D))
+    v_new = workloads.random_halves(rng, (B, H, D))
+    lay = K.layout(2, H, D, P, num_pages)
+    before = O.quantize_write(olayout(lay), k_old, v_old, slots_old)
+    q16 = workloads.random_halves(rng, (B, H * G, D))
+    q, btd, ctxd, kn, vn, sn = dev(q16), dev(bt), dev(ctx), dev(k_new), dev(v_new), dev(slots_new)
+    ws = K.DecodeWorkspace(lay, B, H * G, bt.shape[1], 3)
+    log("prepared append / decode")
+    res = []
+    for prepared in (False, True):
+        cache = dev(before)
+        out = torch.zeros((B, H * G, D), dtype=torch.float16, device="cuda")
+        out2 = torch.zeros_like(out)
+        if prepared:
+            step = K.prepare_decode_attention_append(lay, cache, kn, vn, sn, q, btd, ctxd, 0.09, out, ws.buffer, 3)
+            dec = K.prepare_decode_attention(lay, cache, q, btd, ctxd, 0.09, out2, ws.buffer, None, 3)
+            step(), step(), dec(), dec()
+        else:
+            for _ in range(2):
+                K.kvq_decode_attention_append(lay, cache, kn, vn, sn, q, btd, ctxd, 0.09, out, ws.buffer, 3)
+            for _ in range(2):
+                K.kvq_decode_attention(lay, cache, q, btd, ctxd, 0.09, out2, ws.buffer, None, 3)
+        torch.cuda.synchronize()
+        res.append((cache.cpu().numpy(), out.cpu().numpy(), out2.cpu().numpy()))
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+    # KVarN: two appended tokens per sequence through prepared calls
+    klay = K.layout(5, H, D, 128, 8)
+    kbt = np.arange(8, dtype=np.int32).reshape(2, 4)
+    seq = dev(np.arange(2, dtype=np.int32))
+    kv = [dev(workloads.random_halves(rng, (2, H, D))) for _ in range(4)]
+    log("prepared kvarn append")
+    res = []
+    for prepared in (False, True):
+        cache = torch.zeros(8 * K.kvq_page_bytes(klay), dtype=torch.uint8, device="cuda")
+        tail = torch.zeros((2, 2, H, 128, D), dtype=torch.float16, device="cuda")
+        for j in range(2):
+            pos = dev(np.full(2, j, np.int32))
+            if prepared:
+                K.prepare_kvarn_append(klay, kv[2 * j], kv[2 * j + 1], seq, pos, tail, dev(kbt), cache)()
+            else:
+                K.kvq_kvarn_append(klay, kv[2 * j], kv[2 * j + 1], seq, pos, tail, dev(kbt), cache)
+        torch.cuda.synchronize()
+        res.append((cache.cpu().numpy(), tail.cpu().numpy()))
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
