@@ -179,9 +179,10 @@ kvq_status kvq_check_device(int hip_device);
  *                     channels), scales folded into the metadata above.
  *                     Requires n_tok % 128 == 0; tokens 128i..128i+127 must
  *                     map to slots s0 + 0..127 of one tile of a page, s0 a
- *                     multiple of 128 (only the first slot of each tile is
- *                     read; a first slot off a multiple of 128 skips the
- *                     tile).
+ *                     multiple of 128.  A run whose first slot is outside
+ *                     the pool is skipped; a run that breaks the rule
+ *                     otherwise is skipped and raises
+ *                     KVQ_DEVERR_KVARN_TILE_SLOTS (kvq_take_device_errors).
  * Errors: KVQ_ERR_INVALID_ARG for NULL pointers, n_tok < 0, bad scales or a
  * KVarN n_tok not a multiple of 128; KVQ_ERR_UNSUPPORTED for layouts outside
  * the list above; KVQ_ERR_DEVICE off gfx950. */
@@ -206,9 +207,10 @@ kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const voi
  * page block_tables[seq][pos / P], with exactly the bytes kvq_quantize_write
  * gives for those 128 tokens.  Within one call, the tokens of a sequence must
  * lie in one tile and have distinct positions (a token of the next tile would
- * overwrite a tail row before the tile is quantised); entries with a sequence
- * outside [0, batch), a negative position or a page outside the pool are
- * skipped.  Two launches on `stream` (copy, then tile completion).
+ * overwrite a tail row before the tile is quantised): a call that breaks this
+ * raises KVQ_DEVERR_KVARN_APPEND_SPAN (kvq_take_device_errors) and leaves
+ * that sequence's tail and tile undefined.  Entries with a sequence outside
+ * [0, batch), a negative position or a page outside the pool are skipped.  Two launches on `stream` (copy, then tile completion).
  * Errors: KVQ_ERR_INVALID_ARG for a non-KVarN layout, NULL pointers or
  * negative sizes; KVQ_ERR_DEVICE off gfx950. */
 kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void* v, const int32_t* seq,
@@ -354,6 +356,25 @@ kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int
  * that [P5] §Blackwell 支持不是一个单一布尔值 asks for in place of a silent
  * fallback.  Never NULL; unknown codes give "unknown status". */
 const char* kvq_status_string(kvq_status status);
+
+/* Contract violations the kernels find in arguments that live in device
+ * memory, where the host cannot check them before the launch ([P5]
+ * §需要记录的系统指标 asks for failures to be recorded, not hidden): bits of
+ * the word kvq_take_device_errors returns. */
+#define KVQ_DEVERR_KVARN_TILE_SLOTS (1u << 0)  /* KVarN kvq_quantize_write: a 128-token run's slots are
+                                                  not one tile of a page in order; that run was skipped */
+#define KVQ_DEVERR_KVARN_APPEND_SPAN (1u << 1) /* kvq_kvarn_append: a sequence's tokens in one call span
+                                                  two tiles or repeat a position */
+
+/* Waits for `stream` (a hipStream_t, NULL = the default stream), then returns
+ * in *flags the KVQ_DEVERR_* bits raised on the current HIP device since the
+ * previous call, and clears them.  The word is per device and shared by all
+ * streams: kernels still running on other streams may raise bits after the
+ * read.  Synchronous (a device-to-host copy); not for use under graph
+ * capture.
+ * Errors: KVQ_ERR_INVALID_ARG for NULL flags; KVQ_ERR_DEVICE off gfx950;
+ * KVQ_ERR_HIP when a HIP call fails. */
+kvq_status kvq_take_device_errors(uint32_t* flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,7 @@ def _load():
     sigs = {
         "kvq_page_bytes": (I64, [LP]),
         "kvq_check_device": (ctypes.c_int, [ctypes.c_int]),
+        "kvq_take_device_errors": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), P]),
         "kvq_quantize_write": (ctypes.c_int, [LP, P, P, P, I64, P, P]),
         "kvq_decode_workspace_bytes": (I64, [LP, I32, I32, I32, I32]),
         "kvq_decode_num_splits": (I32, [LP, I32, I32, I32, I32]),
@@ -128,6 +129,18 @@ def kvq_page_bytes(lay: KvqLayout) -> int:
 
 def kvq_check_device(device: int = 0) -> int:
     return int(_lib.kvq_check_device(device))
+
+
+KVQ_DEVERR_KVARN_TILE_SLOTS = 1 << 0
+KVQ_DEVERR_KVARN_APPEND_SPAN = 1 << 1
+
+
+def kvq_take_device_errors(stream=None) -> int:
+    """Waits for the stream, returns the KVQ_DEVERR_* bits raised on the current device since the previous
+    call and clears them."""
+    flags = ctypes.c_uint32(0)
+    _check(_lib.kvq_take_device_errors(ctypes.byref(flags), _stream(stream)), "kvq_take_device_errors")
+    return int(flags.value)
 
 
 def kvq_quantize_write(lay: KvqLayout, k, v, slot_mapping, cache, stream=None):

@@ -34,6 +34,7 @@
 // the canonical order.  Within a wavefront the lanes hold 64 consecutive rows
 // (or columns) of one half, so both access patterns are free of bank
 // conflicts.  Two workgroups fit the LDS of a compute unit: 8 wavefronts.
+#include "kvq.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -280,13 +281,28 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
 
 constexpr int kLdsFloats = N * LDP + 4 * N;
 
+// Contract violations found in device-resident arguments (KVQ_DEVERR_* bits of
+// kvq.h), one word per device: raised with a vector atomic OR, read and
+// cleared by kvq_take_device_errors.
+__device__ uint32_t g_device_errors;
+
+__device__ __forceinline__ void raise_error(uint32_t bit) { atomicOr(&g_device_errors, bit); }
+
 __global__ __launch_bounds__(256) void kvarn_write_kernel(WriteArgs a) {
   __shared__ float lds[kLdsFloats];
   const int ti = blockIdx.x, h = blockIdx.y, side = blockIdx.z;
-  // only the first slot of a tile is read: the tile fills one tile of its
-  // page in order (a first slot off a multiple of 128 is skipped)
+  // The run's first slot places the tile: one outside the pool skips it (as
+  // for every format), and otherwise all 128 slots must be that tile of its
+  // page, in order.  A run that is not is skipped and reported.
   const int64_t s0 = a.slots[(int64_t)ti * N];
-  if (s0 < 0 || s0 >= (int64_t)a.num_pages * a.P || s0 % N != 0) return;
+  if (s0 < 0) return;
+  const int tid = threadIdx.x;
+  const bool bad_slot = tid < N && a.slots[(int64_t)ti * N + tid] != s0 + tid;
+  if (s0 >= (int64_t)a.num_pages * a.P) return;  // outside the pool: skipped, as for every format
+  if (__syncthreads_or(bad_slot || s0 % N != 0)) {
+    if (tid == 0 && h == 0 && side == 0) raise_error(KVQ_DEVERR_KVARN_TILE_SLOTS);
+    return;
+  }
   const int64_t page = s0 / a.P;
   uint8_t* chunk = a.cache + (page * a.H + h) * a.geom.chunk_bytes + (s0 - page * a.P) / N * kTileBytes;
   const uint16_t* src = (side ? a.v : a.k) + ((int64_t)ti * N * a.H + h) * N;
@@ -302,6 +318,15 @@ __global__ __launch_bounds__(64) void kvarn_append_kernel(KvarnAppendArgs a) {
   const int h = hs >> 1, side = hs & 1;
   const int b = a.seq[i], pos = a.pos[i];
   if (b < 0 || b >= a.batch || pos < 0) return;
+  if (hs == 0) {
+    // the call's other tokens of this sequence must share this token's tile
+    // and not its position (rows of the tail would be overwritten before the
+    // tile is quantised); a violation is reported, not repaired
+    bool bad = false;
+    for (int64_t j = threadIdx.x; j < a.n_tok; j += 64)
+      bad |= j != i && a.seq[j] == b && a.pos[j] >= 0 && ((a.pos[j] >> 7) != (pos >> 7) || a.pos[j] == pos);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && threadIdx.x == 0) raise_error(KVQ_DEVERR_KVARN_APPEND_SPAN);
+  }
   const uint16_t* src = (side ? a.v : a.k) + (i * a.H + h) * N;
   uint16_t* dst = a.tail + ((((int64_t)b * 2 + side) * a.H + h) * N + (pos & (N - 1))) * N;
   if (threadIdx.x < N / 8)
@@ -327,6 +352,18 @@ __global__ __launch_bounds__(256) void kvarn_complete_kernel(KvarnAppendArgs a) 
 }
 
 }  // namespace
+
+hipError_t take_device_errors(uint32_t* flags) {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_device_errors));
+  if (e != hipSuccess) return e;
+  uint32_t v = 0;
+  if ((e = hipMemcpy(&v, p, sizeof v, hipMemcpyDeviceToHost)) != hipSuccess) return e;
+  const uint32_t zero = 0;
+  if ((e = hipMemcpy(p, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess) return e;
+  *flags = v;
+  return hipSuccess;
+}
 
 hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s) {
   const int64_t tiles = a.n_tok / N;

@@ -456,6 +456,14 @@ kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int
   return from_hip(launch_dequant(layout->format, a, k_out, v_out, static_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_take_device_errors(uint32_t* flags, void* stream) {
+  if (!flags) return KVQ_ERR_INVALID_ARG;
+  kvq_status st = current_device_ok();
+  if (st != KVQ_OK) return st;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KVQ_ERR_HIP;
+  return from_hip(take_device_errors(flags));
+}
+
 const char* kvq_status_string(kvq_status status) {
   switch (status) {
     case KVQ_OK: return "success";
@@ -463,7 +471,7 @@ const char* kvq_status_string(kvq_status status) {
     case KVQ_ERR_UNSUPPORTED: return "unsupported layout or shape";
     case KVQ_ERR_WORKSPACE_TOO_SMALL: return "decode workspace too small";
     case KVQ_ERR_DEVICE: return "current device is not an MI355X (gfx950)";
-    case KVQ_ERR_HIP: return "HIP kernel launch failed";
+    case KVQ_ERR_HIP: return "a HIP call failed (kernel launch or device query)";
     case KVQ_ERR_SCRATCH_TOO_SMALL:
       return "problem needs more split records than the fixed decode workspace (KVQ_DECODE_SCRATCH_BYTES) holds";
   }

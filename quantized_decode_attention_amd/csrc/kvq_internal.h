@@ -86,6 +86,10 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(int fmt, const WriteArgs& a, float* k_out, float* v_out, hipStream_t s);
 
+// KVQ_DEVERR_* bits raised on the current device since the last call
+// (read and cleared; synchronous).
+hipError_t take_device_errors(uint32_t* flags);
+
 // Device address of the current device's fixed decode workspace
 // (KVQ_DECODE_SCRATCH_BYTES), looked up on the first call per device.
 hipError_t decode_scratch(void** ptr);

@@ -146,6 +146,11 @@ def test_device_check_without_gpu(K):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert K.kvq_check_device(0) == 4
+    # the device-error query checks its pointer first, then the device
+    assert K.lib.kvq_take_device_errors(None, None) == 1
+    flags = ctypes.c_uint32(7)
+    assert K.lib.kvq_take_device_errors(ctypes.byref(flags), None) == 4
+    assert flags.value == 7  # untouched
 
 
 def test_single_hip_runtime_in_process(K):

@@ -304,3 +304,54 @@ def test_kvarn_decode_edge_contexts_and_repeated_tiles(K, O):
         assert_attn_close(got, ref, f"splits={splits}")
         ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
         assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-4 + 1e-4 * np.abs(ref))
+
+
+def test_kvarn_contract_violations_are_reported(K, O):
+    """The KVarN inputs the host cannot check (they live in device memory)
+    are checked by the kernels: a whole-tile write run whose slots are not
+    one tile of a page in order is skipped and raises
+    KVQ_DEVERR_KVARN_TILE_SLOTS; an append whose tokens of one sequence span
+    two tiles or repeat a position raises KVQ_DEVERR_KVARN_APPEND_SPAN.  Valid
+    runs are written bit for bit as the oracle writes them, and every flag is
+    cleared once read."""
+    import torch
+    rng = np.random.default_rng(560)
+    H, n_tiles, num_pages = 2, 5, 8
+    lay = K.layout(5, H, D, P, num_pages)
+    K.kvq_take_device_errors()  # start clean
+    pages = rng.permutation(num_pages)[:n_tiles]
+    good = (pages[:, None].astype(np.int64) * P + np.arange(P)).reshape(-1)
+    k16 = workloads.random_halves(rng, (n_tiles * P, H, D))
+    v16 = workloads.random_halves(rng, (n_tiles * P, H, D))
+    log("kvarn write: valid runs")
+    got = gpu_write(K, lay, k16, v16, good).cpu().numpy()
+    assert K.kvq_take_device_errors() == 0
+    assert first_mismatch(got, O.quantize_write(olayout(lay), k16, v16, good)) is None
+
+    bad = good.copy()
+    bad[1 * P + 5], bad[1 * P + 6] = bad[1 * P + 6], bad[1 * P + 5]  # run 1: two slots swapped
+    bad[3 * P: 4 * P] += 64  # run 3: starts half way into a tile
+    bad[4 * P] = -1  # run 4: first slot negative, skipped without a report
+    kept = good.copy()
+    for r in (1, 3, 4):
+        kept[r * P] = -1
+    log("kvarn write: runs that break the tile rule")
+    got = gpu_write(K, lay, k16, v16, bad).cpu().numpy()
+    assert K.kvq_take_device_errors() == K.KVQ_DEVERR_KVARN_TILE_SLOTS
+    assert K.kvq_take_device_errors() == 0
+    assert first_mismatch(got, O.quantize_write(olayout(lay), k16, v16, kept)) is None
+
+    # appends: one token per sequence is fine; a sequence's tokens at 127 and
+    # 128 (two tiles), or twice at one position, are reported
+    B = 2
+    bt = dev(np.arange(B * 2, dtype=np.int32).reshape(B, 2))
+    cache = torch.zeros(num_pages * K.kvq_page_bytes(lay), dtype=torch.uint8, device="cuda")
+    tail = torch.zeros((B, 2, H, P, D), dtype=torch.float16, device="cuda")
+    for seq, pos, want in (([0, 1], [5, 9], 0), ([0, 1, 0], [127, 3, 128], K.KVQ_DEVERR_KVARN_APPEND_SPAN),
+                           ([1, 1], [7, 7], K.KVQ_DEVERR_KVARN_APPEND_SPAN), ([0, 1], [6, 10], 0)):
+        n = len(seq)
+        log(f"kvarn append seq={seq} pos={pos}")
+        kd = dev(workloads.random_halves(rng, (n, H, D)))
+        vd = dev(workloads.random_halves(rng, (n, H, D)))
+        K.kvq_kvarn_append(lay, kd, vd, dev(np.array(seq, np.int32)), dev(np.array(pos, np.int32)), tail, bt, cache)
+        assert K.kvq_take_device_errors() == want
