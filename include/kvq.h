@@ -96,7 +96,7 @@ typedef enum {
 typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_INVALID_ARG = 1,         /* NULL pointer, negative size, bad scale */
-  KVQ_ERR_UNSUPPORTED = 2,         /* valid request this build does not serve */
+  KVQ_ERR_UNSUPPORTED = 2,         /* valid request the library does not serve */
   KVQ_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace smaller than required */
   KVQ_ERR_DEVICE = 4,              /* current device is not gfx950 */
   KVQ_ERR_HIP = 5,                 /* a HIP call failed (launch error) */
