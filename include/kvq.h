@@ -26,6 +26,10 @@
  *     capability be explicit).
  *   - Tensors are dense and contiguous in the stated shapes; binary16 is IEEE
  *     half precision; inputs are finite.
+ *   - Alignment: binary16 tensors, caches, workspaces and the KVarN tail start
+ *     on 16-byte boundaries, int32 and int64 arrays and binary32 outputs on
+ *     their own size (torch allocations satisfy all of them); other pointers
+ *     are rejected with KVQ_ERR_INVALID_ARG before anything is launched.
  *
  * Cache layout (the storage contract; page_bytes = num_kv_heads * chunk_bytes):
  *   the chunk of (page p, kv head h) starts at byte (p * H + h) * chunk_bytes.

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cstdint>
 
 #include "kvq.h"
 #include "kvq_internal.h"
@@ -116,6 +117,11 @@ kvq_status current_device_ok() {
 }
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+// The kernels move binary16 rows, cache bytes, split records and the KVarN
+// tail with 16-byte vector accesses, and read the index arrays as naturally
+// aligned words; a pointer off those alignments is rejected before launch.
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
 // The split kernel's unit of work along the context: a page, or for KVarN a
 // 128-token tile (a page holds page_size / 128 of them).
@@ -246,6 +252,9 @@ kvq_status check_decode_plan(const kvq_layout* L, const void* cache, const void*
   const int G = num_q_heads / H;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
   if (batch > 0 && (!cache || !q || !block_tables || !context_lens || !out)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(cache, 16) || !aligned(q, 16) || !aligned(out, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4))
+    return KVQ_ERR_INVALID_ARG;
   plan(L, batch, G, max_pages_per_seq, num_splits, splits, pps, waves);
   *need = workspace_bytes_for(L, batch, *splits);
   return KVQ_OK;
@@ -261,7 +270,7 @@ kvq_status check_decode(const kvq_layout* L, const void* cache, const void* q, i
                                           batch, sm_scale, out, num_splits, splits, pps, waves, &need);
   if (st != KVQ_OK) return st;
   if (workspace_bytes < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0 && !workspace) return KVQ_ERR_INVALID_ARG;
+  if (need > 0 && (!workspace || !aligned(workspace, 16))) return KVQ_ERR_INVALID_ARG;
   return current_device_ok();
 }
 
@@ -312,6 +321,8 @@ kvq_status kvq_quantize_write(const kvq_layout* layout, const void* k, const voi
   if (n_tok < 0) return KVQ_ERR_INVALID_ARG;
   if (layout->format == KVQ_KVARN_K4V2_G128 && n_tok % 128 != 0) return KVQ_ERR_INVALID_ARG;
   if (n_tok > 0 && (!k || !v || !slot_mapping || !cache)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(cache, 16) || !aligned(slot_mapping, 8))
+    return KVQ_ERR_INVALID_ARG;
   if ((st = current_device_ok()) != KVQ_OK) return st;
   if (n_tok == 0) return KVQ_OK;
   const WriteArgs a = write_args(layout, k, v, slot_mapping, n_tok, cache);
@@ -328,6 +339,9 @@ kvq_status kvq_kvarn_append(const kvq_layout* layout, const void* k, const void*
   if (layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
   if (n_tok < 0 || batch < 0 || max_pages_per_seq < 1) return KVQ_ERR_INVALID_ARG;
   if (n_tok > 0 && (!k || !v || !seq || !pos || !tail || !block_tables || !cache)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(tail, 16) || !aligned(cache, 16) || !aligned(seq, 4) ||
+      !aligned(pos, 4) || !aligned(block_tables, 4))
+    return KVQ_ERR_INVALID_ARG;
   if ((st = current_device_ok()) != KVQ_OK) return st;
   if (n_tok == 0 || batch == 0) return KVQ_OK;
   KvarnAppendArgs a{};
@@ -374,6 +388,7 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const void* cache, con
                                 const void* kvarn_tail, void* out, void* workspace, int64_t workspace_bytes,
                                 int32_t num_splits, void* stream) {
   if (kvarn_tail && layout && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(kvarn_tail, 16)) return KVQ_ERR_INVALID_ARG;
   int splits, pps, waves;
   const kvq_status st = check_decode(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens,
                                      batch, sm_scale, out, workspace, workspace_bytes, num_splits, &splits, &pps,
@@ -392,6 +407,7 @@ kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const void* ca
                                         const int32_t* context_lens, int32_t batch, float sm_scale,
                                         const void* kvarn_tail, void* out, int32_t num_splits, void* stream) {
   if (kvarn_tail && layout && layout->format != KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(kvarn_tail, 16)) return KVQ_ERR_INVALID_ARG;
   int splits, pps, waves;
   int64_t need = 0;
   kvq_status st = check_decode_plan(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens,
@@ -420,6 +436,7 @@ kvq_status kvq_decode_attention_append(const kvq_layout* layout, void* cache, co
                                        int32_t num_splits, void* stream) {
   if (layout && layout->format == KVQ_KVARN_K4V2_G128) return KVQ_ERR_INVALID_ARG;
   if (batch > 0 && (!k_new || !v_new || !slot_mapping)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8)) return KVQ_ERR_INVALID_ARG;
   int splits, pps, waves;
   const kvq_status st = check_decode(layout, cache, q, num_q_heads, block_tables, max_pages_per_seq, context_lens,
                                      batch, sm_scale, out, workspace, workspace_bytes, num_splits, &splits, &pps,
@@ -440,6 +457,8 @@ kvq_status kvq_dequantize(const kvq_layout* layout, const void* cache, const int
   if (st != KVQ_OK) return st;
   if (n_tok < 0) return KVQ_ERR_INVALID_ARG;
   if (n_tok > 0 && (!cache || !slot_mapping || !k_out || !v_out)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(cache, 16) || !aligned(slot_mapping, 8) || !aligned(k_out, 4) || !aligned(v_out, 4))
+    return KVQ_ERR_INVALID_ARG;
   if ((st = current_device_ok()) != KVQ_OK) return st;
   if (n_tok == 0) return KVQ_OK;
   WriteArgs a{};

@@ -106,6 +106,45 @@ def test_argument_errors_before_launch(K):
                                           None) == 6
 
 
+def test_misaligned_pointers_rejected(K):
+    """Every entry point rejects a data pointer off its 16-byte alignment (or
+    an index array off its own size) with KVQ_ERR_INVALID_ARG before it
+    looks for a device."""
+    L = K.lib
+    lay = K.layout(2, 8, 128, 16, 64)
+    klay = K.layout(5, 8, 128, 128, 8)
+    a = 1 << 20              # aligned stand-in address (never dereferenced)
+    P = lambda x: ctypes.c_void_p(x)
+    for off in (2, 8):
+        m = a + off          # binary16 data off 16 bytes
+        assert L.kvq_quantize_write(ctypes.byref(lay), P(m), P(a), P(a), 16, P(a), None) == 1
+        assert L.kvq_quantize_write(ctypes.byref(lay), P(a), P(a), P(a), 16, P(m), None) == 1
+        assert L.kvq_decode_attention(ctypes.byref(lay), P(a), P(m), 64, P(a), 4, P(a), 2, 0.1, None, P(a),
+                                      None, 0, 1, None) == 1
+        assert L.kvq_decode_attention(ctypes.byref(lay), P(a), P(a), 64, P(a), 4, P(a), 2, 0.1, None, P(m),
+                                      None, 0, 1, None) == 1
+        assert L.kvq_decode_attention_noalloc(ctypes.byref(lay), P(m), P(a), 64, P(a), 4, P(a), 2, 0.1, None,
+                                              P(a), 1, None) == 1
+        assert L.kvq_decode_attention_append(ctypes.byref(lay), P(a), P(m), P(a), P(a), P(a), 64, P(a), 4, P(a),
+                                             2, 0.1, P(a), None, 0, 1, None) == 1
+        assert L.kvq_kvarn_append(ctypes.byref(klay), P(a), P(a), P(a), P(a), 2, P(m), 2, P(a), 4, P(a), None) == 1
+        assert L.kvq_dequantize(ctypes.byref(lay), P(m), P(a), 16, P(a), P(a), None) == 1
+    # index arrays off their own size, a workspace off 16 bytes, a misaligned KVarN tail
+    assert L.kvq_quantize_write(ctypes.byref(lay), P(a), P(a), P(a + 4), 16, P(a), None) == 1
+    assert L.kvq_decode_attention(ctypes.byref(lay), P(a), P(a), 64, P(a + 2), 4, P(a), 2, 0.1, None, P(a),
+                                  None, 0, 1, None) == 1
+    assert L.kvq_decode_attention(ctypes.byref(lay), P(a), P(a), 64, P(a), 4, P(a), 2, 0.1, None, P(a),
+                                  P(a + 4), 1 << 20, 4, None) == 1
+    assert L.kvq_decode_attention(ctypes.byref(klay), P(a), P(a), 64, P(a), 4, P(a), 2, 0.1, P(a + 8), P(a),
+                                  P(a), 1 << 20, 1, None) == 1
+    assert L.kvq_dequantize(ctypes.byref(lay), P(a), P(a), 16, P(a + 2), P(a), None) == 1
+    # the same calls with aligned pointers get past these checks (no device here: KVQ_ERR_DEVICE)
+    import torch
+    if not torch.cuda.is_available():
+        assert L.kvq_quantize_write(ctypes.byref(lay), P(a), P(a), P(a), 16, P(a), None) == 4
+        assert L.kvq_dequantize(ctypes.byref(lay), P(a), P(a), 16, P(a), P(a), None) == 4
+
+
 def test_split_plan_and_workspace(K):
     import torch
     if torch.cuda.is_available():
