@@ -387,10 +387,12 @@ static float dev128(const float* v) {
  * which folds the scales back per channel for keys and per token for values
  * ([P2] §技术原理, stage 4).
  * Readings: the normalisation alternates a pass over tokens and a pass over
- * channels, 4 sweeps, dividing by the population deviation and multiplying
- * the running factor (the log-domain update of the page, done in the linear
- * domain); quantisation is asymmetric round-to-nearest with zero = group
- * minimum and step = (max - min) / (2^bits - 1), codes clipped to the range. */
+ * channels, 4 sweeps; a pass multiplies the values by RN(1 / sigma), sigma
+ * the population deviation, and the running factor by sigma (the page's
+ * log-domain update, subtracting log sigma, done in the linear domain with
+ * one rounding of the reciprocal, as the rotation's x RN(1/sqrt(128)));
+ * quantisation is asymmetric round-to-nearest with zero = group minimum and
+ * step = (max - min) / (2^bits - 1), codes clipped to the range. */
 void kvqo_kvarn_tile(const uint16_t* x16, int64_t stride, int side, float* y_rot,
                      float* y_norm, float* r_out, float* c_out, uint8_t* codes,
                      float* qs, float* qm, float* meta) {
@@ -412,13 +414,15 @@ void kvqo_kvarn_tile(const uint16_t* x16, int64_t stride, int side, float* y_rot
   for (int it = 0; it < KVARN_ITERS; it++) {
     for (int t = 0; t < N; t++) {
       float sd = dev128(Y + t * N);
-      for (int j = 0; j < N; j++) Y[t * N + j] = Y[t * N + j] / sd;
+      float inv = 1.0f / sd;
+      for (int j = 0; j < N; j++) Y[t * N + j] = Y[t * N + j] * inv;
       r[t] = r[t] * sd;
     }
     for (int j = 0; j < N; j++) {
       for (int t = 0; t < N; t++) col[t] = Y[t * N + j];
       float sd = dev128(col);
-      for (int t = 0; t < N; t++) Y[t * N + j] = Y[t * N + j] / sd;
+      float inv = 1.0f / sd;
+      for (int t = 0; t < N; t++) Y[t * N + j] = Y[t * N + j] * inv;
       c[j] = c[j] * sd;
     }
   }

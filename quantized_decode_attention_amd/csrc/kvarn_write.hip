@@ -10,10 +10,12 @@
 //     (a + b, a - b) on pairs (j, j + h), j & h = 0, h = 1, 2, ..., 64, then
 //     one multiplication by RN(1/sqrt(128));
 //   * normalisation: 4 sweeps, each a pass over the token rows followed by a
-//     pass over the channel columns; a pass divides a row (column) by its
-//     population standard deviation (mean and mean square by a balanced
-//     pairwise sum, 1/128 applied exactly) and multiplies the row's (column's)
-//     running factor by it; a zero or non-finite deviation counts as 1;
+//     pass over the channel columns; a pass multiplies a row (column) by
+//     RN(1 / sigma), sigma its population standard deviation (mean and mean
+//     square by a balanced pairwise sum, 1/128 applied exactly), and the
+//     row's (column's) running factor by sigma -- the page's log-domain
+//     update, subtracting log sigma, in the linear domain with one rounding
+//     of the reciprocal; a zero or non-finite deviation counts as 1;
 //   * quantisation: zero = group minimum, step = (max - min) / (2^bits - 1),
 //     code = clip(rne((y - min) / step), 0, 2^bits - 1), all-equal groups
 //     give code 0; keys 4 bits per channel over the tile's tokens, values 2
@@ -26,14 +28,18 @@
 //
 // Mapping.  One workgroup of 256 threads (4 wavefronts) per (tile, kv head,
 // side).  The tile lives in LDS as binary32 with rows padded to 129 words.
-// Thread (i, half) -- i = 64 * (wave & 1) + lane, half = wave >> 1 -- holds
-// the half [64 half, 64 half + 64) of token row i in a token pass and of
-// channel column i in a channel pass.  A 128-value sum is the canonical tree
-// of its two 64-value halves, S = S(left) + S(right): each thread sums its
-// half in registers and the two halves meet through LDS, so every sum keeps
-// the canonical order.  Within a wavefront the lanes hold 64 consecutive rows
-// (or columns) of one half, so both access patterns are free of bank
-// conflicts.  Two workgroups fit the LDS of a compute unit: 8 wavefronts.
+// Lanes l and l + 32 of wavefront w share index i = 32 w + (l & 31): the
+// lower lane holds the left half [0, 64) of token row i in a token pass and
+// of channel column i in a channel pass, the upper lane the right half
+// [64, 128).  A 128-value sum is the canonical tree of its two 64-value
+// halves, S = S(left) + S(right): each lane sums its half in registers and
+// v_permlane32_swap hands both halves' sums to both lanes, with no LDS round
+// trip or barrier.  The upper lane keeps its 64 values rotated by 32 in its
+// registers: value j is element (j + 32) mod 64 of its half.  That leaves
+// every sum unchanged (it swaps the two 32-value subtrees of the half's tree,
+// and binary32 addition commutes) and makes both access patterns free of LDS
+// bank conflicts (the two lanes of a pair sit 32 banks apart).  Two
+// workgroups fit the LDS of a compute unit: 8 wavefronts.
 #include "kvq.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -68,22 +74,28 @@ __device__ __forceinline__ float tree_sum64(const float (&v)[H]) {
   return t[0];
 }
 
-// Workgroup exchange of the two halves' partial results for index i:
-// slot[half][i]; returns the left half's and the right half's values.
+// The two halves' partial results for index i, from lanes l and l + 32:
+// returns the left half's and the right half's values in both lanes.
 struct Halves {
   float left, right;
 };
-__device__ __forceinline__ Halves exchange(float* slot, int i, int half, float v) {
-  slot[half * N + i] = v;
-  __syncthreads();
-  const Halves r{slot[i], slot[N + i]};
-  return r;
+__device__ __forceinline__ Halves exchange(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return Halves{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Column within the row (row within the column) of value j of this lane's
+// half, the right half rotated by 32.
+__device__ __forceinline__ int pos(int j, int half) { return j < 32 ? j + 96 * half : j + 32 * half; }
+// ... and of the same element of the other half.
+__device__ __forceinline__ int partner_pos(int j, int half) {
+  return j < 32 ? j + 64 - 32 * half : j + 64 - 96 * half;
 }
 
 // Population standard deviation of 128 values (this thread's half v and the
 // partner's); a zero or non-finite result becomes 1.
-__device__ __forceinline__ float deviation(const float (&v)[H], float* xa, float* xb, int i, int half) {
-  const Halves s = exchange(xa, i, half, tree_sum64(v));
+__device__ __forceinline__ float deviation(const float (&v)[H]) {
+  const Halves s = exchange(tree_sum64(v));
   const float mean = (s.left + s.right) * 0.0078125f;
   float sq[H];
 #pragma unroll
@@ -91,31 +103,30 @@ __device__ __forceinline__ float deviation(const float (&v)[H], float* xa, float
     const float d = v[k] - mean;
     sq[k] = d * d;
   }
-  const Halves q = exchange(xb, i, half, tree_sum64(sq));
+  const Halves q = exchange(tree_sum64(sq));
   float sd = __builtin_sqrtf((q.left + q.right) * 0.0078125f);
   if (!(sd > 0.0f) || !__builtin_isfinite(sd)) sd = 1.0f;
   return sd;
 }
 
-// x / s correctly rounded (s > 0), zero kept with its sign: the quotient of
-// a non-zero x already has x's sign, so copying the sign only matters for -0.
-__device__ __forceinline__ float div_rn_z(float x, float s, Recip r) {
-  return __builtin_copysignf(div_rn(x, s, r), x);
-}
-
-// Divide the 128 values by their deviation; returns the deviation.
-__device__ __forceinline__ float normalise(float (&v)[H], float* xa, float* xb, int i, int half) {
-  const float sd = deviation(v, xa, xb, i, half);
-  const Recip rc = make_recip(sd);
+// Scale the 128 values by RN(1 / deviation) (one rounding of the reciprocal,
+// one of each product; the sign of zero carries through the product);
+// returns the deviation.
+__device__ __forceinline__ float normalise(float (&v)[H]) {
+  const float sd = deviation(v);
+  const float inv = 1.0f / sd;
 #pragma unroll
-  for (int k = 0; k < H; ++k) v[k] = div_rn_z(v[k], sd, rc);
+  for (int k = 0; k < H; ++k) v[k] = v[k] * inv;
   return sd;
 }
 
-// Butterfly stages h = 1 .. 32 of the rotation, all inside one half.
-__device__ __forceinline__ void rotate_half(float (&y)[H]) {
+// Butterfly stages h = 1 .. 32 of the rotation on this lane's half.  Stages
+// below 32 stay inside each 32-value block, so the right half's rotated order
+// does not matter to them; stage 32 puts each pair's sum and difference at
+// the registers of their own elements.
+__device__ __forceinline__ void rotate_half(float (&y)[H], int half) {
 #pragma unroll
-  for (int h = 1; h < H; h <<= 1)
+  for (int h = 1; h < H / 2; h <<= 1)
 #pragma unroll
     for (int j = 0; j < H; ++j)
       if ((j & h) == 0) {
@@ -123,22 +134,31 @@ __device__ __forceinline__ void rotate_half(float (&y)[H]) {
         y[j] = p + q;
         y[j + h] = p - q;
       }
+#pragma unroll
+  for (int j = 0; j < H / 2; ++j) {
+    // left half: p = element j, q = element j + 32; right half: the reverse
+    const float p = y[j], q = y[j + H / 2];
+    const float sum = p + q;
+    y[j] = half == 0 ? sum : q - p;
+    y[j + H / 2] = half == 0 ? p - q : sum;
+  }
 }
 
-// Asymmetric round-to-nearest of one group of 128 values (this thread's half
-// and the partner's) into LEVELS + 1 codes; this half's codes go to LDS bytes
-// codes[stride * k].  Returns the step; *mn_out receives the zero point.
+// Asymmetric round-to-nearest of one group of 128 values (this lane's half
+// and the partner lane's) into LEVELS + 1 codes; value j's code goes to LDS
+// byte codes[stride * pos(j, half)].  Returns the step; *mn_out receives the
+// zero point.
 template <int LEVELS>
-__device__ __forceinline__ float quantise_group(const float (&y)[H], uint8_t* codes, int stride, float* xa,
-                                                float* xb, int i, int half, float* mn_out) {
+__device__ __forceinline__ float quantise_group(const float (&y)[H], uint8_t* codes, int stride, int half,
+                                                float* mn_out) {
   float mn = y[0], mx = y[0];
 #pragma unroll
   for (int k = 1; k < H; ++k) {
     mn = fminf(mn, y[k]);
     mx = fmaxf(mx, y[k]);
   }
-  const Halves a = exchange(xa, i, half, mn);
-  const Halves b = exchange(xb, i, half, mx);
+  const Halves a = exchange(mn);
+  const Halves b = exchange(mx);
   mn = fminf(a.left, a.right);
   mx = fmaxf(b.left, b.right);
   const float s = (mx - mn) / (float)LEVELS;
@@ -149,27 +169,22 @@ __device__ __forceinline__ float quantise_group(const float (&y)[H], uint8_t* co
 #pragma unroll
   for (int k = 0; k < H; ++k) {
     const float yc = __builtin_amdgcn_fmed3f(div_rn(y[k] - mn, s, rc), 0.0f, (float)LEVELS);
-    codes[stride * k] = s != 0.0f ? (uint8_t)__float_as_uint(yc + 12582912.0f) : (uint8_t)0;
+    codes[stride * pos(k, half)] = s != 0.0f ? (uint8_t)__float_as_uint(yc + 12582912.0f) : (uint8_t)0;
   }
   *mn_out = mn;
   return s;
 }
 
 // One tile-head side, by the 256 threads of a workgroup: token rows at
-// src + t * row_stride (binary16), codes and metadata into chunk.  `lds`
-// holds the tile (N * LDP floats) followed by two exchange arrays (2 * N
-// floats each).
+// src + t * row_stride (binary16), codes and metadata into chunk.  `tile`
+// holds N * LDP floats of LDS.
 __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stride, uint8_t* chunk, int side,
-                                           float* lds) {
-  float* tile = lds;
-  float* xa = lds + N * LDP;
-  float* xb = xa + 2 * N;
+                                           float* tile) {
   uint8_t* cb = reinterpret_cast<uint8_t*>(tile);  // codes [token][channel], after the last pass
   const int t = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int i = 64 * (wv & 1) + (t & 63);  // token row / channel column
-  const int half = wv >> 1;
-  const int o = H * half;                  // first value of this half
+  const int half = (t >> 5) & 1;
+  const int i = 32 * wv + (t & 31);  // token row / channel column
 
   // stage 1: the tile, binary16 -> binary32 (exact), coalesced 16-byte loads
 #pragma unroll 4
@@ -187,34 +202,34 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
   for (int it = 0; it < kSweeps; ++it) {
     // token pass (token row i, this half); stage 2 on the first visit
 #pragma unroll
-    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + o + j];
+    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + pos(j, half)];
     if (it == 0) {
       // stages h = 1 .. 32 in registers, stage 64 across the halves:
       // (a, b) -> (a + b, a - b) with a in the left half, b in the right
-      rotate_half(y);
+      rotate_half(y, half);
 #pragma unroll
-      for (int j = 0; j < H; ++j) tile[i * LDP + o + j] = y[j];
+      for (int j = 0; j < H; ++j) tile[i * LDP + pos(j, half)] = y[j];
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < H; ++j) {
-        const float z = tile[i * LDP + (H - o) + j];
+        const float z = tile[i * LDP + partner_pos(j, half)];
         y[j] = half == 0 ? y[j] + z : z - y[j];
       }
 #pragma unroll
       for (int j = 0; j < H; ++j) y[j] = y[j] * kInvSqrt128;
       __syncthreads();  // both halves have read their partner's values
     }
-    r = r * normalise(y, xa, xb, i, half);
+    r = r * normalise(y);
 #pragma unroll
-    for (int j = 0; j < H; ++j) tile[i * LDP + o + j] = y[j];
+    for (int j = 0; j < H; ++j) tile[i * LDP + pos(j, half)] = y[j];
     __syncthreads();
     // channel pass (channel column i, this half)
 #pragma unroll
-    for (int k = 0; k < H; ++k) y[k] = tile[(o + k) * LDP + i];
-    c = c * normalise(y, xa, xb, i, half);
+    for (int k = 0; k < H; ++k) y[k] = tile[pos(k, half) * LDP + i];
+    c = c * normalise(y);
     if (it + 1 < kSweeps) {
 #pragma unroll
-      for (int k = 0; k < H; ++k) tile[(o + k) * LDP + i] = y[k];
+      for (int k = 0; k < H; ++k) tile[pos(k, half) * LDP + i] = y[k];
       __syncthreads();
     }
   }
@@ -224,7 +239,7 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
     // keys: 4-bit codes per channel over the tile's tokens
     __syncthreads();  // every column has been read: the tile memory is free
     float mn;
-    const float s = quantise_group<15>(y, cb + o * N + i, N, xa, xb, i, half, &mn);
+    const float s = quantise_group<15>(y, cb + i, N, half, &mn);
     if (half == 0) {
       meta[i] = c * s;
       meta[N + i] = c * mn;
@@ -248,13 +263,13 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
   } else {
     // values: back to token rows, 2-bit codes per token over the channels
 #pragma unroll
-    for (int k = 0; k < H; ++k) tile[(o + k) * LDP + i] = y[k];
+    for (int k = 0; k < H; ++k) tile[pos(k, half) * LDP + i] = y[k];
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + o + j];
+    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + pos(j, half)];
     __syncthreads();  // every row has been read: the tile memory is free
     float mn;
-    const float s = quantise_group<3>(y, cb + i * N + o, 1, xa, xb, i, half, &mn);
+    const float s = quantise_group<3>(y, cb + i * N, 1, half, &mn);
     if (half == 0) {
       meta[i] = r * s;
       meta[N + i] = r * mn;
@@ -279,7 +294,7 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
   }
 }
 
-constexpr int kLdsFloats = N * LDP + 4 * N;
+constexpr int kLdsFloats = N * LDP;
 
 // Contract violations found in device-resident arguments (KVQ_DEVERR_* bits of
 // kvq.h), one word per device: raised with a vector atomic OR, read and

@@ -19,7 +19,7 @@ MUTANTS = [
     ("nvfp4_block_max_to_4", "kvqo_e4m3_encode((a / 6.0f) / st)", "kvqo_e4m3_encode((a / 4.0f) / st)", 0,
      [pins.pin_nvfp4]),
     ("wht_sign", "y[j + h] = a - b;", "y[j + h] = b - a;", 0, [pins.pin_kvarn_rotation]),
-    ("kvarn_no_channel_division", "for (int t = 0; t < N; t++) Y[t * N + j] = Y[t * N + j] / sd;",
+    ("kvarn_no_channel_division", "for (int t = 0; t < N; t++) Y[t * N + j] = Y[t * N + j] * inv;",
      "(void)0;", 0, [pins.pin_kvarn_tile]),
     ("kvarn_dev_scale", "float sd = sqrtf(sum_tree(sq, 128) * 0.0078125f);",
      "float sd = sqrtf(sum_tree(sq, 128) * 0.015625f);", 0, [pins.pin_kvarn_tile]),
