@@ -26,20 +26,21 @@
 // correctly rounded division and square root), so the codes and metadata are
 // a deterministic function of the binary16 input.
 //
-// Mapping.  One workgroup of 256 threads (4 wavefronts) per (tile, kv head,
+// Mapping.  One workgroup of 512 threads (8 wavefronts) per (tile, kv head,
 // side).  The tile lives in LDS as binary32 with rows padded to 129 words.
-// Lanes l and l + 32 of wavefront w share index i = 32 w + (l & 31): the
-// lower lane holds the left half [0, 64) of token row i in a token pass and
-// of channel column i in a channel pass, the upper lane the right half
-// [64, 128).  A 128-value sum is the canonical tree of its two 64-value
-// halves, S = S(left) + S(right): each lane sums its half in registers and
-// v_permlane32_swap hands both halves' sums to both lanes, with no LDS round
-// trip or barrier.  The upper lane keeps its 64 values rotated by 32 in its
-// registers: value j is element (j + 32) mod 64 of its half.  That leaves
-// every sum unchanged (it swaps the two 32-value subtrees of the half's tree,
-// and binary32 addition commutes) and makes both access patterns free of LDS
-// bank conflicts (the two lanes of a pair sit 32 banks apart).  Two
-// workgroups fit the LDS of a compute unit: 8 wavefronts.
+// Lanes l, l + 16, l + 32 and l + 48 of wavefront w share index
+// i = 16 w + (l & 15); quarter q = (l >> 4) & 3 holds elements
+// [32 q, 32 q + 32) of token row i in a token pass and of channel column i
+// in a channel pass.  A 128-value sum is the canonical tree
+// (S0 + S1) + (S2 + S3) of its quarters' sums: each lane sums its quarter in
+// registers, v_permlane16_swap and then v_permlane32_swap hand the partial
+// sums across, with no LDS round trip or barrier.  Quarters 1 and 2 keep
+// their values rotated by 16 in their registers.  That leaves every sum
+// unchanged (it swaps the two 16-value subtrees of the quarter's tree, and
+// binary32 addition commutes) and puts a row's four quarters 0, 48, 16 and 32
+// banks apart (mod 64), so row and column accesses are free of LDS bank
+// conflicts.  Two workgroups fit the LDS of a compute unit: 16 wavefronts,
+// four per SIMD.
 #include "kvq.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -59,52 +60,61 @@ constexpr int kMeta = kVCodes + 128 * 32;
 constexpr int kTileBytes = kMeta + 4 * 6 * 128;  // 15360; a page of P tokens holds P / 128 tiles
 static_assert(kTileBytes == 15360, "KVarN tile size");
 
-constexpr int H = N / 2;  // values per thread and pass
+constexpr int kThreads = 512;
+constexpr int Q = N / 4;  // values per lane and pass: a quarter of a row or column
 
-// Balanced pairwise sum of 64 values in index order (one half of the
+// Balanced pairwise sum of 32 values in index order (one quarter of the
 // canonical 128-value tree).
-__device__ __forceinline__ float tree_sum64(const float (&v)[H]) {
-  float t[H / 2];
+__device__ __forceinline__ float tree_sum32(const float (&v)[Q]) {
+  float t[Q / 2];
 #pragma unroll
-  for (int i = 0; i < H / 2; ++i) t[i] = v[2 * i] + v[2 * i + 1];
+  for (int i = 0; i < Q / 2; ++i) t[i] = v[2 * i] + v[2 * i + 1];
 #pragma unroll
-  for (int w = H / 4; w >= 1; w >>= 1)
+  for (int w = Q / 4; w >= 1; w >>= 1)
 #pragma unroll
     for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
   return t[0];
 }
 
-// The two halves' partial results for index i, from lanes l and l + 32:
-// returns the left half's and the right half's values in both lanes.
-struct Halves {
-  float left, right;
+// The four quarters' partial values p0..p3 of one row or column, held by
+// lanes l, l + 16, l + 32 and l + 48, combined as op(op(p0, p1), op(p2, p3))
+// -- the top two levels of the canonical tree -- in all four lanes.
+template <class Op>
+__device__ __forceinline__ float combine4(float v, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float pair = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+struct Add {
+  __device__ float operator()(float a, float b) const { return a + b; }
 };
-__device__ __forceinline__ Halves exchange(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return Halves{__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
+struct Min {
+  __device__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+struct Max {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
 
-// Column within the row (row within the column) of value j of this lane's
-// half, the right half rotated by 32.
-__device__ __forceinline__ int pos(int j, int half) { return j < 32 ? j + 96 * half : j + 32 * half; }
-// ... and of the same element of the other half.
-__device__ __forceinline__ int partner_pos(int j, int half) {
-  return j < 32 ? j + 64 - 32 * half : j + 64 - 96 * half;
-}
+// Quarters 1 and 2 keep their 32 values rotated by 16 in their lane's
+// registers (register j holds element (j + 16) mod 32 of the quarter);
+// quarters 0 and 3 keep them in order.
+__device__ __forceinline__ int rho(int q) { return 16 * ((q ^ (q >> 1)) & 1); }
+// Column within the row (row within the column) of register j of quarter q.
+__device__ __forceinline__ int pos(int j, int q) { return j < 16 ? 32 * q + j + rho(q) : 32 * q + j - rho(q); }
 
-// Population standard deviation of 128 values (this thread's half v and the
-// partner's); a zero or non-finite result becomes 1.
-__device__ __forceinline__ float deviation(const float (&v)[H]) {
-  const Halves s = exchange(tree_sum64(v));
-  const float mean = (s.left + s.right) * 0.0078125f;
-  float sq[H];
+// Population standard deviation of 128 values (this lane's quarter v and
+// the three partner lanes'); a zero or non-finite result becomes 1.
+__device__ __forceinline__ float deviation(const float (&v)[Q]) {
+  const float mean = combine4(tree_sum32(v), Add{}) * 0.0078125f;
+  float sq[Q];
 #pragma unroll
-  for (int k = 0; k < H; ++k) {
+  for (int k = 0; k < Q; ++k) {
     const float d = v[k] - mean;
     sq[k] = d * d;
   }
-  const Halves q = exchange(tree_sum64(sq));
-  float sd = __builtin_sqrtf((q.left + q.right) * 0.0078125f);
+  float sd = __builtin_sqrtf(combine4(tree_sum32(sq), Add{}) * 0.0078125f);
   if (!(sd > 0.0f) || !__builtin_isfinite(sd)) sd = 1.0f;
   return sd;
 }
@@ -112,70 +122,76 @@ __device__ __forceinline__ float deviation(const float (&v)[H]) {
 // Scale the 128 values by RN(1 / deviation) (one rounding of the reciprocal,
 // one of each product; the sign of zero carries through the product);
 // returns the deviation.
-__device__ __forceinline__ float normalise(float (&v)[H]) {
+__device__ __forceinline__ float normalise(float (&v)[Q]) {
   const float sd = deviation(v);
   const float inv = 1.0f / sd;
 #pragma unroll
-  for (int k = 0; k < H; ++k) v[k] = v[k] * inv;
+  for (int k = 0; k < Q; ++k) v[k] = v[k] * inv;
   return sd;
 }
 
-// Butterfly stages h = 1 .. 32 of the rotation on this lane's half.  Stages
-// below 32 stay inside each 32-value block, so the right half's rotated order
-// does not matter to them; stage 32 puts each pair's sum and difference at
-// the registers of their own elements.
-__device__ __forceinline__ void rotate_half(float (&y)[H], int half) {
+// Butterfly stages h = 1 .. 16 of the rotation on this lane's quarter.
+// Stages below 16 stay inside each 16-value block, so a rotated quarter's
+// order does not matter to them; stage 16 puts each pair's sum and
+// difference at the registers of their own elements.  a +- b is formed as
+// fma(+-1, b, a): the product is exact, so the one rounding is that of the
+// sum or difference, signed zeros included.
+__device__ __forceinline__ void rotate_quarter(float (&y)[Q], bool rotated) {
 #pragma unroll
-  for (int h = 1; h < H / 2; h <<= 1)
+  for (int h = 1; h < Q / 2; h <<= 1)
 #pragma unroll
-    for (int j = 0; j < H; ++j)
+    for (int j = 0; j < Q; ++j)
       if ((j & h) == 0) {
         const float p = y[j], q = y[j + h];
         y[j] = p + q;
         y[j + h] = p - q;
       }
+  // in order: register j holds element j, register j + 16 element j + 16
+  // (sum to j, difference to j + 16); rotated: the reverse
+  const float sg = rotated ? -1.0f : 1.0f;
 #pragma unroll
-  for (int j = 0; j < H / 2; ++j) {
-    // left half: p = element j, q = element j + 32; right half: the reverse
-    const float p = y[j], q = y[j + H / 2];
-    const float sum = p + q;
-    y[j] = half == 0 ? sum : q - p;
-    y[j + H / 2] = half == 0 ? p - q : sum;
+  for (int j = 0; j < Q / 2; ++j) {
+    const float u = rotated ? y[j + Q / 2] : y[j];  // element j
+    const float v = rotated ? y[j] : y[j + Q / 2];  // element j + 16
+    y[j] = __builtin_fmaf(sg, v, u);
+    y[j + Q / 2] = __builtin_fmaf(-sg, v, u);
   }
 }
 
-// Asymmetric round-to-nearest of one group of 128 values (this lane's half
-// and the partner lane's) into LEVELS + 1 codes; value j's code goes to LDS
-// byte codes[stride * pos(j, half)].  Returns the step; *mn_out receives the
-// zero point.
+// Asymmetric round-to-nearest of one group of 128 values (this lane's
+// quarter and the partner lanes') into LEVELS + 1 codes; register j's code
+// goes to LDS byte codes[stride * pos(j, q)].  Returns the step; *mn_out
+// receives the zero point.
 template <int LEVELS>
-__device__ __forceinline__ float quantise_group(const float (&y)[H], uint8_t* codes, int stride, int half,
+__device__ __forceinline__ float quantise_group(const float (&y)[Q], uint8_t* codes, int stride, int q,
                                                 float* mn_out) {
   float mn = y[0], mx = y[0];
 #pragma unroll
-  for (int k = 1; k < H; ++k) {
+  for (int k = 1; k < Q; ++k) {
     mn = fminf(mn, y[k]);
     mx = fmaxf(mx, y[k]);
   }
-  const Halves a = exchange(mn);
-  const Halves b = exchange(mx);
-  mn = fminf(a.left, a.right);
-  mx = fmaxf(b.left, b.right);
+  mn = combine4(mn, Min{});
+  mx = combine4(mx, Max{});
   const float s = (mx - mn) / (float)LEVELS;
-  const Recip rc = make_recip(s);
+  // A zero step (all values equal, or a range so small that range / LEVELS
+  // rounds to zero) gives code 0 throughout; dividing by 1 instead does that
+  // with no select per value, since every y - mn is then below 1/2.
+  const float sdiv = s != 0.0f ? s : 1.0f;
+  const Recip rc = make_recip(sdiv);
   // clip(rne(.), 0, LEVELS): the clamp first (integer bounds, so it commutes
   // with the rounding), then adding 1.5 * 2^23 rounds to an integer with ties
   // to even and leaves it in the sum's low mantissa bits
 #pragma unroll
-  for (int k = 0; k < H; ++k) {
-    const float yc = __builtin_amdgcn_fmed3f(div_rn(y[k] - mn, s, rc), 0.0f, (float)LEVELS);
-    codes[stride * pos(k, half)] = s != 0.0f ? (uint8_t)__float_as_uint(yc + 12582912.0f) : (uint8_t)0;
+  for (int k = 0; k < Q; ++k) {
+    const float yc = __builtin_amdgcn_fmed3f(div_rn(y[k] - mn, sdiv, rc), 0.0f, (float)LEVELS);
+    codes[stride * pos(k, q)] = (uint8_t)__float_as_uint(yc + 12582912.0f);
   }
   *mn_out = mn;
   return s;
 }
 
-// One tile-head side, by the 256 threads of a workgroup: token rows at
+// One tile-head side, by the 512 threads of a workgroup: token rows at
 // src + t * row_stride (binary16), codes and metadata into chunk.  `tile`
 // holds N * LDP floats of LDS.
 __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stride, uint8_t* chunk, int side,
@@ -183,53 +199,57 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
   uint8_t* cb = reinterpret_cast<uint8_t*>(tile);  // codes [token][channel], after the last pass
   const int t = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int half = (t >> 5) & 1;
-  const int i = 32 * wv + (t & 31);  // token row / channel column
+  const int q = (t >> 4) & 3;        // quarter: elements [32 q, 32 q + 32)
+  const int i = 16 * wv + (t & 15);  // token row / channel column
 
   // stage 1: the tile, binary16 -> binary32 (exact), coalesced 16-byte loads
-#pragma unroll 4
-  for (int k = 0; k < 8; ++k) {
-    const int p = t + 256 * k, row = p >> 4, c8 = (p & 15) * 8;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int p = t + kThreads * k, row = p >> 4, c8 = (p & 15) * 8;
     const half8_t x = *reinterpret_cast<const half8_t*>(src + row * row_stride + c8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) tile[row * LDP + c8 + e] = (float)x[e];
   }
   __syncthreads();
 
-  float y[H];
+  float y[Q];
   float r = 1.0f, c = 1.0f;  // running token factor r_i, channel factor c_i
 #pragma unroll 1
   for (int it = 0; it < kSweeps; ++it) {
-    // token pass (token row i, this half); stage 2 on the first visit
+    // token pass (token row i, this quarter); stage 2 on the first visit
 #pragma unroll
-    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + pos(j, half)];
+    for (int j = 0; j < Q; ++j) y[j] = tile[i * LDP + pos(j, q)];
     if (it == 0) {
-      // stages h = 1 .. 32 in registers, stage 64 across the halves:
-      // (a, b) -> (a + b, a - b) with a in the left half, b in the right
-      rotate_half(y, half);
+      // stages h = 1 .. 16 in registers; stages 32 and 64 across the
+      // quarters through the tile: with a0..a3 the elements e, e + 32,
+      // e + 64, e + 96 after stage 16, quarter k takes
+      // (a0 +- a1) +- (a2 +- a3), the inner sign minus for odd k, the outer
+      // for k >= 2, each as fma(+-1, b, a)
+      rotate_quarter(y, rho(q) != 0);
 #pragma unroll
-      for (int j = 0; j < H; ++j) tile[i * LDP + pos(j, half)] = y[j];
+      for (int j = 0; j < Q; ++j) tile[i * LDP + pos(j, q)] = y[j];
       __syncthreads();
+      const float s1 = (q & 1) ? -1.0f : 1.0f, s2 = (q & 2) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int j = 0; j < H; ++j) {
-        const float z = tile[i * LDP + partner_pos(j, half)];
-        y[j] = half == 0 ? y[j] + z : z - y[j];
+      for (int j = 0; j < Q; ++j) {
+        const float* a = tile + i * LDP + (pos(j, q) - 32 * q);
+        const float lower = __builtin_fmaf(s1, a[32], a[0]);
+        const float upper = __builtin_fmaf(s1, a[96], a[64]);
+        y[j] = __builtin_fmaf(s2, upper, lower) * kInvSqrt128;
       }
-#pragma unroll
-      for (int j = 0; j < H; ++j) y[j] = y[j] * kInvSqrt128;
-      __syncthreads();  // both halves have read their partner's values
+      __syncthreads();  // every quarter has read the others' values
     }
     r = r * normalise(y);
 #pragma unroll
-    for (int j = 0; j < H; ++j) tile[i * LDP + pos(j, half)] = y[j];
+    for (int j = 0; j < Q; ++j) tile[i * LDP + pos(j, q)] = y[j];
     __syncthreads();
-    // channel pass (channel column i, this half)
+    // channel pass (channel column i, this quarter)
 #pragma unroll
-    for (int k = 0; k < H; ++k) y[k] = tile[pos(k, half) * LDP + i];
+    for (int k = 0; k < Q; ++k) y[k] = tile[pos(k, q) * LDP + i];
     c = c * normalise(y);
     if (it + 1 < kSweeps) {
 #pragma unroll
-      for (int k = 0; k < H; ++k) tile[pos(k, half) * LDP + i] = y[k];
+      for (int k = 0; k < Q; ++k) tile[pos(k, q) * LDP + i] = y[k];
       __syncthreads();
     }
   }
@@ -239,17 +259,16 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
     // keys: 4-bit codes per channel over the tile's tokens
     __syncthreads();  // every column has been read: the tile memory is free
     float mn;
-    const float s = quantise_group<15>(y, cb + i, N, half, &mn);
-    if (half == 0) {
+    const float s = quantise_group<15>(y, cb + i, N, q, &mn);
+    if (q == 0) {
       meta[i] = c * s;
       meta[N + i] = c * mn;
       meta[2 * N + i] = r;
     }
     __syncthreads();
     // pack: output byte t*64 + j/2 holds channel j (low nibble) and j+1
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int o0 = 16 * (t + 256 * k);
+    {
+      const int o0 = 16 * t;
       const uint32_t* w = reinterpret_cast<const uint32_t*>(cb + (o0 >> 6) * N + 2 * (o0 & 63));
       uint32_t out[4];
 #pragma unroll
@@ -263,21 +282,21 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
   } else {
     // values: back to token rows, 2-bit codes per token over the channels
 #pragma unroll
-    for (int k = 0; k < H; ++k) tile[pos(k, half) * LDP + i] = y[k];
+    for (int k = 0; k < Q; ++k) tile[pos(k, q) * LDP + i] = y[k];
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < H; ++j) y[j] = tile[i * LDP + pos(j, half)];
+    for (int j = 0; j < Q; ++j) y[j] = tile[i * LDP + pos(j, q)];
     __syncthreads();  // every row has been read: the tile memory is free
     float mn;
-    const float s = quantise_group<3>(y, cb + i * N, 1, half, &mn);
-    if (half == 0) {
+    const float s = quantise_group<3>(y, cb + i * N, 1, q, &mn);
+    if (q == 0) {
       meta[i] = r * s;
       meta[N + i] = r * mn;
       meta[2 * N + i] = c;
     }
     __syncthreads();
     // pack: output byte 128*(t/4) + j holds token 4*(t/4) + k in bits 2k..2k+1
-    {
+    if (t < 256) {
       const int o0 = 16 * t;
       const int quad = o0 >> 7, j0 = o0 & 127;
       uint32_t out[4];
@@ -285,8 +304,8 @@ __device__ __forceinline__ void kvarn_tile(const uint16_t* src, int64_t row_stri
       for (int m = 0; m < 4; ++m) {
         uint32_t v = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v |= *reinterpret_cast<const uint32_t*>(cb + (4 * quad + q) * N + j0 + 4 * m) << (2 * q);
+        for (int k = 0; k < 4; ++k)
+          v |= *reinterpret_cast<const uint32_t*>(cb + (4 * quad + k) * N + j0 + 4 * m) << (2 * k);
         out[m] = v;
       }
       *reinterpret_cast<uint4*>(chunk + kVCodes + o0) = uint4{out[0], out[1], out[2], out[3]};
@@ -303,7 +322,7 @@ __device__ uint32_t g_device_errors;
 
 __device__ __forceinline__ void raise_error(uint32_t bit) { atomicOr(&g_device_errors, bit); }
 
-__global__ __launch_bounds__(256) void kvarn_write_kernel(WriteArgs a) {
+__global__ __launch_bounds__(kThreads) void kvarn_write_kernel(WriteArgs a) {
   __shared__ float lds[kLdsFloats];
   const int ti = blockIdx.x, h = blockIdx.y, side = blockIdx.z;
   // The run's first slot places the tile: one outside the pool skips it (as
@@ -350,7 +369,7 @@ __global__ __launch_bounds__(64) void kvarn_append_kernel(KvarnAppendArgs a) {
 
 // Tile completion: a token at position 127 mod 128 completes its sequence's
 // tile, which is quantised from the tail into the page of that tile.
-__global__ __launch_bounds__(256) void kvarn_complete_kernel(KvarnAppendArgs a) {
+__global__ __launch_bounds__(kThreads) void kvarn_complete_kernel(KvarnAppendArgs a) {
   __shared__ float lds[kLdsFloats];
   const int64_t i = blockIdx.x;
   const int h = blockIdx.y, side = blockIdx.z;
@@ -384,7 +403,7 @@ hipError_t launch_kvarn_write(const WriteArgs& a, hipStream_t s) {
   const int64_t tiles = a.n_tok / N;
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidValue;
-  kvarn_write_kernel<<<dim3((unsigned)tiles, (unsigned)a.H, 2u), 256, 0, s>>>(a);
+  kvarn_write_kernel<<<dim3((unsigned)tiles, (unsigned)a.H, 2u), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -394,7 +413,7 @@ hipError_t launch_kvarn_append(const KvarnAppendArgs& a, hipStream_t s) {
   kvarn_append_kernel<<<dim3((unsigned)a.n_tok, (unsigned)(2 * a.H)), 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  kvarn_complete_kernel<<<dim3((unsigned)a.n_tok, (unsigned)a.H, 2u), 256, 0, s>>>(a);
+  kvarn_complete_kernel<<<dim3((unsigned)a.n_tok, (unsigned)a.H, 2u), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
