@@ -17,11 +17,14 @@ Also reported on the same line:
   write_mtok_s   whole-context quantise-on-write throughput (tokens/s / 1e6)
   roofline       the step's decode call (split kernel, which also writes and
                  attends the new tokens, plus the merge): algorithmic KV bytes
-                 per call / mean call duration (HIP events around each call, on the launch
-                 stream, over an instrumented pass of as many steps right
-                 after the timed ones: an event recorded between two launches
-                 holds the next one back by a few microseconds, so the timed
-                 steps carry only the pair around all of them) against 8 TB/s
+                 per call / mean call duration against 8 TB/s.  The duration
+                 is the timed region's (one HIP event pair on the launch
+                 stream around all the steps) per step, one call per step;
+                 `event_timed_call_us` adds the distribution of an
+                 instrumented pass right after, with an event pair around
+                 each call (an event recorded between two launches holds the
+                 next one back, so those read ~2 us long).  A KVarN step also
+                 appends, so KVarN entries take the per-call events
   copy           a 1 GiB device-to-device copy (read + write bytes / time):
                  the achievable bandwidth beside the specification
   roofline.access_pattern_floor, formats.*.read_floor_gbs
@@ -270,6 +273,18 @@ class Problem:
         d = self.dec_ms
         pick = lambda f: round(d[min(len(d) - 1, int(f * len(d)))] * 1e3, 2)
         return {"p10_us": pick(0.1), "p50_us": pick(0.5), "p90_us": pick(0.9)}
+
+    def call_ms(self, ms_step, ms_dec):
+        """Mean duration of the decode call.  Every format but KVarN runs one
+        call per step, so it is the timed region's time per step (one event
+        pair around all the steps).  A KVarN step also appends through the
+        tail, so its decode call is timed by the instrumented pass's event
+        pairs, which hold each next launch back and read ~2 us long."""
+        return ms_dec if self.kvarn else ms_step
+
+    def call_timing(self):
+        return ("HIP event pair around each decode call (instrumented steps)" if self.kvarn
+                else "HIP event pair around the timed steps, one decode call per step")
 
 
 _READ_PROBE = None
@@ -523,9 +538,10 @@ def main():
     floor_gbs, floor_us = pb.time_read_floor()
     log(f"[bench] access-pattern read floor: {floor_us:.1f} us ({floor_gbs:.0f} GB/s)")
     value = pb.kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = pb.call_kv_bytes / (ms_dec * 1e-3) / 1e9
-    log(f"[bench] step {ms_step * 1e3:.1f} us ({value:.0f} GB/s), decode launch {ms_dec * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s, {achieved / HBM_PEAK_GBS:.1%} of peak)")
+    ms_call = pb.call_ms(ms_step, ms_dec)
+    achieved = pb.call_kv_bytes / (ms_call * 1e-3) / 1e9
+    log(f"[bench] step {ms_step * 1e3:.1f} us ({value:.0f} GB/s), decode call {ms_call * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s, {achieved / HBM_PEAK_GBS:.1%} of peak); per-call events {ms_dec * 1e3:.1f} us")
     sp, w = pb.sp, pb.w
     result = {
         "metric": METRIC,
@@ -561,8 +577,11 @@ def main():
             "kernel": decode_kernel_name(pb),
             "algorithmic_bytes": pb.call_kv_bytes, "traffic_unit": "HBM bytes per decode call (rocprofv3 "
             "FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a 1 GiB device copy)",
-            "mean_launch_us": round(ms_dec * 1e3, 2),
-            **pb.dec_percentiles_us(),
+            "mean_launch_us": round(ms_call * 1e3, 2), "timing": pb.call_timing(),
+            # the instrumented pass right after the timed steps: an event pair
+            # around each call (upper bounds: an event between two launches
+            # holds the next one back)
+            "event_timed_call_us": {"mean": round(ms_dec * 1e3, 2), **pb.dec_percentiles_us()},
             # the same pages read whole with no arithmetic (libkvq_probe.so):
             # the access pattern's own ceiling beside the 8 TB/s specification
             "access_pattern_floor": {"gbs": round(floor_gbs, 1), "us": round(floor_us, 2),
@@ -589,9 +608,12 @@ def main():
             ms_s, ms_d = p.time_steps(max(20, args.steps // 2), args.warmup)
             fl_gbs, _ = p.time_read_floor()
             key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "") + ("_tp2_share" if name.endswith("_tp2") else "")
-            fmts[key] = {"workload": name, "decode_gbs": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9, 1),
-                         "decode_frac_of_peak": round(p.call_kv_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "decode_us": round(ms_d * 1e3, 2), **p.dec_percentiles_us(), "step_us": round(ms_s * 1e3, 2),
+            ms_c = p.call_ms(ms_s, ms_d)
+            fmts[key] = {"workload": name, "decode_gbs": round(p.call_kv_bytes / (ms_c * 1e-3) / 1e9, 1),
+                         "decode_frac_of_peak": round(p.call_kv_bytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "decode_us": round(ms_c * 1e3, 2), "decode_timing": p.call_timing(),
+                         "event_timed_call_us": {"mean": round(ms_d * 1e3, 2), **p.dec_percentiles_us()},
+                         "step_us": round(ms_s * 1e3, 2),
                          "write_mtok_s": round(wm, 1),
                          "write_frac_of_peak": round(write_bytes(p) / (wms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(entry_key(K, name, fmt, flags)),
