@@ -435,6 +435,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   float* partials = reinterpret_cast<float*>(a.workspace);
   const int64_t rec_floats = ws_record_floats(D);
 
+  // The first chunk's block-table entries are requested before the context
+  // length arrives: entries p_begin .. p_begin + 255 of the split lie inside
+  // the table's row whatever the length is, so the two round trips overlap.
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_pages;
+  const int first_cap = min(kPageChunk, min(a.pages_per_split, a.max_pages - split * a.pages_per_split));
+  const int bt_first = tid < first_cap ? bt[split * a.pages_per_split + tid] : 0;
+
   // wave-uniform bounds (kept in scalar registers)
   int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * P ? a.max_pages * P : ctx);
@@ -497,7 +504,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   const LaneOffs lofs = lane_offsets<FMT, D>(gq, n, P);
   const int sp_shift = a.sp_shift;  // P / 16 == 1 << sp_shift
   const int sp_mask = (1 << sp_shift) - 1;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_pages;
   const uint8_t* head_base = a.cache + (int64_t)kvh * a.geom.chunk_bytes;
   const int64_t page_stride = (int64_t)a.H * a.geom.chunk_bytes;
 
@@ -506,9 +512,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
   // Reading a page index from LDS involves no vector-memory counter, so it
   // never forces a wait on the data loads in flight.
   for (int c0 = p_begin; c0 < p_end; c0 += kPageChunk) {
-    const int nc = min(kPageChunk, p_end - c0);
+    const int nc = min(kPageChunk, p_end - c0);  // <= first_cap for the first chunk
+    static_assert(NT >= kPageChunk, "one block-table entry per thread and chunk");
     __syncthreads();
-    for (int i = tid; i < nc; i += NT) s_pages[i] = bt[c0 + i];
+    if (tid < nc) {
+      if (c0 == p_begin)  // uniform
+        s_pages[tid] = bt_first;
+      else
+        s_pages[tid] = bt[c0 + tid];
+    }
     __syncthreads();
     const int nj = w < nc ? (nc - w + W - 1) / W : 0;  // this wave's pages
     const int nu = nj << sp_shift;

@@ -227,10 +227,18 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   const int S = a.num_splits;
   const int64_t rec_floats = ws_record_floats(D);
 
-  int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
-  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
   // the walk is over 128-token tiles; a page of a.P tokens holds a.P / 128
   const int tshift = a.P == 256 ? 1 : 0;
+  // The first chunk's block-table entries are requested before the context
+  // length arrives: tiles p_begin .. p_begin + 255 of the split lie inside the
+  // table's row whatever the length is, so the two round trips overlap.
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_pages;
+  const int t_first = split * a.pages_per_split;
+  const int first_cap = min(kPageChunk, min(a.pages_per_split, (a.max_pages << tshift) - t_first));
+  const int bt_first = tid < first_cap ? bt[(t_first + tid) >> tshift] : 0;
+
+  int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
   const int n_pages = ctx / P;  // complete tiles; the rest is the caller's tail
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(p_begin + a.pages_per_split, n_pages);
@@ -272,16 +280,21 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
   st.m_run = kNegInf;
   st.l_run = 0.0f;
 
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_pages;
   const uint8_t* head_base = a.cache + (int64_t)kvh * a.geom.chunk_bytes;
   const int64_t page_stride = (int64_t)a.H * a.geom.chunk_bytes;
   float* mt = s_meta[w];
   const LaneOffs lofs = lane_offsets(n, gq);
 
   for (int c0 = p_begin; c0 < p_end; c0 += kPageChunk) {
-    const int nc = min(kPageChunk, p_end - c0);
+    const int nc = min(kPageChunk, p_end - c0);  // <= first_cap for the first chunk
+    static_assert(kPageChunk <= 256, "one block-table entry per thread and chunk");
     __syncthreads();
-    for (int i = tid; i < nc; i += 256) s_pages[i] = bt[(c0 + i) >> tshift];
+    if (tid < nc) {
+      if (c0 == p_begin)  // uniform
+        s_pages[tid] = bt_first;
+      else
+        s_pages[tid] = bt[(c0 + tid) >> tshift];
+    }
     __syncthreads();
     const int nj = w < nc ? (nc - w + kWaves - 1) / kWaves : 0;
     if (nj == 0) continue;
