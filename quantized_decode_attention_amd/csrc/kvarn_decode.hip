@@ -34,6 +34,7 @@ constexpr int D = 128;
 constexpr int P = 128;
 constexpr int kUnits = P / 16;
 constexpr int kRing = 4;  // sub-page buffers per wave (kRing - 1 in flight)
+constexpr int kMergeWaves = 8;  // merge: wave w attends tail rows 16w .. 16w + 15 and finishes head w
 constexpr int kVCodes = P * D / 2;          // V codes [32][128] 2-bit
 constexpr int kMeta = kVCodes + P * D / 4;  // binary32 metadata
 constexpr int kMetaFloats = 3 * D + 3 * P;
@@ -472,21 +473,22 @@ __global__ __launch_bounds__(256) void kvarn_decode_kernel(DecodeArgs a) {
 // rotation back:
 //   M = max(m_s, m_tail), L = sum 2^(m_s-M) l_s + 2^(m_tail-M) l_tail,
 //   o = ( H sum 2^(m_s-M) o_s + 2^(m_tail-M) o_tail ) / L.
-// Four waves.  The tail is read once for the whole group: wave w attends
-// tail rows 16w .. 16w+15 and 16(w+4) .. 16(w+4)+15 with the same two MFMA
-// products as the split kernel's sub-pages (K as the A operand of S^T = K Q^T,
-// P as the A operand of O = P V), K, V and q entering as the binary16 values
-// they are and P as binary16 high halves plus remainders.  A wave first takes
-// the maximum of its 32 scores per head, so every weight is at most 1 and no
-// rescale is needed.  The waves' partials meet in LDS.  Then wave w finishes
-// heads w, w+4: lane l holds channels l and l+64, merges the split records
-// for them, applies the inverse rotation (in-lane stage 64, shuffles for the
-// others) and adds the tail.
+// Eight waves.  The tail is read once for the whole group: wave w attends
+// tail rows 16w .. 16w+15 with the same two MFMA products as the split
+// kernel's sub-pages (K as the A operand of S^T = K Q^T, P as the A operand
+// of O = P V), K, V and q entering as the binary16 values they are and P as
+// binary16 high halves plus remainders.  A wave first takes the maximum of
+// its 16 scores per head, so every weight is at most 1 and no rescale is
+// needed.  The waves' partials meet in LDS.  Then wave w finishes head w:
+// lane l holds channels l and l+64, merges the split records for them,
+// applies the inverse rotation (in-lane stage 64, shuffles for the others)
+// and adds the tail.
 template <int G>
-__global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
-  __shared__ float lds_o[kWaves][2 * G][D];
-  __shared__ float lds_m[kWaves][16];
-  __shared__ float lds_l[kWaves][16];
+__global__ __launch_bounds__(64 * kMergeWaves) void kvarn_merge_kernel(DecodeArgs a) {
+  constexpr int MW = kMergeWaves;
+  __shared__ float lds_o[MW][2 * G][D];
+  __shared__ float lds_m[MW][16];
+  __shared__ float lds_l[MW][16];
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, l = tid & 63, n = l & 15, gq = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -496,13 +498,13 @@ __global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * a.P ? a.max_pages * a.P : ctx);
   const int n_tail = a.tail ? ctx % P : 0;
 
-  // the first 8 split records of the wave's heads, requested before the
+  // the first 8 split records of the wave's head, requested before the
   // tail is read so both round trips overlap
   const float* recs = reinterpret_cast<const float*>(a.workspace) + ((int64_t)b * a.H + kvh) * S * rf;
-  RecGroup rg[2][2];  // [head w + 4j][channel l, l + 64]
+  RecGroup rg[1][2];  // [head w][channel l, l + 64]
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int g = w + kWaves * j;
+  for (int j = 0; j < 1; ++j) {
+    const int g = w + MW * j;
     if (g < G) {  // uniform per wave
       load_recs(recs, rf, S, 0, g, 2 * kMaxGroup + g * D + l, rg[j][0]);
       load_recs(recs, rf, S, 0, g, 2 * kMaxGroup + g * D + l + 64, rg[j][1]);
@@ -524,13 +526,13 @@ __global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
         qB[kk] = n < G ? v : z;
       }
     }
-    // rows 16u + n (K: channels 32 gq .. +31) and 16u + 4 gq + i (V:
-    // channels 8n .. 8n+7) of the wave's two sub-pages; every row below 128
-    // is inside the tail buffer, rows at or past the tail length get weight 0
-    half8_t kr[2][4], vr[2][4];
+    // rows 16w + n (K: channels 32 gq .. +31) and 16w + 4 gq + i (V:
+    // channels 8n .. 8n+7) of the wave's sub-page; every row below 128 is
+    // inside the tail buffer, rows at or past the tail length get weight 0
+    half8_t kr[1][4], vr[1][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int u = w + kWaves * h;
+    for (int h = 0; h < 1; ++h) {
+      const int u = w + MW * h;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         kr[h][kk] = *reinterpret_cast<const half8_t*>(kt + (int64_t)(16 * u + n) * D + 32 * gq + 8 * kk);
@@ -538,14 +540,14 @@ __global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i)
         vr[h][i] = *reinterpret_cast<const half8_t*>(vt + (int64_t)(16 * u + 4 * gq + i) * D + 8 * n);
     }
-    float lg[2][4];
+    float lg[1][4];
     float mx = kNegInf;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 1; ++h) {
       float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[h][kk], qB[kk], s, 0, 0, 0);
-      const int row0 = 16 * (w + kWaves * h) + 4 * gq;
+      const int row0 = 16 * (w + MW * h) + 4 * gq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         lg[h][i] = row0 + i < n_tail ? s[i] * a.qk_scale : kNegInf;
@@ -560,7 +562,7 @@ __global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
     for (int nn = 0; nn < D / 16; ++nn) acc[nn] = float4_t{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 1; ++h) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -594,8 +596,8 @@ __global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
   __syncthreads();
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int g = w + kWaves * j;
+  for (int j = 0; j < 1; ++j) {
+    const int g = w + MW * j;
     if (g >= G) continue;  // uniform per wave
     float M = kNegInf, L = 0.0f, O0 = 0.0f, O1 = 0.0f;
     float M1 = kNegInf, L1 = 0.0f;
@@ -612,10 +614,10 @@ __global__ __launch_bounds__(256) void kvarn_merge_kernel(DecodeArgs a) {
     float Mt = kNegInf, Lt = 0.0f, T0 = 0.0f, T1 = 0.0f;
     if (n_tail > 0) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) Mt = fmaxf(Mt, lds_m[ww][g]);
+      for (int ww = 0; ww < MW; ++ww) Mt = fmaxf(Mt, lds_m[ww][g]);
       if (Mt != kNegInf) {
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
+        for (int ww = 0; ww < MW; ++ww) {
           const float f = exp2f(lds_m[ww][g] - Mt);
           Lt += f * lds_l[ww][g];
           T0 += f * (lds_o[ww][g][l] + lds_o[ww][g + G][l]);
@@ -685,10 +687,10 @@ hipError_t launch_kvarn_decode(const DecodeArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const dim3 mgrid((unsigned)a.H, (unsigned)a.B);
   switch (a.G) {
-    case 1: kvarn_merge_kernel<1><<<mgrid, 256, 0, s>>>(a); break;
-    case 2: kvarn_merge_kernel<2><<<mgrid, 256, 0, s>>>(a); break;
-    case 4: kvarn_merge_kernel<4><<<mgrid, 256, 0, s>>>(a); break;
-    case 8: kvarn_merge_kernel<8><<<mgrid, 256, 0, s>>>(a); break;
+    case 1: kvarn_merge_kernel<1><<<mgrid, 64 * kMergeWaves, 0, s>>>(a); break;
+    case 2: kvarn_merge_kernel<2><<<mgrid, 64 * kMergeWaves, 0, s>>>(a); break;
+    case 4: kvarn_merge_kernel<4><<<mgrid, 64 * kMergeWaves, 0, s>>>(a); break;
+    case 8: kvarn_merge_kernel<8><<<mgrid, 64 * kMergeWaves, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
