@@ -610,7 +610,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void kvarn_merge_kernel(DecodeArg
       merge_recs(r0, M, L, O0);
       merge_recs(r1, M1, L1, O1);
     }
-    // the tail partial of head g over the four waves
+    // the tail partial of head g over the eight waves
     float Mt = kNegInf, Lt = 0.0f, T0 = 0.0f, T1 = 0.0f;
     if (n_tail > 0) {
 #pragma unroll
