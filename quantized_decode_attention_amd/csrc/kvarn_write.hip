@@ -22,9 +22,10 @@
 //     bits per token over the channels;
 //   * metadata (binary32): keys alpha_j = c_j s_j, beta_j = c_j m_j,
 //     rho_t = r_t; values alpha_t = r_t s_t, beta_t = r_t m_t, gamma_j = c_j.
-// All binary32 arithmetic rounds exactly as written (no contraction,
-// correctly rounded division and square root), so the codes and metadata are
-// a deterministic function of the binary16 input.
+// All binary32 arithmetic rounds exactly as written (no contraction;
+// correctly rounded square root, reciprocal and quantiser division; the
+// rotation's fma(+-1, b, a) rounds exactly as a +- b), so the codes and
+// metadata are a deterministic function of the binary16 input.
 //
 // Mapping.  One workgroup of 512 threads (8 wavefronts) per (tile, kv head,
 // side).  The tile lives in LDS as binary32 with rows padded to 129 words.
