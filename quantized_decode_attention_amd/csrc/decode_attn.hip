@@ -248,19 +248,14 @@ struct WaveState {
 
 template <int FMT, int D, int G>
 __device__ __forceinline__ void process_unit(const Raw<FMT, D>& r, bool valid, int tok0, int ctx, int n, int gq,
-                                             int l, const half8_t* qB, float kconst, float kbias,
-                                             WaveState<D>& st) {
+                                             const half8_t* qB, float kconst, float kbias, WaveState<D>& st) {
   constexpr int NK = D / 32;
   constexpr int NV = D / 16;
   constexpr bool PTH = kPth<FMT>;
 
-  half2_t ksc01 = {0, 0}, ksc23 = {0, 0};
-  if constexpr (FMT == 4) {
-    uint32_t lo, hi;
-    e4m3x4_to_h_hw(r.ksc, lo, hi);  // E4M3 block scales -> binary16, exact
-    ksc01 = as_h2(lo);
-    ksc23 = as_h2(hi);
-  }
+  // the lane's two key block scales (its D/4 channels), E4M3 -> binary16, exact
+  half2_t ksc01 = {0, 0};
+  if constexpr (FMT == 4) ksc01 = as_h2(e4m3x2_to_h_hw(r.ksc));
   const float kmx = FMT == 7 ? e8m0_scale(r.ksc) : 0.0f;
   float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -558,7 +553,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecodeArgs a) {
         const int ps = (k + 1) % kDepth;
         load_unit<FMT, D>(unit_page(ul, vv[ls]), a.geom, ul & sp_mask, lofs, rr[ls]);
         const bool live = vv[ps] && up >= 0 && up < nu;
-        process_unit<FMT, D, G>(rr[ps], live, unit_tok0(up < 0 ? 0 : up), ctx, n, gq, l, qB, kconst, kbias, st);
+        process_unit<FMT, D, G>(rr[ps], live, unit_tok0(up < 0 ? 0 : up), ctx, n, gq, qB, kconst, kbias, st);
       }
     }
   }

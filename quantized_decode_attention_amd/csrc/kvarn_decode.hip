@@ -97,7 +97,6 @@ constexpr float kPMaxLog2 = 64.0f;
 // exactly; the dword shifted right by 2 gives tokens 1 and 3 the same way.
 // The MFMA operand of channel m therefore lists its tokens in the order
 // 0, 2, 1, 3, and P's operand is built in the same order.
-constexpr int kTokOrder[4] = {0, 2, 1, 3};
 struct VCodes {
   uint32_t t02[4], t13[4];  // per channel byte: binary16 pairs (token 0, 2) and (1, 3)
 };

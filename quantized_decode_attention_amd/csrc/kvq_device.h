@@ -216,6 +216,16 @@ __device__ __forceinline__ void e4m3x4_to_h_hw(uint32_t w, uint32_t& lo, uint32_
       : "v"(w));
 }
 
+// The two low E4M3 bytes of w as one binary16 pair, exact (scale 1.0).
+__device__ __forceinline__ uint32_t e4m3x2_to_h_hw(uint32_t w) {
+  uint32_t lo;
+  asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0\n\t"
+      "s_nop 1"
+      : "=&v"(lo)
+      : "v"(w));
+  return lo;
+}
+
 // The same with a power-of-two scale.
 __device__ __forceinline__ void e4m3x4_to_h_scaled(uint32_t w, float scale, uint32_t& lo, uint32_t& hi) {
   asm("v_cvt_scalef32_pk_f16_fp8 %0, %2, %3\n\t"
