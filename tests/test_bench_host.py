@@ -88,3 +88,19 @@ def test_format_choice():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "kvarn_16k", "--format",
                         "int8_per_token_head"], capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2 and r.stdout == ""
+
+
+def test_call_time_source():
+    """The decode call's time comes from back-to-back calls inside one event
+    pair: the timed region's time per step where a step is one call, and the
+    KVarN decode calls' own region where a step also appends; the per-call
+    event timing (which reads long) is never the figure."""
+    p = object.__new__(bench.Problem)
+    p.dec_region_ms = 0.061
+    p.kvarn = False
+    assert p.call_ms(0.0905, 0.0927) == 0.0905
+    assert "timed steps" in p.call_timing()
+    p.kvarn = True
+    assert p.call_ms(0.0660, 0.0629) == 0.061
+    assert "back to back" in p.call_timing()
+
