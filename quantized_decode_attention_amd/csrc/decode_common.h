@@ -126,7 +126,7 @@ struct RecGroup {
   float m[8], l[8], o[8];
 };
 
-// Loads of splits s0 .. s0+7.  Splits past S reread split s0 (in bounds) and
+// Loads of splits s0 .. s0+7.  Splits past S reread split 0 (in bounds) and
 // are dropped by their max; every load is unconditional, so all of them are
 // in flight before the first use.
 __device__ __forceinline__ void load_recs(const float* recs, int64_t rf, int S, int s0, int g, int64_t o_off,
@@ -134,7 +134,7 @@ __device__ __forceinline__ void load_recs(const float* recs, int64_t rf, int S, 
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const bool in = s0 + k < S;
-    const float* rec = recs + (int64_t)(in ? s0 + k : s0) * rf;
+    const float* rec = recs + (int64_t)(in ? s0 + k : 0) * rf;
     const float mv = rec[g];
     r.m[k] = in ? mv : kNegInf;
     r.l[k] = rec[kMaxGroup + g];
@@ -165,6 +165,14 @@ __device__ __forceinline__ void merge_recs(const RecGroup& r, float& M, float& L
 
 __device__ __forceinline__ void merge_splits(const float* recs, int64_t rf, int S, int g, int64_t o_off,
                                              float& M, float& L, float& O) {
+  if (S > 8 && S <= 16) {  // uniform: both groups' loads in flight at once, one round trip
+    RecGroup r0, r1;
+    load_recs(recs, rf, S, 0, g, o_off, r0);
+    load_recs(recs, rf, S, 8, g, o_off, r1);
+    merge_recs(r0, M, L, O);
+    merge_recs(r1, M, L, O);
+    return;
+  }
   for (int s0 = 0; s0 < S; s0 += 8) {
     RecGroup r;
     load_recs(recs, rf, S, s0, g, o_off, r);
