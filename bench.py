@@ -36,7 +36,8 @@ Also reported on the same line:
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
   formats        the other formats' workloads (decode GB/s, write Mtok/s), and
                  one GPU's share of the 16K workloads under two-way tensor
-                 parallelism (32 q / 4 kv heads)
+                 parallelism (32 q / 4 kv heads); each times at least 200
+                 steps (a shorter window makes the 40 us calls noisy)
 
 Warm-up: W untimed steps (default 3000, about 0.3 s) before the timed ones,
 and at least 200 ms of back-to-back writes before the write is timed.  The
@@ -621,7 +622,7 @@ def main():
                 continue
             p = Problem(K, name, fmt, flags)
             wm, wms = p.time_write()
-            ms_s, ms_d = p.time_steps(max(20, args.steps // 2), args.warmup)
+            ms_s, ms_d = p.time_steps(max(200, args.steps), args.warmup)
             fl_gbs, _ = p.time_read_floor()
             key = K.FORMAT_NAMES[fmt] + ("_4over6" if flags else "") + ("_tp2_share" if name.endswith("_tp2") else "")
             ms_c = p.call_ms(ms_s, ms_d)
