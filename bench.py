@@ -202,6 +202,9 @@ class Problem:
         keeps counting across warm-up, timed and instrumented steps."""
         import torch
         if self.kvarn:
+            if warmup + 2 * steps > self.w.T - 1:
+                raise SystemExit(f"bench: a KVarN workload appends one token per step, so warm-up + 2 x steps "
+                                 f"({warmup + 2 * steps}) must stay below its context ({self.w.T})")
             self.prepare_incremental(warmup + 2 * steps)
         self.prepare_calls(warmup + 2 * steps)
         torch.cuda.synchronize()
